@@ -1,0 +1,276 @@
+"""CPU oracle for MLA decode over a latent KV cache (fp64, numpy).
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU
+baseline use this module.  The library in ``mla_latent_kv_20_amd`` never
+imports it, and it imports nothing from there: inputs reach it as plain numpy
+arrays (fp64, widened exactly from the storage type).
+
+Pages cited (title, then section / equation):
+  [review]  "DeepSeek-V2 review" (velog.io/@jmsong62)
+  [obsidian] "DeepSeek-V2: A Strong, Economical, and Efficient Mixture-of-Experts Language Model"
+  [notes]   "MLA(Multi-head Latent Attention): DeepSeek-V2 논문정리"
+  [report]  "Техотчёт DeepSeek-V2 (2024): MLA и экономика инференса"
+  [v3]      DeepSeek-V3 Technical Report notes (xuxeong.tistory.com), "Multi-Head Latent Attention"
+
+Notation follows the pages:
+  c^KV_j  latent row j, width d_c                          ([notes] eq. 9)
+  k^C_{j,i} = W^UK_i c^KV_j, v^C_{j,i} = W^UV_i c^KV_j      ([notes] eq. 10, 11); W^UK_i is [d_h, d_c]
+  k^R_j   decoupled RoPE key, width d_h^R, one per row shared by all heads
+          ([notes] "Decoupled Rotary Position Embedding", item 3; [review] 2.3; [report] "Идея 2")
+  q_{t,i} = [q^C_{t,i}; q^R_{t,i}],  k_{j,i} = [k^C_{j,i}; k^R_j]
+  o_{t,i} = sum_j softmax_j(q_{t,i}^T k_{j,i} / sqrt(d_h + d_h^R)) v^C_{j,i}
+          ([v3] eq. 10; [report] "Идея 2"; [obsidian] "Multi-head Latent Attention (MLA)" prints the
+           same sum with the square root lost in extraction)
+  mask    query r of T_q new queries against T_k rows sees rows j <= T_k - T_q + r
+          ([notes] "MLA 코드 구현": triu of -inf with diagonal T_k - T_q + 1)
+
+Two formulations are computed independently:
+  naive_decode     materializes k^C and v^C for every row and head, then runs textbook
+                   softmax attention: the pages' definition.
+  absorbed_decode  folds W^UK into the query and applies W^UV after the weighted sum of
+                   latents ([notes] "Key에 대한 수식 전개" and "Value에 대한 수식 전개";
+                   [report] "Идея 1"): the form the GPU path computes.
+and the per-call pieces of the absorbed form (absorb_q, split_partials, merge_splits,
+out_proj) that the C-ABI entry points are compared against one by one.
+
+Readings where the pages are silent or garbled (each is listed in the design notes):
+  * scale 1/sqrt(d_h + d_h^R) (three pages agree; one prints it without the root);
+  * k^R is one vector per row shared by every head (three pages; one page's code
+    gives each head its own and never uses it);
+  * log-sum-exp is the natural log of sum_j exp(scaled logit);
+  * a split (a contiguous range of rows) that holds no visible row has lse = -inf
+    and a zero output; the merge gives it weight zero.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, Optional
+
+import numpy as np
+
+
+def default_scale(d_h: int, d_r: int) -> float:
+    """1/sqrt(d_h + d_h^R): the attention normalisation of decoupled-RoPE MLA."""
+    return 1.0 / math.sqrt(d_h + d_r)
+
+
+def visible_rows(length: int, q_per_seq: int, r: int) -> int:
+    """Rows query r (0-based, of q_per_seq new queries) may attend in a length-row sequence."""
+    return int(length) - int(q_per_seq) + int(r) + 1
+
+
+def _softmax_stats(s: np.ndarray):
+    """Textbook softmax along axis 0 of s (masked entries are -inf).
+
+    Returns p, the row maximum m and the log-sum-exp m + ln(sum exp(s - m)).
+    """
+    m = np.max(s, axis=0)
+    e = np.exp(s - m)
+    z = np.sum(e, axis=0)
+    return e / z, m, m + np.log(z)
+
+
+# ----------------------------------------------------------------------------
+# The definition: materialized keys and values
+# ----------------------------------------------------------------------------
+
+def naive_decode(c_kv, k_r, offsets, q_c, q_r, w_uk, w_uv, q_per_seq: int,
+                 scale: Optional[float] = None, seqs: Optional[Iterable[int]] = None,
+                 return_weights: bool = False) -> Dict[str, np.ndarray]:
+    """Multi-head attention over keys and values rebuilt from the latent cache (fp64).
+
+    For each sequence b and head i: K^C = C_b W^UK_i^T and V^C = C_b W^UV_i^T over all
+    rows of b ([notes] eq. 10, 11); keys are [K^C ; k^R] with k^R broadcast to every head; the
+    query is [q^C ; q^R]; scores are scaled by ``scale`` (default 1/sqrt(d_h + d_h^R)),
+    masked by the generalized causal rule, normalised by a textbook softmax, and o^C is
+    the weighted sum of V^C.  Also returns the log-sum-exp of the scaled scores and
+    o_lat = sum_j p_j c^KV_j (the latent-space output the absorbed form produces).
+
+    ``seqs`` restricts the work to some sequences (other outputs stay NaN).
+    """
+    c_kv = np.asarray(c_kv, np.float64)
+    k_r = np.asarray(k_r, np.float64)
+    q_c = np.asarray(q_c, np.float64)
+    q_r = np.asarray(q_r, np.float64)
+    w_uk = np.asarray(w_uk, np.float64)
+    w_uv = np.asarray(w_uv, np.float64)
+    n_q, n_h, d_h = q_c.shape
+    d_r = q_r.shape[2]
+    d_c = c_kv.shape[1]
+    B = len(offsets) - 1
+    if scale is None:
+        scale = default_scale(d_h, d_r)
+    o_c = np.full((n_q, n_h, d_h), np.nan)
+    o_lat = np.full((n_q, n_h, d_c), np.nan)
+    lse = np.full((n_q, n_h), np.nan)
+    weights = {}
+    for b in (range(B) if seqs is None else seqs):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        C = c_kv[lo:hi]
+        R = k_r[lo:hi]
+        L = hi - lo
+        for i in range(n_h):
+            K = np.concatenate([C @ w_uk[i].T, R], axis=1)     # [L, d_h + d_h^R]
+            V = C @ w_uv[i].T                                  # [L, d_h]
+            for r in range(q_per_seq):
+                n = b * q_per_seq + r
+                q = np.concatenate([q_c[n, i], q_r[n, i]])
+                s = (K @ q) * scale
+                s[visible_rows(L, q_per_seq, r):] = -np.inf
+                p, _, l = _softmax_stats(s)
+                o_c[n, i] = p @ V
+                o_lat[n, i] = p @ C
+                lse[n, i] = l
+                if return_weights:
+                    weights[(n, i)] = p
+    out = dict(o_c=o_c, o_lat=o_lat, lse=lse)
+    if return_weights:
+        out["weights"] = weights
+    return out
+
+
+# ----------------------------------------------------------------------------
+# The absorbed form, one function per C-ABI call
+# ----------------------------------------------------------------------------
+
+def absorb_q(q_c, q_r, w_uk) -> np.ndarray:
+    """q_abs[n, i] = [ W^UK_i^T q^C_{n,i} ; q^R_{n,i} ].
+
+    Key absorption ([notes] "Key에 대한 수식 전개"; [report] "Идея 1") and the concat
+    identity ([notes] "Decoupled Rotary Position Embedding", item 4).
+
+    The content score q^C . (W^UK c) equals (W^UK^T q^C) . c, so the query moves into
+    latent space once and keys are never rebuilt; the RoPE part is carried unchanged
+    because [a;b].[c;d] = a.c + b.d.
+    """
+    q_c = np.asarray(q_c, np.float64)
+    q_r = np.asarray(q_r, np.float64)
+    w_uk = np.asarray(w_uk, np.float64)
+    lat = np.einsum("nid,idc->nic", q_c, w_uk)
+    return np.concatenate([lat, q_r], axis=2)
+
+
+def split_bounds(visible: int, s: int, num_splits: int, split_rows: int):
+    """Row range [lo, hi) of split s among ``visible`` rows.
+
+    Split s < num_splits-1 covers rows [s*split_rows, (s+1)*split_rows); the last split
+    covers everything from (num_splits-1)*split_rows on; each range is clipped to the
+    visible rows, so it may be empty.  With one split the range is all visible rows.
+    """
+    if num_splits == 1:
+        return 0, visible
+    lo = s * split_rows
+    hi = visible if s == num_splits - 1 else (s + 1) * split_rows
+    return min(lo, visible), min(hi, visible)
+
+
+def split_partials(q_abs, c_kv, k_r, offsets, q_per_seq: int, num_splits: int,
+                   split_rows: int, scale: float):
+    """Softmax attention of every query head over each split's rows, in latent space.
+
+    Row j's key is the whole latent row [c^KV_j ; k^R_j]; its value is c^KV_j.  For each
+    split: o_s = sum_j p_j c_j with p the softmax over the split's rows only, and
+    lse_s = log-sum-exp of the split's scaled scores.  Empty splits: o_s = 0, lse_s = -inf.
+    Returns o_part [S, n_q, n_h, d_c] and lse_part [S, n_q, n_h].
+    """
+    q_abs = np.asarray(q_abs, np.float64)
+    c_kv = np.asarray(c_kv, np.float64)
+    k_r = np.asarray(k_r, np.float64)
+    n_q, n_h, _ = q_abs.shape
+    d_c = c_kv.shape[1]
+    B = len(offsets) - 1
+    o_part = np.zeros((num_splits, n_q, n_h, d_c))
+    lse_part = np.full((num_splits, n_q, n_h), -np.inf)
+    for b in range(B):
+        lo_b, hi_b = int(offsets[b]), int(offsets[b + 1])
+        X = np.concatenate([c_kv[lo_b:hi_b], k_r[lo_b:hi_b]], axis=1)   # [L, d_c + d_r]
+        for r in range(q_per_seq):
+            n = b * q_per_seq + r
+            vis = visible_rows(hi_b - lo_b, q_per_seq, r)
+            for s in range(num_splits):
+                lo, hi = split_bounds(vis, s, num_splits, split_rows)
+                if hi <= lo:
+                    continue
+                S = (X[lo:hi] @ q_abs[n].T) * scale        # [rows, n_h]
+                p, _, l = _softmax_stats(S)
+                o_part[s, n] = p.T @ X[lo:hi, :d_c]
+                lse_part[s, n] = l
+    return o_part, lse_part
+
+
+def merge_splits(o_part, lse_part):
+    """Combine split results: softmax over a disjoint union of row sets.
+
+    With M = max_s lse_s and w_s = exp(lse_s - M): o = sum_s w_s o_s / sum_s w_s and
+    lse = M + ln sum_s w_s.  Splits with lse_s = -inf get w_s = 0.
+    """
+    o_part = np.asarray(o_part, np.float64)
+    lse_part = np.asarray(lse_part, np.float64)
+    M = np.max(lse_part, axis=0)
+    w = np.exp(lse_part - M)                      # [S, n_q, n_h]
+    z = np.sum(w, axis=0)
+    o = np.einsum("snh,snhc->nhc", w, o_part) / z[..., None]
+    return o, M + np.log(z)
+
+
+def attend_latent(q_abs, c_kv, k_r, offsets, q_per_seq: int, scale: float):
+    """Unsplit latent attention: o_lat [n_q, n_h, d_c] and lse [n_q, n_h]."""
+    o, l = split_partials(q_abs, c_kv, k_r, offsets, q_per_seq, 1, 0, scale)
+    return o[0], l[0]
+
+
+def out_proj(o_lat, w_uv) -> np.ndarray:
+    """o^C[n, i] = W^UV_i o_lat[n, i].
+
+    Value absorption ([notes] "Value에 대한 수식 전개"): the weighted sum of latents is
+    projected once instead of projecting every row."""
+    return np.einsum("idc,nic->nid", np.asarray(w_uv, np.float64), np.asarray(o_lat, np.float64))
+
+
+def absorbed_decode(c_kv, k_r, offsets, q_c, q_r, w_uk, w_uv, q_per_seq: int,
+                    scale: Optional[float] = None, num_splits: int = 1,
+                    split_rows: int = 0) -> Dict[str, np.ndarray]:
+    """The four calls end to end: absorb_q -> split_partials -> merge_splits -> out_proj."""
+    d_h = np.asarray(q_c).shape[2]
+    d_r = np.asarray(q_r).shape[2]
+    if scale is None:
+        scale = default_scale(d_h, d_r)
+    qa = absorb_q(q_c, q_r, w_uk)
+    op, lp = split_partials(qa, c_kv, k_r, offsets, q_per_seq, num_splits, split_rows, scale)
+    o_lat, lse = merge_splits(op, lp)
+    return dict(q_abs=qa, o_part=op, lse_part=lp, o_lat=o_lat, lse=lse, o_c=out_proj(o_lat, w_uv))
+
+
+# ----------------------------------------------------------------------------
+# Helpers for the pages' side claims
+# ----------------------------------------------------------------------------
+
+def rope_pairs(x, positions, theta: float = 10000.0) -> np.ndarray:
+    """RoPE as a complex rotation of the pairs (x_k, x_{k+d/2}) by angle pos * theta^(-2k/d).
+
+    Same rotate-half convention as the helpers in [notes] "MLA 코드 구현", written as complex
+    multiplication so that it shares no arithmetic with any other implementation.
+    """
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    h = d // 2
+    z = x[..., :h] + 1j * x[..., h:]
+    k = np.arange(h, dtype=np.float64)
+    ang = np.asarray(positions, np.float64)[..., None] * np.power(theta, -2.0 * k / d)
+    z = z * np.exp(1j * ang)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def cache_elems_per_token(kind: str, layers: int, n_h: int = 0, d_h: int = 0, n_g: int = 0,
+                          d_c: int = 0, d_r: int = 0) -> int:
+    """KV-cache elements per token ([report] "Сколько получилось" table; [review] 2.4)."""
+    if kind == "mha":
+        return 2 * n_h * d_h * layers
+    if kind == "gqa":
+        return 2 * n_g * d_h * layers
+    if kind == "mqa":
+        return 2 * d_h * layers
+    if kind == "mla":
+        return (d_c + d_r) * layers
+    raise ValueError(kind)

@@ -1,0 +1,462 @@
+"""Pins for the CPU oracle.
+
+Every test here checks the oracle against something other than itself: a closed form,
+an invariant, brute force with scalar Python loops, a library attention routine, or a
+number the pages print.  A few tests plant a mistake in the oracle's inputs or
+parameters and check that the pins notice it.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+import oracle as O
+from mla_latent_kv_20_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(float(np.max(np.abs(b))), 1e-300))
+
+
+def args_of(w):
+    return dict(c_kv=w.f64("c_kv"), k_r=w.f64("k_r"), offsets=w.offsets, q_c=w.f64("q_c"),
+                q_r=w.f64("q_r"), w_uk=w.f64("w_uk"), w_uv=w.f64("w_uv"), q_per_seq=w.q_per_seq)
+
+
+def tiny_mtp():
+    """Tiny multi-token case: 4 queries per sequence, each with its own appended row."""
+    return W.make_workload("tiny_mtp", n_h=3, d_h=4, d_c=8, d_r=4, dtype=W.F32,
+                           lengths=[2, 9], q_per_seq=4, appended_rows=True, seed=5)
+
+
+# ----------------------------------------------------------------------------
+# Brute force: scalar Python loops straight from the attention definition
+# ----------------------------------------------------------------------------
+
+def brute_force(c_kv, k_r, offsets, q_c, q_r, w_uk, w_uv, q_per_seq, scale, mask_shift=0):
+    c = np.asarray(c_kv, np.float64).tolist()
+    kr = np.asarray(k_r, np.float64).tolist()
+    qc = np.asarray(q_c, np.float64).tolist()
+    qr = np.asarray(q_r, np.float64).tolist()
+    wk = np.asarray(w_uk, np.float64).tolist()
+    wv = np.asarray(w_uv, np.float64).tolist()
+    n_h, d_h, d_c = len(wk), len(wk[0]), len(wk[0][0])
+    d_r = len(kr[0])
+    out = {}
+    for b in range(len(offsets) - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        for r in range(q_per_seq):
+            n = b * q_per_seq + r
+            vis = (hi - lo) - q_per_seq + r + 1 + mask_shift
+            for i in range(n_h):
+                keys, vals = [], []
+                for j in range(lo, lo + vis):
+                    keys.append([sum(wk[i][d][x] * c[j][x] for x in range(d_c)) for d in range(d_h)]
+                                + kr[j])
+                    vals.append([sum(wv[i][d][x] * c[j][x] for x in range(d_c)) for d in range(d_h)])
+                q = qc[n][i] + qr[n][i]
+                s = [sum(q[k] * key[k] for k in range(d_h + d_r)) * scale for key in keys]
+                mx = max(s)
+                e = [math.exp(v - mx) for v in s]
+                z = sum(e)
+                out[(n, i)] = ([sum(e[j] / z * vals[j][d] for j in range(vis)) for d in range(d_h)],
+                               mx + math.log(z),
+                               [sum(e[j] / z * c[lo + j][x] for j in range(vis)) for x in range(d_c)])
+    return out
+
+
+def check_against_brute(res, brute, tol):
+    for (n, i), (o_c, lse, o_lat) in brute.items():
+        assert rel(res["o_c"][n, i], o_c) <= tol
+        assert abs(res["lse"][n, i] - lse) <= tol * max(1.0, abs(lse))
+        assert rel(res["o_lat"][n, i], o_lat) <= tol
+
+
+@pytest.mark.parametrize("make", [lambda: W.make_config("tiny_f32"),
+                                  lambda: W.make_config("toy_p3"),
+                                  tiny_mtp])
+def test_brute_force_matches_both_formulations(make):
+    w = make()
+    a = args_of(w)
+    scale = O.default_scale(w.d_h, w.d_r)
+    brute = brute_force(**a, scale=scale)
+    check_against_brute(O.naive_decode(**a), brute, 1e-12)
+    check_against_brute(O.absorbed_decode(**a), brute, 1e-12)
+    check_against_brute(O.absorbed_decode(**a, num_splits=3, split_rows=4), brute, 1e-12)
+
+
+@pytest.mark.parametrize("mutant", ["scale_without_root", "rope_term_dropped", "mask_off_by_one",
+                                    "weights_swapped", "scale_head_dim_only"])
+def test_planted_mistakes_are_caught(mutant):
+    """Plausible oracle mistakes change the result far beyond the pins' tolerance."""
+    w = tiny_mtp()
+    a = args_of(w)
+    scale = O.default_scale(w.d_h, w.d_r)
+    brute = brute_force(**a, scale=scale)
+    if mutant == "scale_without_root":          # the garbled normalisation one page prints
+        res = O.naive_decode(**a, scale=1.0 / (w.d_h + w.d_r))
+    elif mutant == "scale_head_dim_only":       # one page's code divides by sqrt(d_h)
+        res = O.naive_decode(**a, scale=1.0 / math.sqrt(w.d_h))
+    elif mutant == "rope_term_dropped":
+        res = O.naive_decode(**dict(a, k_r=np.zeros_like(a["k_r"])))
+    elif mutant == "weights_swapped":
+        res = O.naive_decode(**dict(a, w_uk=a["w_uv"], w_uv=a["w_uk"]))
+    else:
+        res = O.naive_decode(**a)
+        brute = brute_force(**a, scale=scale, mask_shift=-1)
+        # the last query of each sequence sees one row less in the mutant; compare only those
+        brute = {k: v for k, v in brute.items() if k[0] % w.q_per_seq == w.q_per_seq - 1}
+    with pytest.raises(AssertionError):
+        check_against_brute(res, brute, 1e-6)
+
+
+# ----------------------------------------------------------------------------
+# Absorbed form == naive form (the pages' own exercise, extended to the whole decode)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,splits", [("tiny_f32", (1, 0)), ("toy_p3", (2, 4)),
+                                         ("dsv2_small", (3, 256)), ("dsv2_small_mtp", (2, 128))])
+def test_absorbed_equals_naive(name, splits):
+    w = W.make_config(name)
+    a = args_of(w)
+    seqs = None
+    if name == "dsv2_small":
+        seqs = [0, 1]               # keep the CPU suite short; sequence 2 is covered below
+    naive = O.naive_decode(**a, seqs=seqs)
+    absd = O.absorbed_decode(**a, num_splits=splits[0], split_rows=splits[1])
+    keep = slice(None) if seqs is None else slice(0, 2 * w.q_per_seq)
+    assert rel(absd["o_c"][keep], naive["o_c"][keep]) <= 1e-12
+    assert rel(absd["o_lat"][keep], naive["o_lat"][keep]) <= 1e-12
+    assert np.max(np.abs(absd["lse"][keep] - naive["lse"][keep])) <= 1e-12
+
+
+def test_absorbed_equals_naive_long_sequence_sampled_heads():
+    """1000-row DeepSeek-V2-shaped sequence, a handful of heads, naive vs absorbed."""
+    w = W.make_config("dsv2_small")
+    a = args_of(w)
+    heads = [0, 37, 127]
+    sub = dict(a, q_c=a["q_c"][:, heads], q_r=a["q_r"][:, heads], w_uk=a["w_uk"][heads],
+               w_uv=a["w_uv"][heads])
+    naive = O.naive_decode(**sub, seqs=[2])
+    absd = O.absorbed_decode(**sub, num_splits=3, split_rows=256)
+    assert rel(absd["o_c"][2], naive["o_c"][2]) <= 1e-12
+    assert np.max(np.abs(absd["lse"][2] - naive["lse"][2])) <= 1e-12
+
+
+def test_absorb_q_moves_the_key_projection_onto_the_query():
+    """q_abs . c == q^C . (W^UK c) for arbitrary latent rows c (key absorption)."""
+    rng = np.random.default_rng(3)
+    n_q, n_h, d_h, d_c, d_r = 3, 5, 6, 10, 4
+    q_c = rng.standard_normal((n_q, n_h, d_h))
+    q_r = rng.standard_normal((n_q, n_h, d_r))
+    w_uk = rng.standard_normal((n_h, d_h, d_c))
+    qa = O.absorb_q(q_c, q_r, w_uk)
+    assert qa.shape == (n_q, n_h, d_c + d_r)
+    assert np.array_equal(qa[..., d_c:], q_r)
+    c = rng.standard_normal((7, d_c))
+    for n in range(n_q):
+        for i in range(n_h):
+            direct = np.array([q_c[n, i] @ (w_uk[i] @ cj) for cj in c])
+            assert rel(c @ qa[n, i, :d_c], direct) <= 1e-13
+
+
+def test_out_proj_of_a_basis_vector_is_a_weight_column():
+    rng = np.random.default_rng(4)
+    n_h, d_h, d_c = 3, 5, 7
+    w_uv = rng.standard_normal((n_h, d_h, d_c))
+    o_lat = np.zeros((d_c, n_h, d_c))
+    for k in range(d_c):
+        o_lat[k, :, k] = 1.0
+    o = O.out_proj(o_lat, w_uv)
+    for k in range(d_c):
+        for i in range(n_h):
+            assert np.array_equal(o[k, i], w_uv[i][:, k])
+
+
+def test_absorption_identity_from_the_exercise():
+    """(W^UQ c^Q)^T (W^UK c^KV) == (c^Q)^T ((W^UQ)^T W^UK) c^KV for random matrices."""
+    rng = np.random.default_rng(7)
+    w_uq = rng.standard_normal((128, 48))
+    w_uk = rng.standard_normal((128, 64))
+    cq = rng.standard_normal(48)
+    ckv = rng.standard_normal(64)
+    lhs = (w_uq @ cq) @ (w_uk @ ckv)
+    rhs = cq @ ((w_uq.T @ w_uk) @ ckv)
+    assert abs(lhs - rhs) <= 1e-12 * abs(lhs) + 1e-12
+
+
+# ----------------------------------------------------------------------------
+# Closed forms and special cases
+# ----------------------------------------------------------------------------
+
+def test_weights_sum_to_one():
+    w = tiny_mtp()
+    res = O.naive_decode(**args_of(w), return_weights=True)
+    for p in res["weights"].values():
+        assert abs(p.sum() - 1.0) <= 1e-14
+        assert np.all(p >= 0)
+
+
+def test_single_row_returns_its_value_exactly():
+    w = W.make_workload("t1", n_h=4, d_h=16, d_c=32, d_r=8, dtype=W.F32, lengths=[1, 1, 1], seed=9)
+    a = args_of(w)
+    for res in (O.naive_decode(**a), O.absorbed_decode(**a)):
+        for b in range(3):
+            assert np.array_equal(res["o_lat"][b], np.broadcast_to(a["c_kv"][b], (4, 32)))
+            for i in range(4):
+                assert rel(res["o_c"][b, i], a["w_uv"][i] @ a["c_kv"][b]) <= 1e-14
+
+
+def test_zero_query_gives_the_mean_of_visible_rows():
+    w = tiny_mtp()
+    a = args_of(w)
+    a0 = dict(a, q_c=np.zeros_like(a["q_c"]), q_r=np.zeros_like(a["q_r"]))
+    for res in (O.naive_decode(**a0), O.absorbed_decode(**a0, num_splits=2, split_rows=4)):
+        for b in range(w.batch):
+            lo, hi = int(w.offsets[b]), int(w.offsets[b + 1])
+            for r in range(w.q_per_seq):
+                vis = O.visible_rows(hi - lo, w.q_per_seq, r)
+                mean = a["c_kv"][lo:lo + vis].mean(axis=0)
+                n = b * w.q_per_seq + r
+                for i in range(w.n_h):
+                    assert rel(res["o_lat"][n, i], mean) <= 1e-13
+                    assert abs(res["lse"][n, i] - math.log(vis)) <= 1e-13
+
+
+def test_one_dominant_row_wins():
+    rng = np.random.default_rng(11)
+    L, d_c, d_r, n_h = 50, 16, 4, 2
+    c = rng.standard_normal((L, d_c))
+    kr = rng.standard_normal((L, d_r))
+    X = np.concatenate([c, kr], axis=1)
+    star = 17
+    scale = 0.25
+    q_abs = np.zeros((1, n_h, d_c + d_r))
+    # score_j = alpha * scale * x_j . x_star; the gap to the runner-up is >= 40 nats
+    gaps = X[star] @ X[star] - np.delete(X @ X[star], star)
+    alpha = 40.0 / (scale * gaps.min())
+    q_abs[0, :] = alpha * X[star]
+    o, lse = O.attend_latent(q_abs, c, kr, np.array([0, L]), 1, scale)
+    assert rel(o[0, 0], c[star]) <= 1e-15 * L + math.exp(-40) * 10
+    expected_lse = logsumexp(alpha * scale * (X @ X[star]))
+    assert abs(lse[0, 0] - expected_lse) <= 1e-12 * abs(expected_lse)
+
+
+# ----------------------------------------------------------------------------
+# Library attention routine (torch SDPA, fp64 on the CPU) and log-sum-exp
+# ----------------------------------------------------------------------------
+
+def sdpa_reference(a, scale):
+    """Materialize K and V with torch, then call torch's scaled_dot_product_attention."""
+    c = torch.from_numpy(a["c_kv"])
+    kr = torch.from_numpy(a["k_r"])
+    wk = torch.from_numpy(a["w_uk"])
+    wv = torch.from_numpy(a["w_uv"])
+    qc = torch.from_numpy(a["q_c"])
+    qr = torch.from_numpy(a["q_r"])
+    T_q = a["q_per_seq"]
+    n_h = wk.shape[0]
+    out, lse = [], []
+    for b in range(len(a["offsets"]) - 1):
+        lo, hi = int(a["offsets"][b]), int(a["offsets"][b + 1])
+        C, R = c[lo:hi], kr[lo:hi]
+        L = hi - lo
+        K = torch.cat([torch.einsum("jc,hdc->hjd", C, wk), R.expand(n_h, L, R.shape[1])], dim=2)
+        V = torch.einsum("jc,hdc->hjd", C, wv)
+        Q = torch.cat([qc[b * T_q:(b + 1) * T_q], qr[b * T_q:(b + 1) * T_q]], dim=2).transpose(0, 1)
+        masked = torch.triu(torch.ones(T_q, L, dtype=torch.bool), diagonal=L - T_q + 1)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            Q[None], K[None], V[None], attn_mask=~masked, scale=scale)[0]       # [n_h, T_q, d_h]
+        out.append(o.transpose(0, 1))
+        s = (Q @ K.transpose(1, 2)) * scale
+        s = s.masked_fill(masked, float("-inf")).numpy()
+        lse.append(logsumexp(s, axis=2).T)                                        # [T_q, n_h]
+    return torch.cat(out).numpy(), np.concatenate(lse)
+
+
+@pytest.mark.parametrize("make", [lambda: W.make_config("tiny_f32"), tiny_mtp,
+                                  lambda: W.make_config("toy_p3")])
+def test_matches_torch_sdpa_and_logsumexp(make):
+    w = make()
+    a = args_of(w)
+    scale = O.default_scale(w.d_h, w.d_r)
+    o_ref, lse_ref = sdpa_reference(a, scale)
+    for res in (O.naive_decode(**a), O.absorbed_decode(**a, num_splits=2, split_rows=8)):
+        assert rel(res["o_c"], o_ref) <= 1e-12
+        assert np.max(np.abs(res["lse"] - lse_ref)) <= 1e-12
+
+
+def test_identity_weights_reduce_to_plain_attention():
+    """With W^UK = W^UV = I (d_h = d_c) MLA is single-key-head attention over [c; k^R] -> c."""
+    rng = np.random.default_rng(13)
+    d = 8
+    w = W.make_workload("eye", n_h=3, d_h=d, d_c=d, d_r=4, dtype=W.F32, lengths=[6, 10], seed=2)
+    a = args_of(w)
+    a["w_uk"] = np.broadcast_to(np.eye(d), (3, d, d)).copy()
+    a["w_uv"] = a["w_uk"].copy()
+    scale = 0.3 + rng.random()
+    res = O.naive_decode(**a, scale=scale)
+    for b in range(2):
+        lo, hi = int(w.offsets[b]), int(w.offsets[b + 1])
+        k = torch.from_numpy(np.concatenate([a["c_kv"][lo:hi], a["k_r"][lo:hi]], axis=1))
+        v = torch.from_numpy(a["c_kv"][lo:hi])
+        q = torch.from_numpy(np.concatenate([a["q_c"][b], a["q_r"][b]], axis=1))   # [n_h, d+4]
+        o = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None], scale=scale)[0]
+        assert rel(res["o_c"][b], o.numpy()) <= 1e-12
+        assert rel(res["o_lat"][b], o.numpy()) <= 1e-12
+
+
+# ----------------------------------------------------------------------------
+# Split / merge and invariances
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("num_splits,split_rows", [(1, 0), (2, 1), (3, 4), (7, 2), (12, 32), (4, 64)])
+def test_merge_of_any_partition_equals_the_unsplit_result(num_splits, split_rows):
+    w = tiny_mtp()
+    a = args_of(w)
+    scale = O.default_scale(w.d_h, w.d_r)
+    qa = O.absorb_q(a["q_c"], a["q_r"], a["w_uk"])
+    o1, l1 = O.attend_latent(qa, a["c_kv"], a["k_r"], w.offsets, w.q_per_seq, scale)
+    op, lp = O.split_partials(qa, a["c_kv"], a["k_r"], w.offsets, w.q_per_seq, num_splits,
+                              split_rows, scale)
+    o2, l2 = O.merge_splits(op, lp)
+    assert rel(o2, o1) <= 1e-13
+    assert np.max(np.abs(l2 - l1)) <= 1e-13
+    # empty splits carry zero output and -inf lse
+    empty = np.isneginf(lp)
+    assert np.all(op[empty] == 0)
+
+
+def test_split_bounds_cover_every_visible_row_once():
+    for vis in [1, 5, 31, 32, 33, 200]:
+        for S, R in [(1, 0), (2, 32), (3, 7), (10, 32), (4, 100)]:
+            seen = []
+            for s in range(S):
+                lo, hi = O.split_bounds(vis, s, S, R)
+                seen.extend(range(lo, hi))
+            assert seen == list(range(vis))
+
+
+def test_row_permutation_does_not_change_a_single_query():
+    w = W.make_config("toy_p3")
+    a = args_of(w)
+    rng = np.random.default_rng(21)
+    perm = np.concatenate([lo + rng.permutation(hi - lo)
+                           for lo, hi in zip(w.offsets[:-1], w.offsets[1:])])
+    b = dict(a, c_kv=a["c_kv"][perm], k_r=a["k_r"][perm])
+    r1, r2 = O.naive_decode(**a), O.naive_decode(**b)
+    assert rel(r2["o_c"], r1["o_c"]) <= 1e-13
+    assert np.max(np.abs(r2["lse"] - r1["lse"])) <= 1e-13
+
+
+def test_masked_rows_have_no_influence():
+    w = tiny_mtp()
+    a = args_of(w)
+    rng = np.random.default_rng(23)
+    c2, k2 = a["c_kv"].copy(), a["k_r"].copy()
+    # rows the first query of each sequence cannot see: the last q_per_seq-1 rows
+    for b in range(w.batch):
+        hi = int(w.offsets[b + 1])
+        c2[hi - 3:hi] = rng.standard_normal((3, w.d_c)) * 100
+        k2[hi - 3:hi] = rng.standard_normal((3, w.d_r)) * 100
+    r1 = O.naive_decode(**a)
+    r2 = O.naive_decode(**dict(a, c_kv=c2, k_r=k2))
+    for b in range(w.batch):
+        n0 = b * w.q_per_seq
+        assert np.array_equal(r1["o_c"][n0], r2["o_c"][n0])
+        assert np.array_equal(r1["lse"][n0], r2["lse"][n0])
+        assert not np.allclose(r1["o_c"][n0 + 3], r2["o_c"][n0 + 3])
+
+
+# ----------------------------------------------------------------------------
+# RoPE (decoupled key) claims
+# ----------------------------------------------------------------------------
+
+def test_rope_depends_only_on_relative_position_and_keeps_norms():
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal(64)
+    k = rng.standard_normal(64)
+    base = O.rope_pairs(q, 1000) @ O.rope_pairs(k, 990)
+    for shift in [-990, 1, 77, 130000]:
+        assert abs(O.rope_pairs(q, 1000 + shift) @ O.rope_pairs(k, 990 + shift) - base) <= 1e-11
+    for pos in [0, 5, 131071]:
+        assert abs(np.linalg.norm(O.rope_pairs(q, pos)) - np.linalg.norm(q)) <= 1e-12
+    assert np.array_equal(O.rope_pairs(q, 0), q)
+
+
+def test_rope_two_dim_case_is_a_plane_rotation():
+    x = np.array([0.3, -1.7])
+    for p in [0.0, 1.0, 2.5, 1000.0]:
+        c, s = math.cos(p), math.sin(p)
+        want = np.array([0.3 * c + 1.7 * s, -1.7 * c + 0.3 * s])
+        assert rel(O.rope_pairs(x, p), want) <= 1e-15 * 100
+
+
+def test_generator_rope_matches_oracle_rope():
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((40, 64))
+    pos = rng.integers(0, 140000, size=40)
+    assert rel(W.rope_rotate(x, pos), O.rope_pairs(x, pos)) <= 1e-13
+
+
+def test_rope_on_compressed_keys_breaks_absorption():
+    """Rotating k^C by position puts R^T R between W^UQ and W^UK: the absorbed score is wrong."""
+    rng = np.random.default_rng(35)
+    d_h, d_c, L = 16, 32, 20
+    w_uk = rng.standard_normal((d_h, d_c))
+    q = rng.standard_normal(d_h)
+    c = rng.standard_normal((L, d_c))
+    t = L
+    absorbed = c @ (w_uk.T @ q)
+    with_rope = np.array([O.rope_pairs(q, t) @ O.rope_pairs(w_uk @ c[j], j) for j in range(L)])
+    without = np.array([q @ (w_uk @ c[j]) for j in range(L)])
+    assert rel(absorbed, without) <= 1e-13
+    assert rel(absorbed, with_rope) > 1e-2
+
+
+# ----------------------------------------------------------------------------
+# Cache-size numbers printed on the pages
+# ----------------------------------------------------------------------------
+
+def load_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        for line in f:
+            line = line.split("|")[0].strip()
+            if line and not line.startswith("#"):
+                k, v = line.split()
+                vals[k] = float(v)
+    return vals
+
+
+def test_cache_sizes_printed_on_the_pages():
+    g = load_golden("cache_sizes.txt")
+    v2 = dict(n_h=128, d_h=128, d_c=512, d_r=64)
+    assert O.cache_elems_per_token("mla", 1, d_c=512, d_r=64) == g["mla_row_elems_v2"]
+    assert O.cache_elems_per_token("mha", 60, n_h=128, d_h=128) == g["mha_elems_per_token_v2"]
+    assert O.cache_elems_per_token("mqa", 60, d_h=128) == g["mqa_elems_per_token_v2"]
+    mla = O.cache_elems_per_token("mla", 60, d_c=v2["d_c"], d_r=v2["d_r"])
+    assert mla == g["mla_elems_per_token_v2"]
+    assert mla / O.cache_elems_per_token("gqa", 60, n_g=1, d_h=128) == g["mla_equivalent_gqa_groups"]
+    ds67 = O.cache_elems_per_token("gqa", 95, n_g=8, d_h=128)
+    assert ds67 == g["ds67b_gqa8_elems_per_token"]
+    assert ds67 * 2 / 1024 == g["ds67b_gqa8_bf16_kib"]
+    v2_bytes = mla * 6 / 8
+    assert v2_bytes == g["v2_6bit_bytes_per_token"]
+    assert round(v2_bytes / 1024, 1) == g["v2_6bit_kib"]
+    ratio = 100 * (v2_bytes / 1024) / (ds67 * 2 / 1024)
+    assert round(ratio, 1) == g["v2_cache_ratio_percent"]
+    assert round(100 - ratio, 1) == g["v2_cache_reduction_percent"]
+    # toy module: hidden 768, 96 heads of 8, d_c 64, d_h^R 16
+    assert 2 * 768 * 768 == g["toy_mha_kv_proj_params"]
+    assert 768 * 64 + 64 * 768 + 64 * 768 + 768 * 16 == g["toy_mla_kv_path_params"]
+    assert O.cache_elems_per_token("mha", 1, n_h=96, d_h=8) == g["toy_mha_cache_per_token"]
+    assert O.cache_elems_per_token("mla", 1, d_c=64, d_r=16) == g["toy_mla_cache_per_token"]

@@ -1,0 +1,84 @@
+"""The seeded input generator: rounding, draw order, shapes and logit statistics."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mla_latent_kv_20_amd import workloads as W
+
+
+def test_bf16_rounding_known_values():
+    cases = {
+        1.0: 0x3F80,
+        1.0 + 2.0 ** -8: 0x3F80,              # halfway, ties to the even mantissa 0
+        1.0 + 3 * 2.0 ** -8: 0x3F82,          # halfway between mantissas 1 and 2 -> 2
+        1.0 + 2.0 ** -8 + 2.0 ** -30: 0x3F81,  # just above halfway rounds up (no fp32 detour)
+        -2.5: 0xC020,
+        0.0: 0x0000,
+        3.0e38: 0x7F62,
+    }
+    got = W.bf16_bits_from_f64(np.array(list(cases.keys())))
+    assert [int(v) for v in got] == list(cases.values())
+    assert W.f64_from_bf16_bits(np.array([0x3F82], np.uint16))[0] == 1.0 + 2.0 ** -6
+
+
+def test_bf16_rounding_matches_torch_for_fp32_inputs():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    ours = W.bf16_bits_from_f64(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_chunked_draws_equal_one_shot_draws(monkeypatch):
+    monkeypatch.setattr(W, "_DRAW_CHUNK_ROWS", 7)
+    a = W._draw_rows(np.random.default_rng(5), 50, 9, 1.0, W.BF16)
+    b = W.round_to_storage(np.random.default_rng(5).standard_normal((50, 9)), W.BF16)
+    assert np.array_equal(a, b)
+
+
+def test_tiny_config_literal_padded_draw():
+    w = W.make_config("tiny_f32")
+    assert list(w.lengths) == [64, 37] and list(w.offsets) == [0, 64, 101]
+    rng = np.random.default_rng(0)
+    pad_c = rng.standard_normal((2, 64, 32))
+    assert np.array_equal(w.c_kv[:64], pad_c[0].astype(np.float32))
+    assert np.array_equal(w.c_kv[64:], pad_c[1, :37].astype(np.float32))
+    assert w.c_kv.dtype == np.float32 and w.q_c.shape == (2, 4, 16) and w.w_uk.shape == (4, 16, 32)
+
+
+def test_ragged_lengths_are_drawn_first_and_in_range():
+    w = W.make_workload("r", n_h=4, d_h=8, d_c=16, d_r=8, dtype=W.BF16, ragged_range=(512, 16384),
+                        ragged_batch=128, seed=0)
+    want = np.random.default_rng(0).integers(512, 16385, size=128)
+    assert np.array_equal(w.lengths, want)
+    assert w.lengths.min() >= 512 and w.lengths.max() <= 16384
+    assert np.array_equal(np.diff(w.offsets), w.lengths) and w.offsets[0] == 0
+
+
+def test_appended_rows_layout():
+    w = W.make_config("dsv2_small_mtp")
+    assert list(w.lengths) == [7, 254] and w.q_per_seq == 4 and w.n_q == 8
+    assert w.cached_rows() == 3 + 250
+    assert w.c_kv.shape == (261, 512) and w.k_r.shape == (261, 64)
+
+
+def _logits(w, rows=None):
+    qa = O.absorb_q(w.f64("q_c"), w.f64("q_r"), w.f64("w_uk"))
+    X = np.concatenate([w.f64("c_kv"), w.f64("k_r")], axis=1)
+    lo, hi = int(w.offsets[0]), int(w.offsets[1])
+    return (X[lo:hi] @ qa[0].T) * O.default_scale(w.d_h, w.d_r)
+
+
+@pytest.mark.parametrize("q_mult,lo,hi", [(1.0, 0.9, 1.1), (3.0, 2.7, 3.3)])
+def test_logit_std_matches_the_workload_description(q_mult, lo, hi):
+    """Unit-variance draws with W ~ N(0, 1/d_c) give logit variance (d_h*1 + d_r)/(d_h + d_r) = 1."""
+    w = W.make_workload("s", **W.DSV2, dtype=W.BF16, lengths=[2048], q_mult=q_mult, seed=0)
+    s = _logits(w)
+    assert lo <= s.std() <= hi
+
+
+def test_tiny_config_logit_std_near_one():
+    s = _logits(W.make_config("tiny_f32"))
+    assert 0.7 <= s.std() <= 1.3
