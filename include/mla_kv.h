@@ -1,0 +1,194 @@
+/*
+ * mla_kv.h - C ABI of the MLA absorbed-decode library for MI355X (gfx950).
+ *
+ * Multi-head Latent Attention decode over a compressed KV cache with the
+ * up-projections absorbed.  Pages cited (title, then section / equation):
+ *   [notes]  "MLA(Multi-head Latent Attention): DeepSeek-V2 논문정리"
+ *   [report] "Техотчёт DeepSeek-V2 (2024): MLA и экономика инференса"
+ *   [review] "DeepSeek-V2 review" (velog.io/@jmsong62)
+ *   [v3]     DeepSeek-V3 Technical Report notes (xuxeong.tistory.com)
+ *
+ * Each cached token holds one latent row [c^KV (d_c) ; k^R (d_r)]: the
+ * compressed latent of eq. 9 [notes] and the shared decoupled RoPE key, cached
+ * already rotated ([notes] "Decoupled Rotary Position Embedding"; [report]
+ * "Идея 2").  One decode step is four calls:
+ *
+ *   mla_absorb_q      q_abs = [W^UK_i^T q^C_i ; q^R_i]          (key absorption)
+ *   mla_decode        per split of the rows: softmax(q_abs . row * scale)
+ *                     weighted sum of c^KV, plus its log-sum-exp
+ *   mla_merge_splits  log-sum-exp weighted combination of the splits
+ *   mla_out_proj      o^C_i = W^UV_i o_lat_i                     (value absorption)
+ *
+ * Together they compute, for query t and head i,
+ *   o_{t,i} = sum_j softmax_j(q_{t,i}^T k_{j,i} * scale) v^C_{j,i}
+ * with k_{j,i} = [W^UK_i c^KV_j ; k^R_j], v^C_{j,i} = W^UV_i c^KV_j and
+ * scale = 1/sqrt(d_h + d_r) ([v3] eq. 10; [report] "Идея 2").
+ *
+ * Conventions shared by every call
+ *  - All tensor arguments are device pointers, row-major, densely packed unless
+ *    a stride is given.  The caller owns every buffer; the library allocates
+ *    nothing and keeps no state.  Outputs must not overlap inputs.
+ *  - Every call only enqueues work on `stream` (0 = the null stream) and
+ *    returns; it never synchronizes.  Calls on one stream run in order.
+ *  - Arguments are checked on the host before anything is launched; a failed
+ *    check returns its MLA_ERR_* code and launches nothing.  MLA_ERR_LAUNCH
+ *    reports a HIP launch error.  No call aborts or throws.
+ *  - A size of zero (n_q == 0, batch == 0) is a valid no-op.
+ *  - dtype MLA_BF16 runs the MFMA kernels (bf16 operands, fp32 accumulation);
+ *    they need d_c == 512, d_r == 64, n_h % 32 == 0 and d_h % 32 == 0 (the
+ *    DeepSeek-V2 attention shape) and 16-byte aligned rows, and return
+ *    MLA_ERR_UNSUPPORTED for other shapes.  dtype MLA_F32 runs plain fp32
+ *    kernels for any shape (no bf16 rounding anywhere).
+ */
+#ifndef MLA_KV_H_
+#define MLA_KV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,         /* a required pointer is NULL */
+  MLA_ERR_SHAPE = 2,        /* a size, count or stride is out of range */
+  MLA_ERR_ALIGN = 3,        /* a pointer or stride breaks the alignment rule */
+  MLA_ERR_DTYPE = 4,        /* dims->dtype is not an mla_dtype_t value */
+  MLA_ERR_UNSUPPORTED = 5,  /* valid arguments this build has no kernel for */
+  MLA_ERR_LAUNCH = 6        /* a HIP launch failed (see hipGetLastError) */
+} mla_status_t;
+
+typedef enum mla_dtype {
+  MLA_F32 = 0,              /* float32 storage and arithmetic */
+  MLA_BF16 = 1              /* bfloat16 storage, fp32 accumulation */
+} mla_dtype_t;
+
+/* Attention dimensions ([review] 4.1; [v3] MLA dimension list). */
+typedef struct mla_dims {
+  int32_t n_h;              /* query heads (DeepSeek-V2: 128) */
+  int32_t d_h;              /* per-head width of q^C, k^C, v^C (128) */
+  int32_t d_c;              /* latent width of c^KV (512) */
+  int32_t d_r;              /* decoupled RoPE width d_h^R of q^R and k^R (64) */
+  int32_t dtype;            /* mla_dtype_t of every non-fp32 tensor below */
+  float softmax_scale;      /* > 0: used as given; <= 0: 1/sqrt(d_h + d_r) */
+} mla_dims_t;
+
+/* Library ABI version (MLA_ABI_VERSION of the build). */
+int32_t mla_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* mla_status_string(mla_status_t status);
+
+/*
+ * mla_absorb_q - fold W^UK into the query ([notes] "Key에 대한 수식 전개";
+ * [report] "Идея 1") and append the RoPE part unchanged ([notes] "Decoupled
+ * Rotary Position Embedding", item 4: [a;b].[c;d] = a.c + b.d).
+ *
+ *   q_abs[n, i, 0:d_c]       = sum_d q_c[n, i, d] * w_uk[i, d, :]
+ *   q_abs[n, i, d_c:d_c+d_r] = q_r[n, i, :]
+ *
+ *   q_c   [n_q, n_h, d_h]        dtype      per-head content query q^C
+ *   q_r   [n_q, n_h, d_r]        dtype      per-head RoPE query, already rotated
+ *   w_uk  [n_h, d_h, d_c]        dtype      W^UK_i as [d_h, d_c] per head
+ *   q_abs [n_q, n_h, d_c + d_r]  dtype      out; bf16 is rounded once from fp32
+ */
+mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t n_q,
+                          const void* q_c, const void* q_r, const void* w_uk,
+                          void* q_abs, hipStream_t stream);
+
+/* Bytes of o_part for (n_q, num_splits): num_splits * n_q * n_h * d_c * 4.
+ * lse_part holds num_splits * n_q * n_h floats.  Returns 0 on bad arguments. */
+size_t mla_partial_bytes(const mla_dims_t* dims, int32_t n_q, int32_t num_splits);
+
+/*
+ * mla_decode - attention of every query head over the latent rows, one result
+ * per split of the rows.
+ *
+ * Sequence b owns cache rows seq_offsets[b] .. seq_offsets[b+1]-1 (len_b rows,
+ * the q_per_seq newest of them being this step's own tokens when q_per_seq > 1).
+ * Query r (0 <= r < q_per_seq) of sequence b is query n = b*q_per_seq + r and
+ * sees the first vis = len_b - q_per_seq + r + 1 rows (the generalized causal
+ * mask of [notes] "MLA 코드 구현", triu with diagonal T_k - T_q + 1).  Row j's
+ * key is the whole row [c_kv_j ; k_r_j], shared by all heads; its value is c_kv_j.
+ *
+ * Split s covers visible rows [s*split_rows, (s+1)*split_rows); the last split
+ * (s = num_splits-1) runs to the end of the visible rows; with num_splits == 1
+ * the single split covers all of them.  For each (s, n, i), with
+ * x_j = q_abs[n,i,:] . row_j * scale over the split's rows:
+ *   o_part[s, n, i, :] = sum_j softmax(x)_j * c_kv_j        (fp32)
+ *   lse_part[s, n, i]  = ln sum_j exp(x_j)                  (fp32, natural log)
+ * A split with no row gets o_part = 0 and lse_part = -inf.  With num_splits == 1
+ * the outputs already are the final o_lat and lse.
+ *
+ *   q_abs       [batch*q_per_seq, n_h, d_c+d_r]  dtype   from mla_absorb_q
+ *   c_kv        rows of d_c elements at a stride of c_stride elements  dtype
+ *   k_r         rows of d_r elements at a stride of r_stride elements  dtype
+ *               (packed rows: k_r = c_kv + d_c with r_stride == c_stride)
+ *   seq_offsets [batch+1] int64, device memory, nondecreasing, the last entry at
+ *               most the number of rows behind c_kv and k_r; every len_b must be
+ *               >= q_per_seq.  Not read on the host, so not checked here: use
+ *               mla_check_offsets on a host copy.
+ *   num_splits  >= 1;  split_rows >= 1 when num_splits > 1 (ignored otherwise)
+ *   o_part      [num_splits, batch*q_per_seq, n_h, d_c] fp32 out
+ *   lse_part    [num_splits, batch*q_per_seq, n_h] fp32 out
+ * bf16 streams whole 576-element rows, so it needs the packed row layout
+ * [c^KV ; k^R]: k_r == c_kv + d_c and r_stride == c_stride (else
+ * MLA_ERR_UNSUPPORTED); c_kv, q_abs and o_part 16-byte aligned, c_stride a
+ * multiple of 8.  fp32 takes separate c_kv / k_r tensors with any strides.
+ */
+mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, int32_t q_per_seq,
+                        const void* q_abs,
+                        const void* c_kv, int64_t c_stride,
+                        const void* k_r, int64_t r_stride,
+                        const int64_t* seq_offsets,
+                        int32_t num_splits, int32_t split_rows,
+                        float* o_part, float* lse_part, hipStream_t stream);
+
+/*
+ * mla_check_offsets - host-side check of a host copy of seq_offsets against
+ * the rules mla_decode relies on: offsets[0] >= 0, nondecreasing, every
+ * len_b >= q_per_seq, offsets[batch] <= total_rows.  Returns MLA_OK or
+ * MLA_ERR_SHAPE (MLA_ERR_NULL for a NULL array with batch > 0).
+ */
+mla_status_t mla_check_offsets(const int64_t* host_offsets, int32_t batch,
+                               int32_t q_per_seq, int64_t total_rows);
+
+/*
+ * mla_merge_splits - combine split results.  Softmax over a disjoint union of
+ * row sets: with M = max_s lse_s and w_s = exp(lse_s - M),
+ *   o_lat = sum_s w_s o_s / sum_s w_s,   lse = M + ln sum_s w_s.
+ * Splits with lse_s = -inf get weight 0; a query head whose every split is
+ * empty gets o_lat = 0 and lse = -inf.
+ *
+ *   o_part   [num_splits, n_q, n_h, d_c] fp32,  lse_part [num_splits, n_q, n_h] fp32
+ *   o_lat    [n_q, n_h, d_c] fp32 out,          lse      [n_q, n_h] fp32 out
+ * All four must be 16-byte aligned when d_c % 4 == 0.
+ */
+mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t n_q, int32_t num_splits,
+                              const float* o_part, const float* lse_part,
+                              float* o_lat, float* lse, hipStream_t stream);
+
+/*
+ * mla_out_proj - value absorption ([notes] "Value에 대한 수식 전개"): project
+ * the weighted latent once per head.
+ *
+ *   o_c[n, i, d] = sum_c w_uv[i, d, c] * o_lat[n, i, c]
+ *
+ *   o_lat [n_q, n_h, d_c] fp32   (bf16: rounded to bf16 as the MFMA operand)
+ *   w_uv  [n_h, d_h, d_c] dtype  W^UV_i as [d_h, d_c] per head
+ *   o_c   [n_q, n_h, d_h] dtype  out
+ */
+mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t n_q, const float* o_lat,
+                          const void* w_uv, void* o_c, hipStream_t stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* MLA_KV_H_ */

@@ -1,0 +1,204 @@
+"""Thin ctypes binding of the MLA decode C ABI (include/mla_kv.h).
+
+Argument marshalling only: every step runs in the HIP library ``libmla_kv.so``.
+Tensors are torch tensors on the GPU (torch supplies device memory and streams);
+each wrapper passes their device pointers and the current HIP stream through.
+Nothing here computes a result: a missing library raises instead of falling back.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_kv.so")
+
+MLA_OK = 0
+MLA_ERR_NULL = 1
+MLA_ERR_SHAPE = 2
+MLA_ERR_ALIGN = 3
+MLA_ERR_DTYPE = 4
+MLA_ERR_UNSUPPORTED = 5
+MLA_ERR_LAUNCH = 6
+MLA_F32 = 0
+MLA_BF16 = 1
+
+# Every entry point the header declares, with its ctypes signature.
+_I32, _I64, _F32, _P, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class MlaDims(ctypes.Structure):
+    _fields_ = [("n_h", _I32), ("d_h", _I32), ("d_c", _I32), ("d_r", _I32), ("dtype", _I32),
+                ("softmax_scale", _F32)]
+
+
+_DIMS_P = ctypes.POINTER(MlaDims)
+SIGNATURES = {
+    "mla_abi_version": (_I32, []),
+    "mla_status_string": (ctypes.c_char_p, [_I32]),
+    "mla_partial_bytes": (_SZ, [_DIMS_P, _I32, _I32]),
+    "mla_check_offsets": (_I32, [_P, _I32, _I32, _I64]),
+    "mla_absorb_q": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P, _P]),
+    "mla_decode": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _I64, _P, _I64, _P, _I32, _I32, _P, _P, _P]),
+    "mla_merge_splits": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _P]),
+    "mla_out_proj": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P]),
+}
+
+_lib = None
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libmla_kv.so (once).  Raises FileNotFoundError if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(f"{p} is missing: build it with `python -m mla_latent_kv_20_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().mla_status_string(status).decode()
+
+
+def dims(n_h: int, d_h: int, d_c: int, d_r: int, dtype: int, softmax_scale: float = 0.0) -> MlaDims:
+    return MlaDims(n_h, d_h, d_c, d_r, dtype, softmax_scale)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MLA_OK:
+        raise MlaError(fn, status)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    if t.dtype == torch.float32:
+        return MLA_F32
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def dims_for(q_c, q_r, w_uk, softmax_scale: float = 0.0) -> MlaDims:
+    """Dimensions read off the query and weight tensors ([n_q, n_h, d_h], [n_q, n_h, d_r], [n_h, d_h, d_c])."""
+    n_h, d_h, d_c = w_uk.shape
+    return dims(n_h, d_h, d_c, q_r.shape[-1], _dtype_code(q_c), softmax_scale)
+
+
+# ---------------------------------------------------------------------------
+# The four calls
+# ---------------------------------------------------------------------------
+
+def absorb_q(d: MlaDims, q_c, q_r, w_uk, q_abs=None, stream=None):
+    """q_abs[n, i] = [W^UK_i^T q_c[n, i] ; q_r[n, i]]  -> [n_q, n_h, d_c + d_r]."""
+    import torch
+    n_q = q_c.shape[0]
+    if q_abs is None:
+        q_abs = torch.empty((n_q, d.n_h, d.d_c + d.d_r), dtype=q_c.dtype, device=q_c.device)
+    _check("mla_absorb_q", load().mla_absorb_q(ctypes.byref(d), n_q, _ptr(q_c), _ptr(q_r), _ptr(w_uk),
+                                                _ptr(q_abs), _stream(stream)))
+    return q_abs
+
+
+def decode(d: MlaDims, q_abs, c_kv, k_r, offsets, batch: int, q_per_seq: int = 1,
+           num_splits: int = 1, split_rows: int = 0, o_part=None, lse_part=None, stream=None):
+    """Split-KV attention in latent space -> (o_part [S, n_q, n_h, d_c], lse_part [S, n_q, n_h]).
+
+    ``c_kv`` and ``k_r`` are 2-D row views (their row strides are passed through); for the
+    bf16 path they must be the two column ranges of one packed [rows, d_c + d_r] cache.
+    ``offsets`` is an int64 device tensor [batch + 1].
+    """
+    import torch
+    n_q = batch * q_per_seq
+    if o_part is None:
+        o_part = torch.empty((num_splits, n_q, d.n_h, d.d_c), dtype=torch.float32, device=q_abs.device)
+    if lse_part is None:
+        lse_part = torch.empty((num_splits, n_q, d.n_h), dtype=torch.float32, device=q_abs.device)
+    _check("mla_decode", load().mla_decode(
+        ctypes.byref(d), batch, q_per_seq, _ptr(q_abs), _ptr(c_kv), int(c_kv.stride(0)), _ptr(k_r),
+        int(k_r.stride(0)), _ptr(offsets), num_splits, split_rows, _ptr(o_part), _ptr(lse_part),
+        _stream(stream)))
+    return o_part, lse_part
+
+
+def merge_splits(d: MlaDims, o_part, lse_part, o_lat=None, lse=None, stream=None):
+    """Log-sum-exp merge of split results -> (o_lat [n_q, n_h, d_c], lse [n_q, n_h])."""
+    import torch
+    S, n_q = o_part.shape[0], o_part.shape[1]
+    if o_lat is None:
+        o_lat = torch.empty((n_q, d.n_h, d.d_c), dtype=torch.float32, device=o_part.device)
+    if lse is None:
+        lse = torch.empty((n_q, d.n_h), dtype=torch.float32, device=o_part.device)
+    _check("mla_merge_splits", load().mla_merge_splits(ctypes.byref(d), n_q, S, _ptr(o_part),
+                                                        _ptr(lse_part), _ptr(o_lat), _ptr(lse),
+                                                        _stream(stream)))
+    return o_lat, lse
+
+
+def out_proj(d: MlaDims, o_lat, w_uv, o_c=None, out_dtype=None, stream=None):
+    """o_c[n, i] = W^UV_i o_lat[n, i]  -> [n_q, n_h, d_h] in the weights' dtype."""
+    import torch
+    n_q = o_lat.shape[0]
+    if o_c is None:
+        o_c = torch.empty((n_q, d.n_h, d.d_h), dtype=out_dtype or w_uv.dtype, device=o_lat.device)
+    _check("mla_out_proj", load().mla_out_proj(ctypes.byref(d), n_q, _ptr(o_lat), _ptr(w_uv), _ptr(o_c),
+                                                _stream(stream)))
+    return o_c
+
+
+def check_offsets(host_offsets, batch: int, q_per_seq: int, total_rows: int) -> int:
+    """mla_check_offsets on a host int64 numpy array; returns the status code."""
+    import numpy as np
+    a = np.ascontiguousarray(host_offsets, dtype=np.int64)
+    return int(load().mla_check_offsets(a.ctypes.data if a.size else None, batch, q_per_seq, total_rows))
+
+
+def decode_step(d: MlaDims, q_c, q_r, w_uk, w_uv, cache, offsets, batch: int, q_per_seq: int = 1,
+                num_splits: int = 1, split_rows: int = 0, bufs: Optional[dict] = None, stream=None):
+    """All four calls on one packed cache [rows, d_c + d_r]; returns the output buffers.
+
+    ``bufs`` may hold preallocated q_abs / o_part / lse_part / o_lat / lse / o_c tensors.
+    """
+    b = {} if bufs is None else bufs
+    q_abs = absorb_q(d, q_c, q_r, w_uk, b.get("q_abs"), stream)
+    c_kv = cache[:, :d.d_c]
+    k_r = cache[:, d.d_c:d.d_c + d.d_r]
+    o_part, lse_part = decode(d, q_abs, c_kv, k_r, offsets, batch, q_per_seq, num_splits, split_rows,
+                              b.get("o_part"), b.get("lse_part"), stream)
+    if num_splits == 1:
+        o_lat, lse = o_part[0], lse_part[0]
+    else:
+        o_lat, lse = merge_splits(d, o_part, lse_part, b.get("o_lat"), b.get("lse"), stream)
+    o_c = out_proj(d, o_lat, w_uv, b.get("o_c"), stream=stream)
+    return dict(q_abs=q_abs, o_part=o_part, lse_part=lse_part, o_lat=o_lat, lse=lse, o_c=o_c)
+
+
+def default_scale(d_h: int, d_r: int) -> float:
+    return 1.0 / math.sqrt(d_h + d_r)

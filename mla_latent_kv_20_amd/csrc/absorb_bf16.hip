@@ -1,0 +1,203 @@
+// The two weight-absorption GEMMs of MLA decode, bf16 MFMA on gfx950.
+//
+// Pages cited: [notes] "MLA(Multi-head Latent Attention): DeepSeek-V2 논문정리";
+// [report] "Техотчёт DeepSeek-V2 (2024): MLA и экономика инференса".
+//
+// absorb_q (key absorption, [notes] "Key에 대한 수식 전개"; [report] "Идея 1"):
+//   q_abs[n, i, 0:d_c] = q_c[n, i, :] . W^UK_i        per head: [n_q x d_h] x [d_h x d_c]
+//   q_abs[n, i, d_c:]  = q_r[n, i, :]                 ([notes] "Decoupled Rotary ...", item 4)
+// out_proj (value absorption, [notes] "Value에 대한 수식 전개"):
+//   o_c[n, i, :] = W^UV_i o_lat[n, i, :]              per head: [n_q x d_c] x [d_c x d_h]
+//
+// Both stream one weight matrix per head (128 x 512 bf16 = 128 KiB) and are bound by that
+// weight traffic at decode batch sizes.  Each workgroup keeps its weight slice in MFMA B
+// operands and sweeps all query rows over it, so every weight byte is read once.
+#include "mla_common.h"
+
+namespace mla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+
+// ---------------------------------------------------------------------------
+// absorb_q: workgroup = (head i, block of 128 latent columns); wave w owns 32 columns.
+// W^UK rows are [d_h][d_c] with d_c contiguous, but the MFMA B operand needs 8
+// consecutive d_h values per lane, so the slice is staged in LDS and read with the
+// transposing LDS read.
+// ---------------------------------------------------------------------------
+constexpr int kAbsCols = 128;
+constexpr int kAbsPitch = kAbsCols * 2 + 32;   // 288 B: 4 rows x 32 B of a transpose read hit distinct banks
+
+struct AbsorbParams {
+  const bf16_bits* q_c;   // [n_q, n_h, d_h]
+  const bf16_bits* q_r;   // [n_q, n_h, d_r]
+  const bf16_bits* w_uk;  // [n_h, d_h, d_c]
+  bf16_bits* q_abs;       // [n_q, n_h, d_c + d_r]
+  int n_q, n_h, d_h, d_c, d_r;
+};
+
+__global__ void __launch_bounds__(kThreads)
+absorb_q_bf16_kernel(AbsorbParams P) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int i = blockIdx.y;                       // head
+  const int cb = blockIdx.x * kAbsCols;           // first latent column of this block
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int d_qk = P.d_c + P.d_r;
+
+  // RoPE part: copied once per head, by the first column block.
+  if (blockIdx.x == 0) {
+    for (int e = tid; e < P.n_q * P.d_r; e += kThreads) {
+      const int n = e / P.d_r, c = e - n * P.d_r;
+      P.q_abs[((size_t)n * P.n_h + i) * d_qk + P.d_c + c] = P.q_r[((size_t)n * P.n_h + i) * P.d_r + c];
+    }
+  }
+
+  // Stage W^UK_i[:, cb:cb+128] in LDS (16-byte chunks, 16 per row).
+  const bf16_bits* w = P.w_uk + (size_t)i * P.d_h * P.d_c + cb;
+  for (int e = tid; e < P.d_h * (kAbsCols / 8); e += kThreads) {
+    const int r = e >> 4, c = e & 15;
+    *(bf16x8*)(smem + r * kAbsPitch + c * 16) = *(const bf16x8*)(w + (size_t)r * P.d_c + c * 8);
+  }
+  __syncthreads();
+
+  // B operands for every k-step: lane l gets W[16s + 8(l/32) + j][32w + l%32], j = 0..7.
+  const int ksteps = P.d_h / 16;                  // <= 16 (d_h <= 256)
+  bf16x8 wb[16];
+  {
+    const int g = lane >> 4;                      // 16-lane group
+    const int col = 32 * wave + 16 * (g & 1) + 4 * (lane & 3);
+    const int row = 8 * (g >> 1) + ((lane & 15) >> 2);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      if (s < ksteps) {
+        const char* p = smem + (16 * s + row) * kAbsPitch + col * 2;
+        const i16x4 lo4 = lds_read_tr16(p);
+        const i16x4 hi4 = lds_read_tr16(p + 4 * kAbsPitch);
+        const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        wb[s] = __builtin_bit_cast(bf16x8, v8);
+      }
+    }
+  }
+
+  // Sweep the query rows 32 at a time.
+  for (int mb = 0; mb < P.n_q; mb += 32) {
+    const int m = mb + (lane & 31);
+    const bool mrow = m < P.n_q;
+    const bf16_bits* q = P.q_c + ((size_t)(mrow ? m : 0) * P.n_h + i) * P.d_h + 8 * (lane >> 5);
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      if (s < ksteps) {
+        bf16x8 a = *(const bf16x8*)(q + 16 * s);
+        if (!mrow) a = bf16x8{};
+        acc = mfma32x32x16(a, wb[s], acc);
+      }
+    }
+    // D[m][n]: lane l, reg r -> row 8(r/4) + 4(l/32) + r%4, column l%32
+    const int col = cb + 32 * wave + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int mm = mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (mm < P.n_q) P.q_abs[((size_t)mm * P.n_h + i) * d_qk + col] = f32_to_bf16(acc[r]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// out_proj: workgroup = (head i, 32 output columns of d_h); the 4 waves split the d_c
+// reduction and add their partial tiles through LDS.  W^UV_i rows are [d_h][d_c] with
+// d_c (the reduction index) contiguous: B operands load straight from global memory.
+// ---------------------------------------------------------------------------
+struct OutProjParams {
+  const float* o_lat;     // [n_q, n_h, d_c]
+  const bf16_bits* w_uv;  // [n_h, d_h, d_c]
+  bf16_bits* o_c;         // [n_q, n_h, d_h]
+  int n_q, n_h, d_h, d_c;
+};
+
+constexpr int kOutMaxSteps = 8;   // k-steps per wave: d_c <= 4 * 8 * 16 = 512
+
+__global__ void __launch_bounds__(kThreads)
+out_proj_bf16_kernel(OutProjParams P) {
+  __shared__ float red[kWaves][32][33];
+  const int i = blockIdx.y;
+  const int nb = blockIdx.x * 32;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int steps = P.d_c / 16 / kWaves;          // k-steps of this wave
+  const int k0 = wave * steps * 16;
+
+  bf16x8 wb[kOutMaxSteps];
+  {
+    const bf16_bits* w = P.w_uv + ((size_t)i * P.d_h + nb + (lane & 31)) * P.d_c + k0 + 8 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < kOutMaxSteps; ++s)
+      if (s < steps) wb[s] = *(const bf16x8*)(w + 16 * s);
+  }
+
+  for (int mb = 0; mb < P.n_q; mb += 32) {
+    const int m = mb + (lane & 31);
+    const bool mrow = m < P.n_q;
+    const float* a = P.o_lat + ((size_t)(mrow ? m : 0) * P.n_h + i) * P.d_c + k0 + 8 * (lane >> 5);
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < kOutMaxSteps; ++s) {
+      if (s < steps) {
+        const f32x4 x0 = *(const f32x4*)(a + 16 * s);
+        const f32x4 x1 = *(const f32x4*)(a + 16 * s + 4);
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 pk = {pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
+                    pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
+        if (!mrow) pk = u32x4{0u, 0u, 0u, 0u};
+        acc = mfma32x32x16(__builtin_bit_cast(bf16x8, pk), wb[s], acc);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wave][8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)][lane & 31] = acc[r];
+    __syncthreads();
+    for (int e = tid; e < 32 * 32; e += kThreads) {
+      const int row = e >> 5, col = e & 31;
+      const int mm = mb + row;
+      if (mm < P.n_q) {
+        const float v = red[0][row][col] + red[1][row][col] + red[2][row][col] + red[3][row][col];
+        P.o_c[((size_t)mm * P.n_h + i) * P.d_h + nb + col] = f32_to_bf16(v);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+bool absorb_bf16_supported(int d_h, int d_c) {
+  return d_h % 16 == 0 && d_h <= 256 && d_c % kAbsCols == 0;
+}
+bool out_proj_bf16_supported(int d_h, int d_c) {
+  return d_h % 32 == 0 && d_c % (16 * kWaves) == 0 && d_c <= 16 * kWaves * kOutMaxSteps;
+}
+
+hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, const bf16_bits* w_uk,
+                                bf16_bits* q_abs, int n_q, int n_h, int d_h, int d_c, int d_r,
+                                hipStream_t stream) {
+  AbsorbParams P{q_c, q_r, w_uk, q_abs, n_q, n_h, d_h, d_c, d_r};
+  const size_t smem = (size_t)d_h * kAbsPitch;
+  hipLaunchKernelGGL(absorb_q_bf16_kernel, dim3(d_c / kAbsCols, n_h), dim3(kThreads), smem, stream, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_out_proj_bf16(const float* o_lat, const bf16_bits* w_uv, bf16_bits* o_c, int n_q,
+                                int n_h, int d_h, int d_c, hipStream_t stream) {
+  OutProjParams P{o_lat, w_uv, o_c, n_q, n_h, d_h, d_c};
+  hipLaunchKernelGGL(out_proj_bf16_kernel, dim3(d_h / 32, n_h), dim3(kThreads), 0, stream, P);
+  return hipGetLastError();
+}
+
+}  // namespace mla

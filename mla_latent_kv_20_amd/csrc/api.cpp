@@ -1,0 +1,201 @@
+// C ABI of the MLA absorbed-decode library: argument checks and kernel dispatch.
+// Every check runs before anything is launched; a failed check returns its status.
+#include "../../include/mla_kv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+namespace mla {
+typedef uint16_t bf16_bits;
+// kernels (decode_bf16.hip, absorb_bf16.hip, merge_f32.hip)
+hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* c_kv, int64_t c_stride,
+                              const bf16_bits* k_r, int64_t r_stride, const int64_t* offsets,
+                              float* o_part, float* lse_part, int batch, int q_per_seq, int n_h,
+                              int num_splits, int split_rows, float scale, hipStream_t stream);
+hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, const bf16_bits* w_uk,
+                                bf16_bits* q_abs, int n_q, int n_h, int d_h, int d_c, int d_r,
+                                hipStream_t stream);
+hipError_t launch_out_proj_bf16(const float* o_lat, const bf16_bits* w_uv, bf16_bits* o_c, int n_q,
+                                int n_h, int d_h, int d_c, hipStream_t stream);
+bool absorb_bf16_supported(int d_h, int d_c);
+bool out_proj_bf16_supported(int d_h, int d_c);
+hipError_t launch_merge(const float* o_part, const float* lse_part, float* o_lat, float* lse, int n_q,
+                        int n_h, int d_c, int num_splits, hipStream_t stream);
+hipError_t launch_absorb_q_f32(const float* q_c, const float* q_r, const float* w_uk, float* q_abs,
+                               int n_q, int n_h, int d_h, int d_c, int d_r, hipStream_t stream);
+size_t decode_f32_smem_bytes(int d_c, int d_r);
+hipError_t launch_decode_f32(const float* q_abs, const float* c_kv, int64_t c_stride, const float* k_r,
+                             int64_t r_stride, const int64_t* offsets, float* o_part, float* lse_part,
+                             int batch, int q_per_seq, int n_h, int d_c, int d_r, int num_splits,
+                             int split_rows, float scale, hipStream_t stream);
+hipError_t launch_out_proj_f32(const float* o_lat, const float* w_uv, float* o_c, int n_q, int n_h,
+                               int d_h, int d_c, hipStream_t stream);
+}  // namespace mla
+
+namespace {
+
+// The bf16 decode kernel's fixed shape: 576-wide rows (512 latent + 64 RoPE), heads in
+// groups of 32 per wave.
+constexpr int kDecodeDc = 512;
+constexpr int kDecodeDr = 64;
+constexpr int64_t kMaxElems = (int64_t)1 << 31;   // any one tensor: < 2^31 elements per index
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+mla_status_t check_dims(const mla_dims_t* d) {
+  if (!d) return MLA_ERR_NULL;
+  if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (d->n_h <= 0 || d->d_h <= 0 || d->d_c <= 0 || d->d_r <= 0) return MLA_ERR_SHAPE;
+  if (d->n_h > 65535 || d->d_h > 65536 || d->d_c > 65536 || d->d_r > 65536) return MLA_ERR_SHAPE;
+  if (d->d_r % 2) return MLA_ERR_SHAPE;       // RoPE pairs
+  if (!(d->softmax_scale == d->softmax_scale) || std::isinf(d->softmax_scale)) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+float scale_of(const mla_dims_t* d) {
+  return d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / std::sqrt((double)(d->d_h + d->d_r)));
+}
+
+size_t esize(const mla_dims_t* d) { return d->dtype == MLA_BF16 ? 2 : 4; }
+
+mla_status_t launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(mla_status_t s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "a size, count or stride is out of range";
+    case MLA_ERR_ALIGN: return "a pointer or stride is not aligned as required";
+    case MLA_ERR_DTYPE: return "unknown dtype";
+    case MLA_ERR_UNSUPPORTED: return "no kernel in this build for these arguments";
+    case MLA_ERR_LAUNCH: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t mla_partial_bytes(const mla_dims_t* dims, int32_t n_q, int32_t num_splits) {
+  if (check_dims(dims) != MLA_OK || n_q < 0 || num_splits < 1) return 0;
+  return (size_t)num_splits * (size_t)n_q * (size_t)dims->n_h * (size_t)dims->d_c * sizeof(float);
+}
+
+mla_status_t mla_check_offsets(const int64_t* host_offsets, int32_t batch, int32_t q_per_seq,
+                               int64_t total_rows) {
+  if (batch < 0 || q_per_seq < 1 || total_rows < 0) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!host_offsets) return MLA_ERR_NULL;
+  if (host_offsets[0] < 0) return MLA_ERR_SHAPE;
+  for (int32_t b = 0; b < batch; ++b)
+    if (host_offsets[b + 1] - host_offsets[b] < q_per_seq) return MLA_ERR_SHAPE;
+  if (host_offsets[batch] > total_rows) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t n_q, const void* q_c, const void* q_r,
+                          const void* w_uk, void* q_abs, hipStream_t stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_q < 0) return MLA_ERR_SHAPE;
+  if (n_q == 0) return MLA_OK;
+  if (!q_c || !q_r || !w_uk || !q_abs) return MLA_ERR_NULL;
+  const int64_t d_qk = (int64_t)dims->d_c + dims->d_r;
+  if ((int64_t)n_q * dims->n_h * d_qk >= kMaxElems ||
+      (int64_t)dims->n_h * dims->d_h * dims->d_c >= kMaxElems)
+    return MLA_ERR_SHAPE;
+  const uintptr_t a = esize(dims);
+  if (!aligned(q_c, a) || !aligned(q_r, a) || !aligned(w_uk, a) || !aligned(q_abs, a)) return MLA_ERR_ALIGN;
+  if (dims->dtype == MLA_F32)
+    return launched(mla::launch_absorb_q_f32((const float*)q_c, (const float*)q_r, (const float*)w_uk,
+                                             (float*)q_abs, n_q, dims->n_h, dims->d_h, dims->d_c,
+                                             dims->d_r, stream));
+  if (!mla::absorb_bf16_supported(dims->d_h, dims->d_c) || dims->d_r % 8) return MLA_ERR_UNSUPPORTED;
+  if (!aligned(q_c, 16) || !aligned(w_uk, 16)) return MLA_ERR_ALIGN;
+  return launched(mla::launch_absorb_q_bf16((const uint16_t*)q_c, (const uint16_t*)q_r,
+                                            (const uint16_t*)w_uk, (uint16_t*)q_abs, n_q, dims->n_h,
+                                            dims->d_h, dims->d_c, dims->d_r, stream));
+}
+
+mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, int32_t q_per_seq, const void* q_abs,
+                        const void* c_kv, int64_t c_stride, const void* k_r, int64_t r_stride,
+                        const int64_t* seq_offsets, int32_t num_splits, int32_t split_rows,
+                        float* o_part, float* lse_part, hipStream_t stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || q_per_seq < 1 || num_splits < 1) return MLA_ERR_SHAPE;
+  if (num_splits > 1 && split_rows < 1) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!q_abs || !c_kv || !k_r || !seq_offsets || !o_part || !lse_part) return MLA_ERR_NULL;
+  if (c_stride < dims->d_c || r_stride < dims->d_r) return MLA_ERR_SHAPE;
+  const int64_t n_q = (int64_t)batch * q_per_seq;
+  if (n_q >= kMaxElems / dims->n_h || (int64_t)num_splits * n_q * dims->n_h * dims->d_c >= ((int64_t)1 << 40))
+    return MLA_ERR_SHAPE;
+  if ((int64_t)num_splits * n_q * dims->n_h >= kMaxElems) return MLA_ERR_SHAPE;
+  if (!aligned(seq_offsets, 8) || !aligned(o_part, 4) || !aligned(lse_part, 4)) return MLA_ERR_ALIGN;
+  const float scale = scale_of(dims);
+  if (dims->dtype == MLA_F32) {
+    if (!aligned(q_abs, 4) || !aligned(c_kv, 4) || !aligned(k_r, 4)) return MLA_ERR_ALIGN;
+    if (mla::decode_f32_smem_bytes(dims->d_c, dims->d_r) > 64 * 1024) return MLA_ERR_UNSUPPORTED;
+    if (num_splits > 65535 || n_q > 65535) return MLA_ERR_UNSUPPORTED;
+    return launched(mla::launch_decode_f32((const float*)q_abs, (const float*)c_kv, c_stride,
+                                           (const float*)k_r, r_stride, seq_offsets, o_part, lse_part,
+                                           batch, q_per_seq, dims->n_h, dims->d_c, dims->d_r,
+                                           num_splits, split_rows, scale, stream));
+  }
+  if (dims->d_c != kDecodeDc || dims->d_r != kDecodeDr || dims->n_h % 32) return MLA_ERR_UNSUPPORTED;
+  // The kernel streams whole 576-wide rows: the RoPE key must directly follow the latent.
+  const bool packed = (const char*)k_r == (const char*)c_kv + 2 * (size_t)dims->d_c && r_stride == c_stride;
+  if (!packed) return MLA_ERR_UNSUPPORTED;
+  if (!aligned(q_abs, 16) || !aligned(c_kv, 16) || c_stride % 8) return MLA_ERR_ALIGN;
+  if (!aligned(o_part, 16)) return MLA_ERR_ALIGN;
+  if (c_stride * 2 * 32 >= ((int64_t)1 << 31)) return MLA_ERR_SHAPE;
+  return launched(mla::launch_decode_bf16((const uint16_t*)q_abs, (const uint16_t*)c_kv, c_stride,
+                                          (const uint16_t*)k_r, r_stride, seq_offsets, o_part, lse_part,
+                                          batch, q_per_seq, dims->n_h, num_splits, split_rows, scale,
+                                          stream));
+}
+
+mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t n_q, int32_t num_splits,
+                              const float* o_part, const float* lse_part, float* o_lat, float* lse,
+                              hipStream_t stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_q < 0 || num_splits < 1) return MLA_ERR_SHAPE;
+  if (n_q == 0) return MLA_OK;
+  if (!o_part || !lse_part || !o_lat || !lse) return MLA_ERR_NULL;
+  if ((int64_t)n_q * dims->n_h >= kMaxElems || (int64_t)num_splits * n_q * dims->n_h >= kMaxElems)
+    return MLA_ERR_SHAPE;
+  const uintptr_t a = dims->d_c % 4 == 0 ? 16 : 4;
+  if (!aligned(o_part, a) || !aligned(o_lat, a) || !aligned(lse_part, 4) || !aligned(lse, 4))
+    return MLA_ERR_ALIGN;
+  return launched(mla::launch_merge(o_part, lse_part, o_lat, lse, n_q, dims->n_h, dims->d_c, num_splits,
+                                    stream));
+}
+
+mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t n_q, const float* o_lat, const void* w_uv,
+                          void* o_c, hipStream_t stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_q < 0) return MLA_ERR_SHAPE;
+  if (n_q == 0) return MLA_OK;
+  if (!o_lat || !w_uv || !o_c) return MLA_ERR_NULL;
+  if ((int64_t)n_q * dims->n_h * dims->d_c >= kMaxElems ||
+      (int64_t)dims->n_h * dims->d_h * dims->d_c >= kMaxElems)
+    return MLA_ERR_SHAPE;
+  if (!aligned(o_lat, 4) || !aligned(w_uv, esize(dims)) || !aligned(o_c, esize(dims))) return MLA_ERR_ALIGN;
+  if (dims->dtype == MLA_F32)
+    return launched(mla::launch_out_proj_f32(o_lat, (const float*)w_uv, (float*)o_c, n_q, dims->n_h,
+                                             dims->d_h, dims->d_c, stream));
+  if (!mla::out_proj_bf16_supported(dims->d_h, dims->d_c)) return MLA_ERR_UNSUPPORTED;
+  if (!aligned(o_lat, 16) || !aligned(w_uv, 16)) return MLA_ERR_ALIGN;
+  return launched(mla::launch_out_proj_bf16(o_lat, (const uint16_t*)w_uv, (uint16_t*)o_c, n_q,
+                                            dims->n_h, dims->d_h, dims->d_c, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,247 @@
+// Split-KV log-sum-exp merge and the plain fp32 kernels of the MLA decode library.
+//
+// Pages cited: [notes] "MLA(Multi-head Latent Attention): DeepSeek-V2 논문정리";
+// [report] "Техотчёт DeepSeek-V2 (2024): MLA и экономика инференса";
+// [v3] DeepSeek-V3 Technical Report notes (xuxeong.tistory.com).
+//
+// merge: softmax over the union of disjoint row sets.  With M = max_s lse_s and
+// w_s = exp(lse_s - M), o = sum_s w_s o_s / sum_s w_s and lse = M + ln sum_s w_s.
+//
+// The fp32 kernels compute the same four steps with no bf16 rounding, for any shape.
+// They are simple (one thread per output element, or one workgroup per query head)
+// and serve the fp32 dtype, whose use is exactness on small problems.
+#include "mla_common.h"
+
+namespace mla {
+namespace {
+
+// ---------------------------------------------------------------------------
+// merge: one workgroup per (query, head); threads sweep d_c four floats at a time.
+// ---------------------------------------------------------------------------
+constexpr int kMergeThreads = 128;
+
+__global__ void __launch_bounds__(kMergeThreads)
+merge_splits_kernel(const float* __restrict__ o_part, const float* __restrict__ lse_part,
+                    float* __restrict__ o_lat, float* __restrict__ lse, int qh_count, int d_c,
+                    int num_splits) {
+  const int qh = blockIdx.x;                      // n * n_h + i
+  float M = -INFINITY;
+  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, lse_part[(size_t)s * qh_count + qh]);
+  float* out = o_lat + (size_t)qh * d_c;
+  if (M == -INFINITY) {                           // no split saw a row
+    for (int c = threadIdx.x; c < d_c; c += kMergeThreads) out[c] = 0.f;
+    if (threadIdx.x == 0) lse[qh] = -INFINITY;
+    return;
+  }
+  float z = 0.f;
+  for (int s = 0; s < num_splits; ++s) z += expf(lse_part[(size_t)s * qh_count + qh] - M);
+  const float inv_z = 1.0f / z;
+  if ((d_c & 3) == 0) {
+    for (int c = 4 * threadIdx.x; c < d_c; c += 4 * kMergeThreads) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < num_splits; ++s) {
+        const float w = expf(lse_part[(size_t)s * qh_count + qh] - M);
+        const f32x4 v = *(const f32x4*)(o_part + ((size_t)s * qh_count + qh) * d_c + c);
+        acc += w * v;
+      }
+      *(f32x4*)(out + c) = acc * inv_z;
+    }
+  } else {
+    for (int c = threadIdx.x; c < d_c; c += kMergeThreads) {
+      float acc = 0.f;
+      for (int s = 0; s < num_splits; ++s)
+        acc += expf(lse_part[(size_t)s * qh_count + qh] - M) * o_part[((size_t)s * qh_count + qh) * d_c + c];
+      out[c] = acc * inv_z;
+    }
+  }
+  if (threadIdx.x == 0) lse[qh] = M + logf(z);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 absorb_q: one thread per output element.
+// ---------------------------------------------------------------------------
+__global__ void absorb_q_f32_kernel(const float* __restrict__ q_c, const float* __restrict__ q_r,
+                                    const float* __restrict__ w_uk, float* __restrict__ q_abs,
+                                    int n_q, int n_h, int d_h, int d_c, int d_r) {
+  const int d_qk = d_c + d_r;
+  const size_t total = (size_t)n_q * n_h * d_qk;
+  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total;
+       e += (size_t)gridDim.x * blockDim.x) {
+    const int c = (int)(e % d_qk);
+    const size_t ni = e / d_qk;                    // n * n_h + i
+    const int i = (int)(ni % n_h);
+    if (c < d_c) {
+      const float* q = q_c + ni * d_h;
+      const float* w = w_uk + (size_t)i * d_h * d_c + c;
+      float acc = 0.f;
+      for (int d = 0; d < d_h; ++d) acc = fmaf(q[d], w[(size_t)d * d_c], acc);
+      q_abs[e] = acc;
+    } else {
+      q_abs[e] = q_r[ni * d_r + (c - d_c)];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 decode: one workgroup per (query, split, head).  Rows go 256 at a time: each
+// thread scores one row, the block takes the max and the sum, and the latent
+// accumulator (in LDS) is rescaled and updated with the block's weights.
+// ---------------------------------------------------------------------------
+constexpr int kDecThreads = 256;
+
+__device__ float block_max(float v, float* red) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int k = 1; k < kDecThreads / 64; ++k) r = fmaxf(r, red[k]);
+  return r;
+}
+__device__ float block_sum(float v, float* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = 0.f;
+  for (int k = 0; k < kDecThreads / 64; ++k) r += red[k];
+  return r;
+}
+
+__global__ void __launch_bounds__(kDecThreads)
+decode_f32_kernel(const float* __restrict__ q_abs, const float* __restrict__ c_kv, int64_t c_stride,
+                  const float* __restrict__ k_r, int64_t r_stride, const int64_t* __restrict__ offsets,
+                  float* __restrict__ o_part, float* __restrict__ lse_part, int n_q, int n_h, int d_c,
+                  int d_r, int q_per_seq, int num_splits, int split_rows, float scale) {
+  extern __shared__ float sm[];
+  const int d_qk = d_c + d_r;
+  float* q = sm;                  // [d_qk]
+  float* o = q + d_qk;            // [d_c]
+  float* p = o + d_c;             // [256]
+  float* red = p + kDecThreads;   // [4]
+  const int i = blockIdx.x;
+  const int s = blockIdx.y;
+  const int n = blockIdx.z;
+  const int b = n / q_per_seq, r = n - b * q_per_seq;
+  const int64_t row0 = offsets[b];
+  const int64_t vis = offsets[b + 1] - row0 - q_per_seq + r + 1;
+  int64_t lo = 0, hi = vis;
+  if (num_splits > 1) {
+    lo = (int64_t)s * split_rows;
+    hi = (s == num_splits - 1) ? vis : lo + split_rows;
+    lo = lo < vis ? lo : vis;
+    hi = hi < vis ? hi : vis;
+  }
+  if (lo < 0) lo = 0;
+  const size_t qh = (size_t)n * n_h + i;
+  for (int c = threadIdx.x; c < d_qk; c += kDecThreads) q[c] = q_abs[qh * d_qk + c];
+  for (int c = threadIdx.x; c < d_c; c += kDecThreads) o[c] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  __syncthreads();
+  for (int64_t j0 = lo; j0 < hi; j0 += kDecThreads) {
+    const int64_t j = j0 + threadIdx.x;
+    float x = -INFINITY;
+    if (j < hi) {
+      const float* cr = c_kv + (row0 + j) * c_stride;
+      const float* rr = k_r + (row0 + j) * r_stride;
+      float acc = 0.f;
+      for (int c = 0; c < d_c; ++c) acc = fmaf(q[c], cr[c], acc);
+      for (int c = 0; c < d_r; ++c) acc = fmaf(q[d_c + c], rr[c], acc);
+      x = acc * scale;
+    }
+    const float mt = block_max(x, red);
+    const float m_new = fmaxf(m, mt);
+    const float alpha = expf(m - m_new);        // 0 on the first block (m = -inf)
+    const float pj = (j < hi) ? expf(x - m_new) : 0.f;
+    p[threadIdx.x] = pj;
+    const float lt = block_sum(pj, red);          // also orders the p[] writes
+    l = l * alpha + lt;
+    m = m_new;
+    const int cnt = (int)((hi - j0) < kDecThreads ? (hi - j0) : kDecThreads);
+    for (int c = threadIdx.x; c < d_c; c += kDecThreads) {
+      float acc = o[c] * alpha;
+      for (int jj = 0; jj < cnt; ++jj) acc = fmaf(p[jj], c_kv[(row0 + j0 + jj) * c_stride + c], acc);
+      o[c] = acc;
+    }
+    __syncthreads();
+  }
+  const size_t out = (size_t)s * n_q * n_h + qh;
+  if (hi <= lo) {
+    for (int c = threadIdx.x; c < d_c; c += kDecThreads) o_part[out * d_c + c] = 0.f;
+    if (threadIdx.x == 0) lse_part[out] = -INFINITY;
+    return;
+  }
+  const float inv = 1.0f / l;
+  for (int c = threadIdx.x; c < d_c; c += kDecThreads) o_part[out * d_c + c] = o[c] * inv;
+  if (threadIdx.x == 0) lse_part[out] = m + logf(l);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 out_proj: one thread per output element.
+// ---------------------------------------------------------------------------
+__global__ void out_proj_f32_kernel(const float* __restrict__ o_lat, const float* __restrict__ w_uv,
+                                    float* __restrict__ o_c, int n_q, int n_h, int d_h, int d_c) {
+  const size_t total = (size_t)n_q * n_h * d_h;
+  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total;
+       e += (size_t)gridDim.x * blockDim.x) {
+    const int d = (int)(e % d_h);
+    const size_t ni = e / d_h;
+    const int i = (int)(ni % n_h);
+    const float* a = o_lat + ni * d_c;
+    const float* w = w_uv + ((size_t)i * d_h + d) * d_c;
+    float acc = 0.f;
+    for (int c = 0; c < d_c; ++c) acc = fmaf(w[c], a[c], acc);
+    o_c[e] = acc;
+  }
+}
+
+unsigned grid_for(size_t total, int threads) {
+  size_t g = (total + threads - 1) / threads;
+  return (unsigned)(g < 65536 ? (g ? g : 1) : 65536);
+}
+
+}  // namespace
+
+hipError_t launch_merge(const float* o_part, const float* lse_part, float* o_lat, float* lse, int n_q,
+                        int n_h, int d_c, int num_splits, hipStream_t stream) {
+  const int qh = n_q * n_h;
+  hipLaunchKernelGGL(merge_splits_kernel, dim3(qh), dim3(kMergeThreads), 0, stream, o_part, lse_part,
+                     o_lat, lse, qh, d_c, num_splits);
+  return hipGetLastError();
+}
+
+hipError_t launch_absorb_q_f32(const float* q_c, const float* q_r, const float* w_uk, float* q_abs,
+                               int n_q, int n_h, int d_h, int d_c, int d_r, hipStream_t stream) {
+  const size_t total = (size_t)n_q * n_h * (d_c + d_r);
+  hipLaunchKernelGGL(absorb_q_f32_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream, q_c, q_r,
+                     w_uk, q_abs, n_q, n_h, d_h, d_c, d_r);
+  return hipGetLastError();
+}
+
+size_t decode_f32_smem_bytes(int d_c, int d_r) {
+  return sizeof(float) * ((size_t)2 * d_c + d_r + kDecThreads + 4);
+}
+
+hipError_t launch_decode_f32(const float* q_abs, const float* c_kv, int64_t c_stride, const float* k_r,
+                             int64_t r_stride, const int64_t* offsets, float* o_part, float* lse_part,
+                             int batch, int q_per_seq, int n_h, int d_c, int d_r, int num_splits,
+                             int split_rows, float scale, hipStream_t stream) {
+  const int n_q = batch * q_per_seq;
+  const size_t smem = decode_f32_smem_bytes(d_c, d_r);
+  hipLaunchKernelGGL(decode_f32_kernel, dim3(n_h, num_splits, n_q), dim3(kDecThreads), smem, stream,
+                     q_abs, c_kv, c_stride, k_r, r_stride, offsets, o_part, lse_part, n_q, n_h, d_c,
+                     d_r, q_per_seq, num_splits, split_rows, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_out_proj_f32(const float* o_lat, const float* w_uv, float* o_c, int n_q, int n_h,
+                               int d_h, int d_c, hipStream_t stream) {
+  const size_t total = (size_t)n_q * n_h * d_h;
+  hipLaunchKernelGGL(out_proj_f32_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream, o_lat,
+                     w_uv, o_c, n_q, n_h, d_h, d_c);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,106 @@
+// Shared device helpers for the gfx950 kernels of the MLA decode library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t bf16_bits;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bf16 <-> fp32, round to nearest even (finite inputs).
+__device__ __forceinline__ float bf16_to_f32(bf16_bits b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ bf16_bits f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_bits)(u >> 16);
+}
+// Two floats -> packed bf16 pair (low half = a), hardware RNE conversion.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// D = A x B + C for 32x32x16 bf16 MFMA (gfx950). Lane l holds A[l%32][8(l/32)+j],
+// B[8(l/32)+j][l%32] (j = 0..7) and D[8(r/4)+4(l/32)+r%4][l%32] (r = 0..15).
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read: within each 16-lane group, lane i receives element i%4 of
+// the 4-element vectors addressed by group lanes i/4, 4+i/4, 8+i/4, 12+i/4.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)lds_ptr);
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
+}
+
+// Asynchronous 16-byte global -> LDS copy; lane l's 16 bytes land at LDS address
+// lds_base + 16*l (lds_base wave-uniform).  Issued from asm so that the compiler
+// does not treat every later LDS read as dependent on it (it would otherwise wait
+// for all outstanding loads, including prefetches of later tiles); callers order
+// it with wait_vmcnt and lds_barrier.  The instruction writes no VGPR.
+__device__ __forceinline__ void global_to_lds16(const void* gptr, uint32_t lds_base) {
+  uint32_t saved_m0;
+  // M0 is reserved by the compiler, so the block restores it; the load reads M0 at issue.
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved_m0)
+      : "v"(gptr), "s"(lds_base)
+      : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier that also orders LDS traffic: every wave's LDS reads are
+// complete before any wave passes.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// a *= alpha for an MFMA accumulator that lives in AGPRs.  VALU arithmetic cannot
+// read AGPRs, so each element goes AGPR -> VGPR -> AGPR inside one asm block; this
+// keeps the accumulator's only uses AGPR-compatible, so the register allocator
+// never copies the whole accumulator to VGPRs around a loop.
+__device__ __forceinline__ void scale_acc_agpr(f32x16& a, float alpha) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float v = a[i];
+    float tmp;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "v_mul_f32 %1, %1, %2\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(v), "=&v"(tmp)
+        : "v"(alpha));
+    a[i] = v;
+  }
+}
+
+}  // namespace mla

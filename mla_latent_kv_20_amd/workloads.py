@@ -327,3 +327,42 @@ def make_config(name: str, seed: int = 0, **overrides) -> Workload:
     kw = dict(kw)
     kw.update(overrides)
     return make_workload(name, seed=seed, **kw)
+
+
+# ----------------------------------------------------------------------------
+# Inputs for testing one call on its own (drawn, never computed from another call)
+# ----------------------------------------------------------------------------
+
+def draw_q_abs(w: Workload, seed: int = 1, q_mult: float = 1.0) -> np.ndarray:
+    """Absorbed queries [n_q, n_h, d_c + d_r] in storage type, drawn directly.
+
+    The latent part has the variance of W^UK^T q^C for unit queries and weights of
+    variance 1/d_c (that is d_h/d_c); the RoPE part is unit variance.
+    """
+    rng = np.random.default_rng(seed)
+    lat = rng.standard_normal((w.n_q, w.n_h, w.d_c)) * math.sqrt(w.d_h / w.d_c) * q_mult
+    rope = rng.standard_normal((w.n_q, w.n_h, w.d_r)) * q_mult
+    return round_to_storage(np.concatenate([lat, rope], axis=2), w.dtype)
+
+
+def draw_partials(num_splits: int, n_q: int, n_h: int, d_c: int, seed: int = 2,
+                  empty_frac: float = 0.2):
+    """Split results (o_part fp32 [S, n_q, n_h, d_c], lse_part fp32 [S, n_q, n_h]).
+
+    A fraction of the (split, query, head) entries are empty splits (lse = -inf, o = 0);
+    the first split of every query head is never empty.
+    """
+    rng = np.random.default_rng(seed)
+    o = rng.standard_normal((num_splits, n_q, n_h, d_c)).astype(np.float32)
+    lse = (rng.standard_normal((num_splits, n_q, n_h)) * 3.0 + 5.0).astype(np.float32)
+    empty = rng.random((num_splits, n_q, n_h)) < empty_frac
+    empty[0] = False
+    lse[empty] = -np.inf
+    o[empty] = 0.0
+    return o, lse
+
+
+def draw_o_lat(n_q: int, n_h: int, d_c: int, seed: int = 3) -> np.ndarray:
+    """Latent attention outputs [n_q, n_h, d_c] fp32 (scale of a softmax-weighted mean)."""
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((n_q, n_h, d_c)) * 0.05).astype(np.float32)

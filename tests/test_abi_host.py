@@ -1,0 +1,122 @@
+"""The C-ABI library on the host: it loads without a GPU, exports every declared
+entry point, and rejects bad arguments with the documented status before launching.
+
+No call here passes arguments that would reach a kernel launch.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from mla_latent_kv_20_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_kv.h")
+
+FAKE = 0x100000          # 1 MiB-aligned fake device address: never dereferenced in these tests
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from mla_latent_kv_20_amd import build
+        build.build()
+    return B.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(mla_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_every_declared_entry_point_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(B.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n)
+    assert lib.mla_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.mla_status_string(code)
+    assert lib.mla_status_string(99) == b"unknown status"
+
+
+DSV2_BF16 = dict(n_h=128, d_h=128, d_c=512, d_r=64, dtype=B.MLA_BF16)
+
+
+def dims(**kw):
+    a = dict(DSV2_BF16)
+    a.update(kw)
+    return B.dims(**a)
+
+
+def decode(lib, d, batch=2, q_per_seq=1, q_abs=FAKE, c_kv=FAKE, c_stride=576, k_r=FAKE + 1024,
+           r_stride=576, offsets=FAKE, num_splits=1, split_rows=0, o_part=FAKE, lse_part=FAKE):
+    return lib.mla_decode(ctypes.byref(d), batch, q_per_seq, q_abs, c_kv, c_stride, k_r, r_stride,
+                          offsets, num_splits, split_rows, o_part, lse_part, None)
+
+
+def test_decode_argument_checks(lib):
+    d = dims()
+    assert lib.mla_decode(None, 2, 1, FAKE, FAKE, 576, FAKE, 576, FAKE, 1, 0, FAKE, FAKE, None) == B.MLA_ERR_NULL
+    assert decode(lib, d, batch=0) == B.MLA_OK                      # empty batch: no-op
+    assert decode(lib, d, batch=-1) == B.MLA_ERR_SHAPE
+    assert decode(lib, d, q_per_seq=0) == B.MLA_ERR_SHAPE
+    assert decode(lib, d, num_splits=0) == B.MLA_ERR_SHAPE
+    assert decode(lib, d, num_splits=4, split_rows=0) == B.MLA_ERR_SHAPE
+    assert decode(lib, d, q_abs=None) == B.MLA_ERR_NULL
+    assert decode(lib, d, offsets=None) == B.MLA_ERR_NULL
+    assert decode(lib, d, o_part=None) == B.MLA_ERR_NULL
+    assert decode(lib, d, c_stride=100) == B.MLA_ERR_SHAPE          # stride shorter than a latent
+    assert decode(lib, dims(dtype=7)) == B.MLA_ERR_DTYPE
+    assert decode(lib, dims(n_h=0)) == B.MLA_ERR_SHAPE
+    assert decode(lib, dims(d_r=63)) == B.MLA_ERR_SHAPE             # RoPE works on pairs
+    assert decode(lib, dims(softmax_scale=float("nan"))) == B.MLA_ERR_SHAPE
+    assert decode(lib, dims(d_c=256)) == B.MLA_ERR_UNSUPPORTED      # bf16 kernel is 512 + 64
+    assert decode(lib, dims(n_h=48)) == B.MLA_ERR_UNSUPPORTED       # heads go 32 per wave
+    assert decode(lib, d, k_r=FAKE + 4096) == B.MLA_ERR_UNSUPPORTED  # bf16 needs packed rows
+    assert decode(lib, d, c_kv=FAKE + 2, k_r=FAKE + 2 + 1024) == B.MLA_ERR_ALIGN
+    assert decode(lib, d, c_stride=580, r_stride=580) == B.MLA_ERR_ALIGN
+    assert decode(lib, d, offsets=FAKE + 4) == B.MLA_ERR_ALIGN
+    assert decode(lib, d, q_abs=FAKE + 8) == B.MLA_ERR_ALIGN
+
+
+def test_absorb_merge_out_proj_argument_checks(lib):
+    d = dims()
+    byref = ctypes.byref
+    assert lib.mla_absorb_q(byref(d), 0, None, None, None, None, None) == B.MLA_OK
+    assert lib.mla_absorb_q(byref(d), -3, FAKE, FAKE, FAKE, FAKE, None) == B.MLA_ERR_SHAPE
+    assert lib.mla_absorb_q(byref(d), 4, FAKE, None, FAKE, FAKE, None) == B.MLA_ERR_NULL
+    assert lib.mla_absorb_q(byref(d), 4, FAKE + 1, FAKE, FAKE, FAKE, None) == B.MLA_ERR_ALIGN
+    assert lib.mla_absorb_q(byref(dims(d_c=200)), 4, FAKE, FAKE, FAKE, FAKE, None) == B.MLA_ERR_UNSUPPORTED
+    assert lib.mla_merge_splits(byref(d), 4, 0, FAKE, FAKE, FAKE, FAKE, None) == B.MLA_ERR_SHAPE
+    assert lib.mla_merge_splits(byref(d), 4, 2, FAKE, FAKE, None, FAKE, None) == B.MLA_ERR_NULL
+    assert lib.mla_merge_splits(byref(d), 4, 2, FAKE + 4, FAKE, FAKE, FAKE, None) == B.MLA_ERR_ALIGN
+    assert lib.mla_merge_splits(byref(d), 0, 2, None, None, None, None, None) == B.MLA_OK
+    assert lib.mla_out_proj(byref(d), 4, FAKE, FAKE, None, None) == B.MLA_ERR_NULL
+    assert lib.mla_out_proj(byref(d), 4, FAKE + 2, FAKE, FAKE, None) == B.MLA_ERR_ALIGN
+    assert lib.mla_out_proj(byref(dims(d_h=100)), 4, FAKE, FAKE, FAKE, None) == B.MLA_ERR_UNSUPPORTED
+    assert lib.mla_out_proj(byref(dims(dtype=3)), 4, FAKE, FAKE, FAKE, None) == B.MLA_ERR_DTYPE
+
+
+def test_partial_bytes(lib):
+    d = dims()
+    assert lib.mla_partial_bytes(ctypes.byref(d), 32, 8) == 8 * 32 * 128 * 512 * 4
+    assert lib.mla_partial_bytes(ctypes.byref(d), 32, 0) == 0
+    assert lib.mla_partial_bytes(None, 32, 1) == 0
+
+
+def test_check_offsets(lib):
+    ok = np.array([0, 64, 101], np.int64)
+    assert B.check_offsets(ok, 2, 1, 101) == B.MLA_OK
+    assert B.check_offsets(ok, 2, 1, 100) == B.MLA_ERR_SHAPE          # beyond the cache
+    assert B.check_offsets(np.array([0, 64, 60], np.int64), 2, 1, 101) == B.MLA_ERR_SHAPE
+    assert B.check_offsets(np.array([0, 3, 9], np.int64), 2, 4, 9) == B.MLA_ERR_SHAPE   # len < q_per_seq
+    assert B.check_offsets(np.array([0, 4, 9], np.int64), 2, 4, 9) == B.MLA_OK
+    assert B.check_offsets(np.array([-1, 4], np.int64), 1, 1, 9) == B.MLA_ERR_SHAPE
+    assert B.check_offsets(np.zeros(1, np.int64), 0, 1, 0) == B.MLA_OK
