@@ -3,9 +3,12 @@
 Tolerances (on outputs o; m = max|o_ref|):
   fp32 workloads  max|o - o_ref| <= 1e-5 * m
   bf16 workloads  max|o - o_ref| <= 1e-2 * m + 1e-3
-log-sum-exp values are checked in absolute terms (|d lse| <= 1e-3 bf16, 1e-5 fp32): the
-scores are exact fp32 sums of exact bf16 products, so only summation order and exp2
-rounding separate them from the fp64 values.
+log-sum-exp values of mla_decode on a given q_abs are checked in absolute terms
+(|d lse| <= 1e-3 bf16, 1e-5 fp32): the scores are then exact fp32 sums of exact bf16
+products, so only summation order and exp2 rounding separate them from the fp64 values.
+End to end, q_abs itself is rounded to bf16 (2^-9 relative per element), which moves each
+logit by up to 2^-9 * scale * sum_c |q_c||row_c| (about 1e-2 here); there lse is checked
+with the same formula as the outputs.
 
 Every GPU step first prints the case it runs (test, workload, split plan).
 """
@@ -53,13 +56,17 @@ def bound(w, ref):
     return 1e-5 * m if w.dtype == W.F32 else 1e-2 * m + 1e-3
 
 
-def assert_close(what, got, ref, w, lse=False):
+def assert_close(what, got, ref, w, lse=False, lse_formula=False):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     fin = np.isfinite(ref)
     assert np.array_equal(np.isfinite(got), fin), f"{what}: non-finite pattern differs"
-    if lse:
+    if lse and lse_formula:
+        assert np.array_equal(got[~fin], ref[~fin]), what
+        tol = bound(w, ref[fin])
+        err = float(np.max(np.abs(got[fin] - ref[fin]))) if fin.any() else 0.0
+    elif lse:
         assert np.array_equal(got[~fin], ref[~fin]), what
         tol = 1e-5 if w.dtype == W.F32 else 1e-3
         err = float(np.max(np.abs(got[fin] - ref[fin]))) if fin.any() else 0.0
@@ -183,7 +190,7 @@ def test_end_to_end(torch, name):
         ref = O.absorbed_decode(**a, num_splits=S, split_rows=R)
         assert_close("o_c", got["o_c"], ref["o_c"], w)
         assert_close("o_lat", got["o_lat"], ref["o_lat"], w)
-        assert_close("lse", got["lse"], ref["lse"], w, lse=True)
+        assert_close("lse", got["lse"], ref["lse"], w, lse=True, lse_formula=True)
         sel = ~np.isnan(naive["o_c"][:, 0, 0])
         assert_close("o_c vs naive", got["o_c"][sel], naive["o_c"][sel], w)
 
@@ -229,7 +236,7 @@ def test_head_counts_off_the_group_size(torch, n_h):
     got = run_step(w, 2, 64)
     ref = O.absorbed_decode(**oracle_args(w), num_splits=2, split_rows=64)
     assert_close("o_c", got["o_c"], ref["o_c"], w)
-    assert_close("lse", got["lse"], ref["lse"], w, lse=True)
+    assert_close("lse", got["lse"], ref["lse"], w, lse=True, lse_formula=True)
 
 
 def test_split_plans_agree_and_runs_repeat_bitwise(torch):
@@ -307,7 +314,7 @@ def test_full_size(torch, name):
     ref = O.absorbed_decode(**a, num_splits=w.num_splits, split_rows=w.split_rows)
     assert_close("o_c", got["o_c"][qs], ref["o_c"], w)
     assert_close("o_lat", got["o_lat"][qs], ref["o_lat"], w)
-    assert_close("lse", got["lse"][qs], ref["lse"], w, lse=True)
+    assert_close("lse", got["lse"][qs], ref["lse"], w, lse=True, lse_formula=True)
     if name in ("dsv2_b32_t4096", "dsv2_mtp4_b64_t8192"):
         heads = [5, 100]
         b0 = seqs[0]
