@@ -104,6 +104,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="layer copies (0: enough to exceed 2x MALL)")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--split-rows", type=int, default=0)
+    ap.add_argument("--partials", choices=["auto", "f32", "f16"], default="auto",
+                    help="storage of split results (auto: fp16 when there is a merge)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -139,8 +141,10 @@ def main():
     layers = [base] + [dict(base, cache=base["cache"].clone(), w_uk=base["w_uk"].clone(),
                             w_uv=base["w_uv"].clone()) for _ in range(copies - 1)]
     n_q = w.n_q
+    part = B.default_partial_dtype(d, S) if args.partials == "auto" else \
+        {"f32": B.MLA_F32, "f16": B.MLA_F16}[args.partials]
     bufs = dict(q_abs=torch.empty((n_q, w.n_h, w.d_c + w.d_r), dtype=base["q_c"].dtype, device=dev),
-                o_part=torch.empty((S, n_q, w.n_h, w.d_c), dtype=torch.float32, device=dev),
+                o_part=torch.empty((S, n_q, w.n_h, w.d_c), dtype=B._torch_dtype(part), device=dev),
                 lse_part=torch.empty((S, n_q, w.n_h), dtype=torch.float32, device=dev),
                 o_lat=torch.empty((n_q, w.n_h, w.d_c), dtype=torch.float32, device=dev),
                 lse=torch.empty((n_q, w.n_h), dtype=torch.float32, device=dev),
@@ -157,7 +161,7 @@ def main():
                           w.q_per_seq, S, R, bufs["o_part"], bufs["lse_part"])
         if ev is not None:
             ev[2].record()
-        if S > 1:
+        if S > 1 or part != B.MLA_F32:
             o_lat, _ = B.merge_splits(d, op, lp, bufs["o_lat"], bufs["lse"])
         else:
             o_lat = op[0]
@@ -215,7 +219,8 @@ def main():
         "data": "synthetic (seeded Gaussian latent cache, DeepSeek-V2 attention dims, random weights)",
         "config": {"workload": args.config, "batch": w.batch, "seq_len": int(w.lengths.max()),
                    "cached_rows": cached, "q_per_seq": w.q_per_seq, "n_h": w.n_h, "d_h": w.d_h,
-                   "d_c": w.d_c, "d_r": w.d_r, "num_splits": S, "split_rows": R, "layer_copies": copies},
+                   "d_c": w.d_c, "d_r": w.d_r, "num_splits": S, "split_rows": R, "layer_copies": copies,
+                   "partials": {B.MLA_F32: "f32", B.MLA_F16: "f16"}[part]},
         "roofline": roof,
         "kernels_ms": {n: round(float(v.mean()), 5) for n, v in per.items()},
         "decode_merge_tokens_per_s": round(cached / ((per["decode"].mean() + per["merge"].mean()) * 1e-3), 1),

@@ -34,10 +34,12 @@
  *    check returns its MLA_ERR_* code and launches nothing.  MLA_ERR_LAUNCH
  *    reports a HIP launch error.  No call aborts or throws.
  *  - A size of zero (n_q == 0, batch == 0) is a valid no-op.
- *  - dtype MLA_BF16 runs the MFMA kernels (bf16 operands, fp32 accumulation);
- *    they need d_c == 512, d_r == 64, n_h % 32 == 0 and d_h % 32 == 0 (the
- *    DeepSeek-V2 attention shape) and 16-byte aligned rows, and return
- *    MLA_ERR_UNSUPPORTED for other shapes.  dtype MLA_F32 runs plain fp32
+ *  - dtype MLA_BF16 runs the MFMA kernels (bf16 operands, fp32 accumulation):
+ *    mla_decode needs d_c == 512, d_r == 64 and n_h % 32 == 0; mla_absorb_q
+ *    needs d_c % 128 == 0, d_h % 16 == 0, d_h <= 256, d_r % 8 == 0;
+ *    mla_out_proj needs d_h % 32 == 0, d_c % 16 == 0, d_c <= 512 (the
+ *    DeepSeek-V2 attention shape fits all) and 16-byte aligned rows; other
+ *    shapes return MLA_ERR_UNSUPPORTED.  dtype MLA_F32 runs plain fp32
  *    kernels for any shape (no bf16 rounding anywhere).
  */
 #ifndef MLA_KV_H_
@@ -52,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -66,7 +68,8 @@ typedef enum mla_status {
 
 typedef enum mla_dtype {
   MLA_F32 = 0,              /* float32 storage and arithmetic */
-  MLA_BF16 = 1              /* bfloat16 storage, fp32 accumulation */
+  MLA_BF16 = 1,             /* bfloat16 storage, fp32 accumulation */
+  MLA_F16 = 2               /* float16: storage of split partials only (see mla_decode) */
 } mla_dtype_t;
 
 /* Attention dimensions ([review] 4.1; [v3] MLA dimension list). */
@@ -102,9 +105,11 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t n_q,
                           const void* q_c, const void* q_r, const void* w_uk,
                           void* q_abs, hipStream_t stream);
 
-/* Bytes of o_part for (n_q, num_splits): num_splits * n_q * n_h * d_c * 4.
- * lse_part holds num_splits * n_q * n_h floats.  Returns 0 on bad arguments. */
-size_t mla_partial_bytes(const mla_dims_t* dims, int32_t n_q, int32_t num_splits);
+/* Bytes of o_part for (n_q, num_splits, partial_dtype):
+ * num_splits * n_q * n_h * d_c * (4 for MLA_F32, 2 for MLA_F16).  lse_part holds
+ * num_splits * n_q * n_h floats.  Returns 0 on bad arguments. */
+size_t mla_partial_bytes(const mla_dims_t* dims, int32_t n_q, int32_t num_splits,
+                         int32_t partial_dtype);
 
 /*
  * mla_decode - attention of every query head over the latent rows, one result
@@ -135,7 +140,11 @@ size_t mla_partial_bytes(const mla_dims_t* dims, int32_t n_q, int32_t num_splits
  *               >= q_per_seq.  Not read on the host, so not checked here: use
  *               mla_check_offsets on a host copy.
  *   num_splits  >= 1;  split_rows >= 1 when num_splits > 1 (ignored otherwise)
- *   o_part      [num_splits, batch*q_per_seq, n_h, d_c] fp32 out
+ *   partial_dtype  MLA_F32, or MLA_F16 (bf16 dtype only): storage of o_part.  fp16
+ *               halves the traffic of the split results (each split's o is a softmax-
+ *               weighted mean of latents, rounded once to 11 significant bits); it
+ *               needs |c_kv| < 65504.
+ *   o_part      [num_splits, batch*q_per_seq, n_h, d_c] out, in partial_dtype
  *   lse_part    [num_splits, batch*q_per_seq, n_h] fp32 out
  * bf16 streams whole 576-element rows, so it needs the packed row layout
  * [c^KV ; k^R]: k_r == c_kv + d_c and r_stride == c_stride (else
@@ -147,8 +156,8 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, int32_t q_per_seq
                         const void* c_kv, int64_t c_stride,
                         const void* k_r, int64_t r_stride,
                         const int64_t* seq_offsets,
-                        int32_t num_splits, int32_t split_rows,
-                        float* o_part, float* lse_part, hipStream_t stream);
+                        int32_t num_splits, int32_t split_rows, int32_t partial_dtype,
+                        void* o_part, float* lse_part, hipStream_t stream);
 
 /*
  * mla_check_offsets - host-side check of a host copy of seq_offsets against
@@ -166,12 +175,13 @@ mla_status_t mla_check_offsets(const int64_t* host_offsets, int32_t batch,
  * Splits with lse_s = -inf get weight 0; a query head whose every split is
  * empty gets o_lat = 0 and lse = -inf.
  *
- *   o_part   [num_splits, n_q, n_h, d_c] fp32,  lse_part [num_splits, n_q, n_h] fp32
+ *   o_part   [num_splits, n_q, n_h, d_c] in partial_dtype (MLA_F32 or MLA_F16)
+ *   lse_part [num_splits, n_q, n_h] fp32
  *   o_lat    [n_q, n_h, d_c] fp32 out,          lse      [n_q, n_h] fp32 out
- * All four must be 16-byte aligned when d_c % 4 == 0.
+ * o_part and o_lat must be 16-byte aligned when d_c % 8 == 0.
  */
 mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t n_q, int32_t num_splits,
-                              const float* o_part, const float* lse_part,
+                              int32_t partial_dtype, const void* o_part, const float* lse_part,
                               float* o_lat, float* lse, hipStream_t stream);
 
 /*

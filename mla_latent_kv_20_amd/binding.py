@@ -25,6 +25,7 @@ MLA_ERR_UNSUPPORTED = 5
 MLA_ERR_LAUNCH = 6
 MLA_F32 = 0
 MLA_BF16 = 1
+MLA_F16 = 2
 
 # Every entry point the header declares, with its ctypes signature.
 _I32, _I64, _F32, _P, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -39,11 +40,11 @@ _DIMS_P = ctypes.POINTER(MlaDims)
 SIGNATURES = {
     "mla_abi_version": (_I32, []),
     "mla_status_string": (ctypes.c_char_p, [_I32]),
-    "mla_partial_bytes": (_SZ, [_DIMS_P, _I32, _I32]),
+    "mla_partial_bytes": (_SZ, [_DIMS_P, _I32, _I32, _I32]),
     "mla_check_offsets": (_I32, [_P, _I32, _I32, _I64]),
     "mla_absorb_q": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P, _P]),
-    "mla_decode": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _I64, _P, _I64, _P, _I32, _I32, _P, _P, _P]),
-    "mla_merge_splits": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _P]),
+    "mla_decode": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _I64, _P, _I64, _P, _I32, _I32, _I32, _P, _P, _P]),
+    "mla_merge_splits": (_I32, [_DIMS_P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "mla_out_proj": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P]),
 }
 
@@ -103,7 +104,14 @@ def _dtype_code(t) -> int:
         return MLA_BF16
     if t.dtype == torch.float32:
         return MLA_F32
+    if t.dtype == torch.float16:
+        return MLA_F16
     raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _torch_dtype(code: int):
+    import torch
+    return {MLA_F32: torch.float32, MLA_BF16: torch.bfloat16, MLA_F16: torch.float16}[code]
 
 
 def dims_for(q_c, q_r, w_uk, softmax_scale: float = 0.0) -> MlaDims:
@@ -128,23 +136,27 @@ def absorb_q(d: MlaDims, q_c, q_r, w_uk, q_abs=None, stream=None):
 
 
 def decode(d: MlaDims, q_abs, c_kv, k_r, offsets, batch: int, q_per_seq: int = 1,
-           num_splits: int = 1, split_rows: int = 0, o_part=None, lse_part=None, stream=None):
+           num_splits: int = 1, split_rows: int = 0, o_part=None, lse_part=None, stream=None,
+           partial_dtype: int = MLA_F32):
     """Split-KV attention in latent space -> (o_part [S, n_q, n_h, d_c], lse_part [S, n_q, n_h]).
 
     ``c_kv`` and ``k_r`` are 2-D row views (their row strides are passed through); for the
     bf16 path they must be the two column ranges of one packed [rows, d_c + d_r] cache.
-    ``offsets`` is an int64 device tensor [batch + 1].
+    ``offsets`` is an int64 device tensor [batch + 1].  o_part is stored in ``partial_dtype``
+    (MLA_F32 or MLA_F16); a given ``o_part`` tensor decides it.
     """
     import torch
     n_q = batch * q_per_seq
     if o_part is None:
-        o_part = torch.empty((num_splits, n_q, d.n_h, d.d_c), dtype=torch.float32, device=q_abs.device)
+        o_part = torch.empty((num_splits, n_q, d.n_h, d.d_c), dtype=_torch_dtype(partial_dtype),
+                             device=q_abs.device)
+    partial_dtype = _dtype_code(o_part)
     if lse_part is None:
         lse_part = torch.empty((num_splits, n_q, d.n_h), dtype=torch.float32, device=q_abs.device)
     _check("mla_decode", load().mla_decode(
         ctypes.byref(d), batch, q_per_seq, _ptr(q_abs), _ptr(c_kv), int(c_kv.stride(0)), _ptr(k_r),
-        int(k_r.stride(0)), _ptr(offsets), num_splits, split_rows, _ptr(o_part), _ptr(lse_part),
-        _stream(stream)))
+        int(k_r.stride(0)), _ptr(offsets), num_splits, split_rows, partial_dtype, _ptr(o_part),
+        _ptr(lse_part), _stream(stream)))
     return o_part, lse_part
 
 
@@ -156,9 +168,9 @@ def merge_splits(d: MlaDims, o_part, lse_part, o_lat=None, lse=None, stream=None
         o_lat = torch.empty((n_q, d.n_h, d.d_c), dtype=torch.float32, device=o_part.device)
     if lse is None:
         lse = torch.empty((n_q, d.n_h), dtype=torch.float32, device=o_part.device)
-    _check("mla_merge_splits", load().mla_merge_splits(ctypes.byref(d), n_q, S, _ptr(o_part),
-                                                        _ptr(lse_part), _ptr(o_lat), _ptr(lse),
-                                                        _stream(stream)))
+    _check("mla_merge_splits", load().mla_merge_splits(ctypes.byref(d), n_q, S, _dtype_code(o_part),
+                                                        _ptr(o_part), _ptr(lse_part), _ptr(o_lat),
+                                                        _ptr(lse), _stream(stream)))
     return o_lat, lse
 
 
@@ -180,19 +192,28 @@ def check_offsets(host_offsets, batch: int, q_per_seq: int, total_rows: int) -> 
     return int(load().mla_check_offsets(a.ctypes.data if a.size else None, batch, q_per_seq, total_rows))
 
 
+def default_partial_dtype(d: MlaDims, num_splits: int) -> int:
+    """fp16 split results for the bf16 path when there is a merge to do, else fp32."""
+    return MLA_F16 if d.dtype == MLA_BF16 and num_splits > 1 else MLA_F32
+
+
 def decode_step(d: MlaDims, q_c, q_r, w_uk, w_uv, cache, offsets, batch: int, q_per_seq: int = 1,
-                num_splits: int = 1, split_rows: int = 0, bufs: Optional[dict] = None, stream=None):
+                num_splits: int = 1, split_rows: int = 0, bufs: Optional[dict] = None, stream=None,
+                partial_dtype: Optional[int] = None):
     """All four calls on one packed cache [rows, d_c + d_r]; returns the output buffers.
 
     ``bufs`` may hold preallocated q_abs / o_part / lse_part / o_lat / lse / o_c tensors.
+    With one split the decode writes fp32 results that are already o_lat and lse.
     """
+    if partial_dtype is None:
+        partial_dtype = default_partial_dtype(d, num_splits)
     b = {} if bufs is None else bufs
     q_abs = absorb_q(d, q_c, q_r, w_uk, b.get("q_abs"), stream)
     c_kv = cache[:, :d.d_c]
     k_r = cache[:, d.d_c:d.d_c + d.d_r]
     o_part, lse_part = decode(d, q_abs, c_kv, k_r, offsets, batch, q_per_seq, num_splits, split_rows,
-                              b.get("o_part"), b.get("lse_part"), stream)
-    if num_splits == 1:
+                              b.get("o_part"), b.get("lse_part"), stream, partial_dtype)
+    if num_splits == 1 and _dtype_code(o_part) == MLA_F32:
         o_lat, lse = o_part[0], lse_part[0]
     else:
         o_lat, lse = merge_splits(d, o_part, lse_part, b.get("o_lat"), b.get("lse"), stream)

@@ -47,19 +47,44 @@ absorb_q_bf16_kernel(AbsorbParams P) {
   const int lane = tid & 63;
   const int d_qk = P.d_c + P.d_r;
 
-  // RoPE part: copied once per head, by the first column block.
+  // RoPE part: copied once per head, by the first column block, 16 bytes per thread with
+  // every load of a thread in flight before its stores.
   if (blockIdx.x == 0) {
-    for (int e = tid; e < P.n_q * P.d_r; e += kThreads) {
-      const int n = e / P.d_r, c = e - n * P.d_r;
-      P.q_abs[((size_t)n * P.n_h + i) * d_qk + P.d_c + c] = P.q_r[((size_t)n * P.n_h + i) * P.d_r + c];
+    const int cpr = P.d_r / 8;                    // 16-byte chunks per query row (d_r % 8 == 0)
+    const int total = P.n_q * cpr;
+    for (int e0 = 0; e0 < total; e0 += 4 * kThreads) {
+      bf16x8 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kThreads + tid;
+        if (e < total)
+          v[u] = *(const bf16x8*)(P.q_r + ((size_t)(e / cpr) * P.n_h + i) * P.d_r + (e % cpr) * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kThreads + tid;
+        if (e < total)
+          *(bf16x8*)(P.q_abs + ((size_t)(e / cpr) * P.n_h + i) * d_qk + P.d_c + (e % cpr) * 8) = v[u];
+      }
     }
   }
 
-  // Stage W^UK_i[:, cb:cb+128] in LDS (16-byte chunks, 16 per row).
+  // Stage W^UK_i[:, cb:cb+128] in LDS (16-byte chunks, 16 per row): all loads of a
+  // thread are issued before its LDS writes, so their latencies overlap.
   const bf16_bits* w = P.w_uk + (size_t)i * P.d_h * P.d_c + cb;
-  for (int e = tid; e < P.d_h * (kAbsCols / 8); e += kThreads) {
-    const int r = e >> 4, c = e & 15;
-    *(bf16x8*)(smem + r * kAbsPitch + c * 16) = *(const bf16x8*)(w + (size_t)r * P.d_c + c * 8);
+  const int chunks = P.d_h * (kAbsCols / 8);     // <= 4096 (d_h <= 256)
+  for (int e0 = 0; e0 < chunks; e0 += 8 * kThreads) {
+    bf16x8 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * kThreads + tid;
+      if (e < chunks) v[u] = *(const bf16x8*)(w + (size_t)(e >> 4) * P.d_c + (e & 15) * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * kThreads + tid;
+      if (e < chunks) *(bf16x8*)(smem + (e >> 4) * kAbsPitch + (e & 15) * 16) = v[u];
+    }
   }
   __syncthreads();
 
@@ -109,9 +134,11 @@ absorb_q_bf16_kernel(AbsorbParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// out_proj: workgroup = (head i, 32 output columns of d_h); the 4 waves split the d_c
-// reduction and add their partial tiles through LDS.  W^UV_i rows are [d_h][d_c] with
-// d_c (the reduction index) contiguous: B operands load straight from global memory.
+// out_proj: workgroup = head i; wave w owns output columns [32w, 32w+32) of d_h (waves
+// loop when d_h > 128) and runs the whole d_c reduction.  W^UV_i rows are [d_h][d_c] with
+// d_c (the reduction index) contiguous, so B operands load straight from global memory
+// and stay in VGPRs; the o_lat rows (fp32, rounded to bf16 as A operands) are read once
+// per wave and shared by the waves through L1.
 // ---------------------------------------------------------------------------
 struct OutProjParams {
   const float* o_lat;     // [n_q, n_h, d_c]
@@ -120,58 +147,78 @@ struct OutProjParams {
   int n_q, n_h, d_h, d_c;
 };
 
-constexpr int kOutMaxSteps = 8;   // k-steps per wave: d_c <= 4 * 8 * 16 = 512
+constexpr int kOutMaxSteps = 32;   // k-steps of 16: d_c <= 512
+constexpr int kOutRows = 64;       // query rows staged in LDS per round
+constexpr int kOutPitch = 512 * 2 + 16;   // bf16 row of d_c <= 512, plus padding against bank conflicts
 
 __global__ void __launch_bounds__(kThreads)
 out_proj_bf16_kernel(OutProjParams P) {
-  __shared__ float red[kWaves][32][33];
-  const int i = blockIdx.y;
-  const int nb = blockIdx.x * 32;
+  __shared__ __attribute__((aligned(16))) char a_lds[kOutRows * kOutPitch];
+  const int i = blockIdx.x;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int steps = P.d_c / 16 / kWaves;          // k-steps of this wave
-  const int k0 = wave * steps * 16;
+  const int steps = P.d_c / 16;
+  const int q4 = P.d_c / 4;                      // float4 chunks per o_lat row
 
-  bf16x8 wb[kOutMaxSteps];
-  {
-    const bf16_bits* w = P.w_uv + ((size_t)i * P.d_h + nb + (lane & 31)) * P.d_c + k0 + 8 * (lane >> 5);
+  for (int mb0 = 0; mb0 < P.n_q; mb0 += kOutRows) {
+    // stage rows mb0 .. mb0+63 of o_lat[:, i, :] as bf16: every load of a thread in flight first
+    const int rows = P.n_q - mb0 < kOutRows ? P.n_q - mb0 : kOutRows;
+    const int total = rows * q4;
+    __syncthreads();                               // the previous round's reads are done
+    for (int e0 = 0; e0 < total; e0 += 8 * kThreads) {
+      f32x4 v[8];
 #pragma unroll
-    for (int s = 0; s < kOutMaxSteps; ++s)
-      if (s < steps) wb[s] = *(const bf16x8*)(w + 16 * s);
-  }
-
-  for (int mb = 0; mb < P.n_q; mb += 32) {
-    const int m = mb + (lane & 31);
-    const bool mrow = m < P.n_q;
-    const float* a = P.o_lat + ((size_t)(mrow ? m : 0) * P.n_h + i) * P.d_c + k0 + 8 * (lane >> 5);
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < kOutMaxSteps; ++s) {
-      if (s < steps) {
-        const f32x4 x0 = *(const f32x4*)(a + 16 * s);
-        const f32x4 x1 = *(const f32x4*)(a + 16 * s + 4);
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        u32x4 pk = {pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
-                    pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
-        if (!mrow) pk = u32x4{0u, 0u, 0u, 0u};
-        acc = mfma32x32x16(__builtin_bit_cast(bf16x8, pk), wb[s], acc);
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kThreads + tid;
+        if (e < total)
+          v[u] = *(const f32x4*)(P.o_lat + ((size_t)(mb0 + e / q4) * P.n_h + i) * P.d_c + (e % q4) * 4);
       }
-    }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[wave][8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)][lane & 31] = acc[r];
-    __syncthreads();
-    for (int e = tid; e < 32 * 32; e += kThreads) {
-      const int row = e >> 5, col = e & 31;
-      const int mm = mb + row;
-      if (mm < P.n_q) {
-        const float v = red[0][row][col] + red[1][row][col] + red[2][row][col] + red[3][row][col];
-        P.o_c[((size_t)mm * P.n_h + i) * P.d_h + nb + col] = f32_to_bf16(v);
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kThreads + tid;
+        if (e < total) {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          *(u32x2*)(a_lds + (e / q4) * kOutPitch + (e % q4) * 8) =
+              u32x2{pack_bf16x2(v[u][0], v[u][1]), pack_bf16x2(v[u][2], v[u][3])};
+        }
       }
     }
     __syncthreads();
+
+    for (int nb = 32 * wave; nb < P.d_h; nb += 32 * kWaves) {
+      // B operands: lane l holds W^UV_i[nb + l%32][16s + 8(l/32) .. +7]
+      bf16x8 wb[kOutMaxSteps];
+      const bf16_bits* w = P.w_uv + ((size_t)i * P.d_h + nb + (lane & 31)) * P.d_c + 8 * (lane >> 5);
+#pragma unroll
+      for (int s = 0; s < kOutMaxSteps; ++s)
+        if (s < steps) wb[s] = *(const bf16x8*)(w + 16 * s);
+      for (int mb = 0; mb < rows; mb += 32) {
+        const int m = mb + (lane & 31);
+        const char* a = a_lds + (m < rows ? m : 0) * kOutPitch + 16 * (lane >> 5);
+        f32x16 acc, acc1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          acc[r] = 0.f;
+          acc1[r] = 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < kOutMaxSteps; ++s) {
+          if (s < steps) {
+            const bf16x8 av = *(const bf16x8*)(a + 32 * s);
+            if (s & 1) acc1 = mfma32x32x16(av, wb[s], acc1);
+            else acc = mfma32x32x16(av, wb[s], acc);
+          }
+        }
+        // D[m][n]: lane l, reg r -> query mb0 + mb + 8(r/4) + 4(l/32) + r%4, column nb + l%32
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int mm = mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (mm < rows)
+            P.o_c[((size_t)(mb0 + mm) * P.n_h + i) * P.d_h + nb + (lane & 31)] = f32_to_bf16(acc[r] + acc1[r]);
+        }
+      }
+    }
   }
 }
 
@@ -181,7 +228,7 @@ bool absorb_bf16_supported(int d_h, int d_c) {
   return d_h % 16 == 0 && d_h <= 256 && d_c % kAbsCols == 0;
 }
 bool out_proj_bf16_supported(int d_h, int d_c) {
-  return d_h % 32 == 0 && d_c % (16 * kWaves) == 0 && d_c <= 16 * kWaves * kOutMaxSteps;
+  return d_h % 32 == 0 && d_c % 16 == 0 && d_c <= 16 * kOutMaxSteps;   // rows staged as <= 512 bf16
 }
 
 hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, const bf16_bits* w_uk,
@@ -196,7 +243,7 @@ hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, cons
 hipError_t launch_out_proj_bf16(const float* o_lat, const bf16_bits* w_uv, bf16_bits* o_c, int n_q,
                                 int n_h, int d_h, int d_c, hipStream_t stream) {
   OutProjParams P{o_lat, w_uv, o_c, n_q, n_h, d_h, d_c};
-  hipLaunchKernelGGL(out_proj_bf16_kernel, dim3(d_h / 32, n_h), dim3(kThreads), 0, stream, P);
+  hipLaunchKernelGGL(out_proj_bf16_kernel, dim3(n_h), dim3(kThreads), 0, stream, P);
   return hipGetLastError();
 }
 

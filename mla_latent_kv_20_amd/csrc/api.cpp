@@ -10,10 +10,10 @@
 namespace mla {
 typedef uint16_t bf16_bits;
 // kernels (decode_bf16.hip, absorb_bf16.hip, merge_f32.hip)
-hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* c_kv, int64_t c_stride,
-                              const bf16_bits* k_r, int64_t r_stride, const int64_t* offsets,
-                              float* o_part, float* lse_part, int batch, int q_per_seq, int n_h,
-                              int num_splits, int split_rows, float scale, hipStream_t stream);
+hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* rows, int64_t stride,
+                              const int64_t* offsets, void* o_part, bool f16_partials,
+                              float* lse_part, int batch, int q_per_seq, int n_h, int num_splits,
+                              int split_rows, float scale, hipStream_t stream);
 hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, const bf16_bits* w_uk,
                                 bf16_bits* q_abs, int n_q, int n_h, int d_h, int d_c, int d_r,
                                 hipStream_t stream);
@@ -21,8 +21,8 @@ hipError_t launch_out_proj_bf16(const float* o_lat, const bf16_bits* w_uv, bf16_
                                 int n_h, int d_h, int d_c, hipStream_t stream);
 bool absorb_bf16_supported(int d_h, int d_c);
 bool out_proj_bf16_supported(int d_h, int d_c);
-hipError_t launch_merge(const float* o_part, const float* lse_part, float* o_lat, float* lse, int n_q,
-                        int n_h, int d_c, int num_splits, hipStream_t stream);
+hipError_t launch_merge(const void* o_part, bool f16_partials, const float* lse_part, float* o_lat,
+                        float* lse, int n_q, int n_h, int d_c, int num_splits, hipStream_t stream);
 hipError_t launch_absorb_q_f32(const float* q_c, const float* q_r, const float* w_uk, float* q_abs,
                                int n_q, int n_h, int d_h, int d_c, int d_r, hipStream_t stream);
 size_t decode_f32_smem_bytes(int d_c, int d_r);
@@ -81,9 +81,11 @@ const char* mla_status_string(mla_status_t s) {
   return "unknown status";
 }
 
-size_t mla_partial_bytes(const mla_dims_t* dims, int32_t n_q, int32_t num_splits) {
+size_t mla_partial_bytes(const mla_dims_t* dims, int32_t n_q, int32_t num_splits, int32_t partial_dtype) {
   if (check_dims(dims) != MLA_OK || n_q < 0 || num_splits < 1) return 0;
-  return (size_t)num_splits * (size_t)n_q * (size_t)dims->n_h * (size_t)dims->d_c * sizeof(float);
+  if (partial_dtype != MLA_F32 && partial_dtype != MLA_F16) return 0;
+  return (size_t)num_splits * (size_t)n_q * (size_t)dims->n_h * (size_t)dims->d_c *
+         (partial_dtype == MLA_F16 ? 2 : 4);
 }
 
 mla_status_t mla_check_offsets(const int64_t* host_offsets, int32_t batch, int32_t q_per_seq,
@@ -125,9 +127,10 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t n_q, const void* q_c, 
 mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, int32_t q_per_seq, const void* q_abs,
                         const void* c_kv, int64_t c_stride, const void* k_r, int64_t r_stride,
                         const int64_t* seq_offsets, int32_t num_splits, int32_t split_rows,
-                        float* o_part, float* lse_part, hipStream_t stream) {
+                        int32_t partial_dtype, void* o_part, float* lse_part, hipStream_t stream) {
   mla_status_t st = check_dims(dims);
   if (st != MLA_OK) return st;
+  if (partial_dtype != MLA_F32 && partial_dtype != MLA_F16) return MLA_ERR_DTYPE;
   if (batch < 0 || q_per_seq < 1 || num_splits < 1) return MLA_ERR_SHAPE;
   if (num_splits > 1 && split_rows < 1) return MLA_ERR_SHAPE;
   if (batch == 0) return MLA_OK;
@@ -143,8 +146,9 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, int32_t q_per_seq
     if (!aligned(q_abs, 4) || !aligned(c_kv, 4) || !aligned(k_r, 4)) return MLA_ERR_ALIGN;
     if (mla::decode_f32_smem_bytes(dims->d_c, dims->d_r) > 64 * 1024) return MLA_ERR_UNSUPPORTED;
     if (num_splits > 65535 || n_q > 65535) return MLA_ERR_UNSUPPORTED;
+    if (partial_dtype != MLA_F32) return MLA_ERR_UNSUPPORTED;
     return launched(mla::launch_decode_f32((const float*)q_abs, (const float*)c_kv, c_stride,
-                                           (const float*)k_r, r_stride, seq_offsets, o_part, lse_part,
+                                           (const float*)k_r, r_stride, seq_offsets, (float*)o_part, lse_part,
                                            batch, q_per_seq, dims->n_h, dims->d_c, dims->d_r,
                                            num_splits, split_rows, scale, stream));
   }
@@ -156,26 +160,28 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, int32_t q_per_seq
   if (!aligned(o_part, 16)) return MLA_ERR_ALIGN;
   if (c_stride * 2 * 32 >= ((int64_t)1 << 31)) return MLA_ERR_SHAPE;
   return launched(mla::launch_decode_bf16((const uint16_t*)q_abs, (const uint16_t*)c_kv, c_stride,
-                                          (const uint16_t*)k_r, r_stride, seq_offsets, o_part, lse_part,
+                                          seq_offsets, o_part, partial_dtype == MLA_F16, lse_part,
                                           batch, q_per_seq, dims->n_h, num_splits, split_rows, scale,
                                           stream));
 }
 
 mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t n_q, int32_t num_splits,
-                              const float* o_part, const float* lse_part, float* o_lat, float* lse,
-                              hipStream_t stream) {
+                              int32_t partial_dtype, const void* o_part, const float* lse_part,
+                              float* o_lat, float* lse, hipStream_t stream) {
   mla_status_t st = check_dims(dims);
   if (st != MLA_OK) return st;
+  if (partial_dtype != MLA_F32 && partial_dtype != MLA_F16) return MLA_ERR_DTYPE;
   if (n_q < 0 || num_splits < 1) return MLA_ERR_SHAPE;
   if (n_q == 0) return MLA_OK;
   if (!o_part || !lse_part || !o_lat || !lse) return MLA_ERR_NULL;
   if ((int64_t)n_q * dims->n_h >= kMaxElems || (int64_t)num_splits * n_q * dims->n_h >= kMaxElems)
     return MLA_ERR_SHAPE;
-  const uintptr_t a = dims->d_c % 4 == 0 ? 16 : 4;
-  if (!aligned(o_part, a) || !aligned(o_lat, a) || !aligned(lse_part, 4) || !aligned(lse, 4))
+  const uintptr_t a = dims->d_c % 8 == 0 ? 16 : (partial_dtype == MLA_F16 ? 2 : 4);
+  if (!aligned(o_part, a) || !aligned(o_lat, dims->d_c % 8 == 0 ? 16 : 4) || !aligned(lse_part, 4) ||
+      !aligned(lse, 4))
     return MLA_ERR_ALIGN;
-  return launched(mla::launch_merge(o_part, lse_part, o_lat, lse, n_q, dims->n_h, dims->d_c, num_splits,
-                                    stream));
+  return launched(mla::launch_merge(o_part, partial_dtype == MLA_F16, lse_part, o_lat, lse, n_q,
+                                    dims->n_h, dims->d_c, num_splits, stream));
 }
 
 mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t n_q, const float* o_lat, const void* w_uv,

@@ -10,16 +10,17 @@
 // for the scores and 128 x 512 for the weighted sum -- a dense contraction.
 //
 // One workgroup = one (query token, split of rows, group of 128 heads); 4 waves,
-// wave w owns heads [32w, 32w+32) of the group.  Per 32-row tile:
-//   * the tile streams HBM -> LDS with 16-byte direct-to-LDS loads, STAGES deep;
+// wave w owns heads [32w, 32w+32) of the group, one wave per SIMD.  Per 32-row tile:
+//   * the tile streams HBM -> LDS as 16-byte direct-to-LDS loads, kStages deep; the
+//     loads of tile t+kStages-1 are interleaved with the score MFMAs of tile t;
 //   * S^T[32 rows x 32 heads] = K_tile[32 x 576] . Q^T (36 MFMA 32x32x16), with the
 //     wave's queries resident in VGPRs as MFMA B operands;
-//   * online softmax in registers: lane l owns head l%32 (16 of the 32 rows; its
-//     partner lane l^32 owns the other 16), max/sum exchanged across the pair;
-//   * O^T[512 dv x 32 heads] += V_tile^T . P^T (32 MFMA), V^T operands read from
-//     the row-major tile with the LDS transpose read, accumulators in AGPRs.
-// The softmax works in the log2 domain (scale folded with log2 e) and rescales
-// the accumulators only when a head's running maximum grows by more than 8.
+//   * online softmax in registers: lane l owns head l%32 (16 of the 32 rows; lane
+//     l^32 owns the other 16), max exchanged across the pair;
+//   * O^T[512 dv x 32 heads] += V_tile^T . P^T (32 MFMA), V^T operands read from the
+//     row-major tile with the LDS transpose read, accumulators in AGPRs.
+// The softmax works in the log2 domain (scale folded with log2 e) and rescales the
+// accumulators only when a head's running maximum grows by more than 8.
 #include "mla_common.h"
 
 namespace mla {
@@ -30,70 +31,90 @@ constexpr int kDr = 64;                  // RoPE key width
 constexpr int kDqk = kDc + kDr;          // 576: key width
 constexpr int kTile = 32;                // rows per tile
 constexpr int kChunks = kDqk / 8;        // 16-byte chunks per row (72)
-constexpr int kRowChunks = kChunks + 1;  // LDS row pitch in chunks: one chunk of padding
-constexpr int kRowBytes = kRowChunks * 16;                    // 1168
-constexpr int kTileBytes = kTile * kRowBytes;                 // 37376
-constexpr int kTileBlocks = (kTile * kRowChunks + 63) / 64;   // 1 KiB direct-to-LDS blocks (37)
+constexpr int kRowBytes = kChunks * 16;  // 1152
+constexpr int kTileBytes = kTile * kRowBytes;                 // 36864
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kHeadsPerWg = kWaves * 32;
-constexpr int kLoadsPerThread = (kTileBlocks + kWaves - 1) / kWaves;   // 10 (wave 0), else 9
+constexpr int kLoads = kTile * kChunks / kThreads;            // 9 loads of 1 KiB per wave per tile
 constexpr int kStages = 3;
 constexpr int kKSteps = kDqk / 16;       // 36 MFMA k-steps for the scores
+constexpr int kKReg = kDc / 16;          // 32 k-steps with the query operand in VGPRs (latent part)
+constexpr int kQRopeBytes = kHeadsPerWg * kDr * 2;            // RoPE part of the queries, in LDS
 constexpr int kDvTiles = kDc / 32;       // 16 output tiles of 32 dv
 constexpr float kRescaleSlack = 8.0f;    // log2 units
-constexpr int kKAhead = 4;               // K operand reads in flight
-constexpr int kVAhead = 3;               // V^T operand reads in flight
+constexpr int kKAhead = 6;               // K operand reads in flight
+constexpr int kVAhead = 6;               // V^T operand reads in flight
+constexpr int kOutHalf = kDc / 2;         // dv per epilogue round (256)
 constexpr int kWaitVmcnt0 = 0x0F70;      // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15) (gfx9 encoding)
 
-static_assert(kStages >= 2 && kStages <= 4, "stage count");
+static_assert(kTile * kChunks == kLoads * kThreads, "tile must split evenly into 1 KiB loads");
+static_assert(kKSteps == 4 * kLoads, "one tile load per 4 score steps");
+static_assert(kKSteps - kKReg == 4, "RoPE part: 4 k-steps of 16");
 
 struct DecodeParams {
   const bf16_bits* q_abs;       // [n_q, n_h, 576]
-  const bf16_bits* c_kv;        // rows, stride c_stride
-  const bf16_bits* k_r;         // rows, stride r_stride
+  const bf16_bits* rows;        // packed rows [c_kv | k_r], stride `stride` elements
   const int64_t* offsets;       // [batch+1]
-  float* o_part;                // [S, n_q, n_h, 512]
+  void* o_part;                 // [S, n_q, n_h, 512] fp32 or fp16
   float* lse_part;              // [S, n_q, n_h]
-  int64_t c_stride, r_stride;
+  int64_t stride;
   int n_q, n_h, q_per_seq, num_splits, split_rows;
-  int head_groups, group_size, streams;
+  int head_groups, group_size, streams, streams_per_xcd;
   float scale_log2;             // softmax scale * log2(e)
 };
 
-// LDS layout of a tile: row r at r * 1168 bytes (73 chunks of 16 bytes, the last one
-// padding), chunk c of the row at +16c.  The pitch is 292 dwords = 36 banks mod 64,
-// so 16 rows read at one chunk column, and 4 rows x 32 bytes of a transpose read,
-// land on distinct banks.
-__device__ __forceinline__ int chunk_offset(int r, int c) { return r * kRowBytes + c * 16; }
+// LDS layout of a tile: row r at r * 1152 bytes; logical chunk c of the row (16 bytes)
+// stored at physical chunk c ^ (r & 7), a swap inside the row's aligned groups of 8.
+// The 32 rows read at one logical chunk, and the 4 rows x 32 bytes of a transpose
+// read, then fall on different banks.  Because LDS slot p of the tile holds a chunk of
+// row p / 72, loading the tile is a contiguous copy with a small per-lane swap.
 
-// Issue the direct-to-LDS loads of one tile (packed rows: k^R follows c^KV in a row).
-// Block blk covers LDS slots 64*blk .. 64*blk+63; slot p is row p/73, chunk p%73.  Padding
-// slots and slots past the tile are masked off.  Rows past `rmax` re-read row `rmax`
-// (their scores are masked).  `tile_row` points at the tile's first row.
-__device__ __forceinline__ void issue_tile(const char* tile_row, int64_t stride_bytes, int rmax,
-                                           char* stage, int wave, int lane) {
+// Per-lane chunk swaps of the 9 loads: load i of lane l fills LDS slot
+// p = 64 * (9w + i) + l with global chunk p + delta_i, delta_i in [-7, 7] (4-bit fields).
+__device__ __forceinline__ void make_deltas(int wave, int lane, uint32_t& d0, uint32_t& d1) {
+  d0 = 0;
+  d1 = 0;
 #pragma unroll
-  for (int i = 0; i < kLoadsPerThread; ++i) {
-    const int blk = wave + kWaves * i;
-    if (blk < kTileBlocks) {
-      const int p = blk * 64 + lane;
-      const int r = p / kRowChunks;
-      const int c = p - r * kRowChunks;
-      if (c < kChunks && r < kTile) {
-        const int rr = r < rmax ? r : rmax;
-        global_to_lds16(tile_row + rr * stride_bytes + c * 16,
-                        __builtin_amdgcn_readfirstlane(lds_addr(stage + blk * 1024)));
-      }
-    }
+  for (int i = 0; i < kLoads; ++i) {
+    const int p = 64 * (kLoads * wave + i) + lane;
+    const int r = p / kChunks;
+    const int pc = p - r * kChunks;
+    const int delta = (pc ^ (r & 7)) - pc;
+    if (i < 8) d0 |= (uint32_t)(delta & 15) << (4 * i);
+    else d1 |= (uint32_t)(delta & 15) << (4 * (i - 8));
   }
 }
 
-// V^T operand of O^T step u (u < 16: rows 0-15, else rows 16-31; dv tile u % 16):
-// lane l gets rows {0..3, 8..11} + 4(l/32) (+16) of dv column 32(u%16) + l%32.
-// `vbase` is the lane's address for u = 0 (row v_row, dv v_dv).
-__device__ __forceinline__ bf16x8 load_vt(const char* vbase, int u) {
-  const char* p = vbase + (16 * (u / kDvTiles)) * kRowBytes + 64 * (u % kDvTiles);
+// Load i of one tile: contiguous rows (stride 576), every row inside the cache.
+__device__ __forceinline__ void load_fast(const char* tile_src, char* stage, int wave, int i,
+                                          uint32_t d0, uint32_t d1, uint32_t lane16) {
+  const int blk = kLoads * wave + i;
+  const uint32_t bits = i < 8 ? d0 >> (4 * i) : d1 >> (4 * (i - 8));
+  const int delta = ((int)(bits << 28)) >> 28;           // sign-extend the 4-bit field
+  global_to_lds16_sv(tile_src + blk * 1024, lane16 + (uint32_t)(delta * 16),
+                     __builtin_amdgcn_readfirstlane(lds_addr(stage + blk * 1024)));
+}
+
+// Load i of one tile, general form: any row stride, rows past `rmax` re-read row `rmax`.
+__device__ __forceinline__ void load_clamped(const char* tile_src, int64_t stride_bytes, int rmax,
+                                             char* stage, int wave, int i, int lane) {
+  const int blk = kLoads * wave + i;
+  const int p = 64 * blk + lane;
+  const int r = p / kChunks;
+  const int pc = p - r * kChunks;
+  const int lc = pc ^ (r & 7);
+  const int rr = r < rmax ? r : rmax;
+  global_to_lds16_sv(tile_src, (uint32_t)(rr * stride_bytes + lc * 16),
+                     __builtin_amdgcn_readfirstlane(lds_addr(stage + blk * 1024)));
+}
+
+// V^T operand for O^T step u (u < 16: rows 0-15, else rows 16-31; dv tile m = u % 16):
+// lane l gets rows {0..3, 8..11} + 4(l/32) (+16) of dv column 32m + l%32.  `vb` holds the
+// lane's address (row v_row, dv tile pair parity) for even and odd m.
+__device__ __forceinline__ bf16x8 load_vt(const char* tile, const int* vb, int u) {
+  const int m = u % kDvTiles;
+  const char* p = tile + vb[m & 1] + (16 * (u / kDvTiles)) * kRowBytes + 128 * (m >> 1);
   const i16x4 lo4 = lds_read_tr16(p);
   const i16x4 hi4 = lds_read_tr16(p + 8 * kRowBytes);
   const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
@@ -102,23 +123,39 @@ __device__ __forceinline__ bf16x8 load_vt(const char* vbase, int u) {
 
 // Wait until this wave's loads of all but the newest `pending` tiles have landed.
 template <int kPending>
-__device__ __forceinline__ void wait_tile(int wave) {
-  if (wave < kTileBlocks - (kLoadsPerThread - 1) * kWaves) wait_vmcnt<kPending * kLoadsPerThread>();
-  else wait_vmcnt<kPending * (kLoadsPerThread - 1)>();
+__device__ __forceinline__ void wait_tile() {
+  wait_vmcnt<kPending * kLoads>();
 }
 
+// Epilogue staging: wave w's 32 heads x 256 dv of one round, in LDS at w * stage_bytes,
+// one row of 256 outputs (+16 bytes of padding) per head; rows are then stored whole.
+template <typename OutT>
+__host__ __device__ constexpr int out_row_bytes() { return kOutHalf * (int)sizeof(OutT) + 16; }
+
+__device__ __forceinline__ void put4(float* p, float a, float b, float c, float d) {
+  *(f32x4*)p = f32x4{a, b, c, d};
+}
+__device__ __forceinline__ void put4(_Float16* p, float a, float b, float c, float d) {
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  *(f16x4*)p = f16x4{(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+}
+
+template <typename OutT>
 __global__ void __launch_bounds__(kThreads, 1)
 mla_decode_bf16_kernel(DecodeParams P) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-  // ---- work item: (row stream, member); members of one stream share its rows
-  // and sit on one XCD (workgroups are dealt round-robin over the 8 XCDs).
+  // ---- work item.  Workgroups are dealt round-robin over the 8 XCDs; XCD x takes the
+  // contiguous stream range [x * streams_per_xcd, ...), so the splits of one sequence
+  // share an XCD's L2 (one fetch of the queries), and the members of a stream (query
+  // tokens, head groups: same rows) run side by side on it.
   const int L = blockIdx.x;
   const int xcd = L & 7;
   const int k = L >> 3;
   const int member = k % P.group_size;
-  const int stream = (k / P.group_size) * 8 + xcd;
-  if (stream >= P.streams) return;
+  const int j = k / P.group_size;
+  const int stream = xcd * P.streams_per_xcd + j;
+  if (j >= P.streams_per_xcd || stream >= P.streams) return;
   const int hg = member % P.head_groups;
   const int r = member / P.head_groups;
   const int b = stream / P.num_splits;
@@ -151,31 +188,59 @@ mla_decode_bf16_kernel(DecodeParams P) {
   const size_t out_row = ((size_t)s * P.n_q + n) * P.n_h;
   if (hi <= lo) {                      // empty split: zero output, lse = -inf
     if (!active) return;
-    float* o = P.o_part + (out_row + head) * kDc;
-    for (int c = (lane >> 5) * 4; c < kDc; c += 8) *(f32x4*)(o + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+    OutT* o = (OutT*)P.o_part + (out_row + head) * kDc;
+    for (int c = (lane >> 5) * 4; c < kDc; c += 8) put4(o + c, 0.f, 0.f, 0.f, 0.f);
     if (lane < 32) P.lse_part[out_row + head] = -INFINITY;
     return;
   }
 
   const int ntiles = (int)((hi - lo + kTile - 1) / kTile);
-  const int64_t stride_bytes = P.c_stride * 2;
-  const char* first_row = (const char*)(P.c_kv + (row0 + lo) * P.c_stride);
+  const int64_t stride_bytes = P.stride * 2;
+  const char* first_row = (const char*)(P.rows + (row0 + lo) * P.stride);
   const int last_rel = (int)(hi - 1 - lo);        // last valid row, relative to lo
+  const bool contiguous = P.stride == kDqk;
+  const bool last_full = ((hi - lo) % kTile) == 0;
+
+  uint32_t d0, d1;
+  make_deltas(wave, lane, d0, d1);
+  const uint32_t lane16 = (uint32_t)lane * 16;
 
   // ---- prologue: start the first tiles, then fetch this wave's queries
 #pragma unroll
-  for (int t = 0; t < kStages - 1; ++t)
+  for (int t = 0; t < kStages - 1; ++t) {
     if (t < ntiles) {
-      const int rmax = last_rel - t * kTile;
-      issue_tile(first_row + (int64_t)t * kTile * stride_bytes, stride_bytes,
-                 rmax < kTile - 1 ? rmax : kTile - 1, smem + t * kTileBytes, wave, lane);
+      const char* src = first_row + (int64_t)t * kTile * stride_bytes;
+      char* stage = smem + t * kTileBytes;
+      if (contiguous && (t < ntiles - 1 || last_full)) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) load_fast(src, stage, wave, i, d0, d1, lane16);
+      } else {
+        const int rmax = last_rel - t * kTile < kTile - 1 ? last_rel - t * kTile : kTile - 1;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) load_clamped(src, stride_bytes, rmax, stage, wave, i, lane);
+      }
     }
+  }
 
-  bf16x8 qb[kKSteps];
+  // Queries: the latent part (k-steps 0..31) lives in VGPRs as MFMA B operands; the RoPE
+  // part (k-steps 32..35) of all 128 heads sits in LDS after the tile stages, 128 bytes
+  // per head with its 16-byte chunks swapped by (head & 7), and is read per tile.
+  bf16x8 qb[kKReg];
+  char* qrope = smem + kStages * kTileBytes;
   {
     const bf16_bits* q = P.q_abs + ((size_t)n * P.n_h + head_ld) * kDqk + (lane >> 5) * 8;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) qb[ks] = *(const bf16x8*)(q + ks * 16);
+    for (int ks = 0; ks < kKReg; ++ks) qb[ks] = *(const bf16x8*)(q + ks * 16);
+    // RoPE part: thread t copies chunk t%8 of head t/8 and of head t/8 + 32, 64, 96.
+    const int hc = threadIdx.x & 7;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int h = (threadIdx.x >> 3) + 32 * g;                 // head within the group
+      int hq = hg * kHeadsPerWg + h;
+      hq = hq < P.n_h ? hq : P.n_h - 1;
+      const bf16x8 v = *(const bf16x8*)(P.q_abs + ((size_t)n * P.n_h + hq) * kDqk + kDc + hc * 8);
+      *(bf16x8*)(qrope + h * 128 + 16 * (hc ^ (h & 7))) = v;
+    }
   }
   // All queries (and the prologue tiles) resident.  A builtin wait, so the compiler knows
   // the queries have landed and places no vmcnt waits for them inside the tile loop,
@@ -191,53 +256,93 @@ mla_decode_bf16_kernel(DecodeParams P) {
   float l_run = 0.f;                 // this lane's share of the softmax denominator
 
   // lane constants of the operand layouts
-  const int k_off = chunk_offset(lane & 31, lane >> 5);        // K operand, k-step 0
-  const int v_off = chunk_offset(4 * (lane >> 5) + ((lane & 15) >> 2), 2 * ((lane >> 4) & 1)) +
-                    8 * (lane & 3);                              // V^T operand, step 0
+  const int a_row = lane & 31;                 // K operand: tile row of this lane
+  int kb[4];                                   // K operand address for k-steps 4q + j
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) kb[jj] = a_row * kRowBytes + 16 * ((2 * jj + (lane >> 5)) ^ (a_row & 7));
+  const int v_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int v_cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  int vb[2];
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp)
+    vb[pp] = v_row * kRowBytes + 16 * ((4 * pp + v_cl) ^ (v_row & 7)) + 8 * (lane & 1);
   const int row_base = 4 * (lane >> 5);        // S^T rows held: 8(i/4) + row_base + i%4
 
   for (int t = 0; t < ntiles; ++t) {
     // tile t resident in LDS for every wave; the stage of tile t-1 is free
-    if (t + 1 < ntiles && kStages > 2) wait_tile<kStages - 2>(wave);
-    else wait_tile<0>(wave);
+    if (t + 1 < ntiles) wait_tile<kStages - 2>();
+    else wait_tile<0>();
     lds_barrier();
-    {
-      const int tn = t + kStages - 1;
-      if (tn < ntiles) {
-        int lane_v = lane;
-        asm volatile("" : "+v"(lane_v));   // recompute load offsets per tile instead of holding them
-        const int rmax = last_rel - tn * kTile;
-        issue_tile(first_row + (int64_t)tn * kTile * stride_bytes, stride_bytes,
-                   rmax < kTile - 1 ? rmax : kTile - 1, smem + (tn % kStages) * kTileBytes, wave,
-                   lane_v);
-      }
-    }
+
+    // Hide the load-offset inputs from loop-invariant hoisting: recomputing an offset
+    // costs two VALU ops, keeping nine of them live would cost nine VGPRs we do not have.
+    uint32_t dd0 = d0, dd1 = d1, ln16 = lane16;
+    int lane_v = lane;
+    asm volatile("" : "+v"(dd0), "+v"(dd1), "+v"(ln16), "+v"(lane_v));
 
     const char* tile = smem + (t % kStages) * kTileBytes;
-
-    // ---- scores S^T = K . Q^T; K operands read kKAhead steps ahead of their MFMA
-    const char* kp = tile + k_off;
-    f32x16 st;
+    const int tn = t + kStages - 1;              // tile whose loads go out during this one
+    const bool next_fast = tn < ntiles && contiguous && (tn < ntiles - 1 || last_full);
+    const char* next_src = first_row + (int64_t)tn * kTile * stride_bytes;
+    char* next_stage = smem + (tn % kStages) * kTileBytes;
+    if (tn < ntiles && !next_fast) {             // general loads (odd stride, partial tile): up front
+      const int rmax = last_rel - tn * kTile < kTile - 1 ? last_rel - tn * kTile : kTile - 1;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) st[i] = 0.f;
+      for (int i = 0; i < kLoads; ++i) load_clamped(next_src, stride_bytes, rmax, next_stage, wave, i, lane_v);
+    }
+
+    // ---- scores S^T = K . Q^T; K operands kKAhead steps ahead; one next-tile load per
+    // 4 steps
+    // two accumulation chains (even / odd k-steps): a dependent MFMA chain issues at about
+    // 60 cycles per step, two interleaved chains at the MFMA rate (about 37)
+    f32x16 st, st1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      st[i] = 0.f;
+      st1[i] = 0.f;
+    }
     bf16x8 ka[kKSteps];
 #pragma unroll
-    for (int ks = 0; ks < kKAhead; ++ks) ka[ks] = *(const bf16x8*)(kp + 32 * ks);
+    for (int ks = 0; ks < kKAhead; ++ks)
+      ka[ks] = *(const bf16x8*)(tile + kb[ks & 3] + 128 * (ks >> 2));
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
-      if (ks + kKAhead < kKSteps) ka[ks + kKAhead] = *(const bf16x8*)(kp + 32 * (ks + kKAhead));
-      st = mfma32x32x16(ka[ks], qb[ks], st);
+      if (ks + kKAhead < kKSteps) {
+        const int kn = ks + kKAhead;
+        ka[kn] = *(const bf16x8*)(tile + kb[kn & 3] + 128 * (kn >> 2));
+      }
+      bf16x8 qop;
+      if (ks < kKReg) {
+        qop = qb[ks];
+      } else {                                   // RoPE k-step: chunk 2(ks-32) + l/32 of head l%32
+        const int hl = wave * 32 + (lane & 31);
+        const int c = 2 * (ks - kKReg) + (lane >> 5);
+        qop = *(const bf16x8*)(qrope + hl * 128 + 16 * (c ^ (hl & 7)));
+      }
+      if (ks & 1) st1 = mfma32x32x16(ka[ks], qop, st1);
+      else st = mfma32x32x16(ka[ks], qop, st);
+      if ((ks & 3) == 3 && next_fast) load_fast(next_src, next_stage, wave, ks >> 2, dd0, dd1, ln16);
       __builtin_amdgcn_sched_barrier(0);
     }
 
+    st += st1;
+
     // ---- online softmax (log2 domain)
-    const int rem = last_rel - t * kTile;        // rows of this tile with index <= rem count
     float mt = -INFINITY;
+    const int rem = last_rel - t * kTile;        // rows of this tile with index <= rem count
+    if (rem >= kTile - 1) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 8 * (i >> 2) + row_base + (i & 3);
-      st[i] = row <= rem ? st[i] * P.scale_log2 : -INFINITY;
-      mt = fmaxf(mt, st[i]);
+      for (int i = 0; i < 16; ++i) {
+        st[i] *= P.scale_log2;
+        mt = fmaxf(mt, st[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + row_base + (i & 3);
+        st[i] = row <= rem ? st[i] * P.scale_log2 : -INFINITY;
+        mt = fmaxf(mt, st[i]);
+      }
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const bool grow = mt > m_ref + kRescaleSlack;
@@ -262,51 +367,65 @@ mla_decode_bf16_kernel(DecodeParams P) {
     const bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
 
     // ---- O^T += V^T . P^T: 2 row k-steps x 16 dv tiles, V^T operands read kVAhead ahead
-    const char* vp = tile + v_off;
     bf16x8 va[2 * kDvTiles];
 #pragma unroll
-    for (int u = 0; u < kVAhead; ++u) va[u] = load_vt(vp, u);
+    for (int u = 0; u < kVAhead; ++u) va[u] = load_vt(tile, vb, u);
 #pragma unroll
     for (int u = 0; u < 2 * kDvTiles; ++u) {
-      if (u + kVAhead < 2 * kDvTiles) va[u + kVAhead] = load_vt(vp, u + kVAhead);
+      if (u + kVAhead < 2 * kDvTiles) va[u + kVAhead] = load_vt(tile, vb, u + kVAhead);
       acc[u % kDvTiles] = mfma32x32x16(va[u], u < kDvTiles ? pb0 : pb1, acc[u % kDvTiles]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // ---- finalize: o = acc / l, lse = ln(sum exp)
-  if (!active) return;
+  // ---- finalize: o = acc / l, lse = ln(sum exp).  The outputs go through LDS in two
+  // rounds of 256 dv so that every store writes whole rows (1 KiB per instruction).
+  lds_barrier();                                 // every wave is done with the tiles
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
-  float* o = P.o_part + (out_row + head) * kDc;
+  constexpr int kRowB = out_row_bytes<OutT>();
+  char* ost = smem + wave * 32 * kRowB;
+  OutT* o = (OutT*)P.o_part + (out_row + hg * kHeadsPerWg + wave * 32) * kDc;
 #pragma unroll
-  for (int mt2 = 0; mt2 < kDvTiles; ++mt2)
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int dv = 32 * mt2 + 8 * g + row_base;
-      *(f32x4*)(o + dv) = f32x4{acc[mt2][4 * g] * inv, acc[mt2][4 * g + 1] * inv,
-                                acc[mt2][4 * g + 2] * inv, acc[mt2][4 * g + 3] * inv};
+    for (int mt2 = 0; mt2 < kDvTiles / 2; ++mt2)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& a = acc[half * (kDvTiles / 2) + mt2];
+        const int dv = 32 * mt2 + 8 * g + row_base;          // within the round
+        put4((OutT*)(ost + (lane & 31) * kRowB) + dv, a[4 * g] * inv, a[4 * g + 1] * inv,
+             a[4 * g + 2] * inv, a[4 * g + 3] * inv);
+      }
+    // read back whole rows: a row is kOutHalf * sizeof(OutT) bytes = 64 or 32 lanes x 16 bytes
+    constexpr int kLanesPerRow = kOutHalf * (int)sizeof(OutT) / 16;
+    constexpr int kRowsPerStore = 64 / kLanesPerRow;
+    const int rr = lane / kLanesPerRow;
+    const int cc = lane % kLanesPerRow;
+#pragma unroll
+    for (int h0 = 0; h0 < 32; h0 += kRowsPerStore) {
+      const int h = h0 + rr;
+      const f32x4 v = *(const f32x4*)(ost + h * kRowB + cc * 16);
+      if (active) *(f32x4*)((char*)(o + (size_t)h * kDc + half * kOutHalf) + cc * 16) = v;
     }
-  if (lane < 32) P.lse_part[out_row + head] = (m_ref + __log2f(l_tot)) * kLn2;
+  }
+  if (active && lane < 32) P.lse_part[out_row + head] = (m_ref + __log2f(l_tot)) * kLn2;
 }
 
 }  // namespace
 
-// Host launcher (arguments already validated).
-hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* c_kv, int64_t c_stride,
-                              const bf16_bits* k_r, int64_t r_stride, const int64_t* offsets,
-                              float* o_part, float* lse_part, int batch, int q_per_seq,
-                              int n_h, int num_splits, int split_rows, float scale,
-                              hipStream_t stream) {
+// Host launcher (arguments already validated; rows are packed [c_kv | k_r]).
+hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* rows, int64_t stride,
+                              const int64_t* offsets, void* o_part, bool f16_partials,
+                              float* lse_part, int batch, int q_per_seq, int n_h, int num_splits,
+                              int split_rows, float scale, hipStream_t stream) {
   DecodeParams P;
   P.q_abs = q_abs;
-  P.c_kv = c_kv;
-  P.k_r = k_r;
+  P.rows = rows;
   P.offsets = offsets;
   P.o_part = o_part;
   P.lse_part = lse_part;
-  P.c_stride = c_stride;
-  P.r_stride = r_stride;
+  P.stride = stride;
   P.n_q = batch * q_per_seq;
   P.n_h = n_h;
   P.q_per_seq = q_per_seq;
@@ -315,16 +434,24 @@ hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* c_kv, int
   P.head_groups = (n_h + kHeadsPerWg - 1) / kHeadsPerWg;
   P.group_size = P.head_groups * q_per_seq;
   P.streams = batch * num_splits;
+  P.streams_per_xcd = (P.streams + 7) / 8;
   P.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  const int stream_slots = (P.streams + 7) / 8;
-  const long long grid = (long long)stream_slots * 8 * P.group_size;
+  const long long grid = (long long)P.streams_per_xcd * 8 * P.group_size;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const size_t smem = (size_t)kStages * kTileBytes;
-  // Dynamic LDS above 64 KiB must be allowed once per function (thread-safe static init).
-  static const hipError_t attr_err = hipFuncSetAttribute(
-      (const void*)mla_decode_bf16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (attr_err != hipSuccess) return attr_err;
-  hipLaunchKernelGGL(mla_decode_bf16_kernel, dim3((unsigned)grid), dim3(kThreads), smem, stream, P);
+  size_t smem = (size_t)kStages * kTileBytes + kQRopeBytes;
+  const size_t out_stage = (size_t)kWaves * 32 * (f16_partials ? out_row_bytes<_Float16>() : out_row_bytes<float>());
+  smem = smem > out_stage ? smem : out_stage;
+  // Dynamic LDS above 64 KiB must be allowed once per kernel (thread-safe static init).
+  static const hipError_t attr32 = hipFuncSetAttribute(
+      (const void*)mla_decode_bf16_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  static const hipError_t attr16 = hipFuncSetAttribute(
+      (const void*)mla_decode_bf16_kernel<_Float16>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr32 != hipSuccess) return attr32;
+  if (attr16 != hipSuccess) return attr16;
+  if (f16_partials)
+    hipLaunchKernelGGL(mla_decode_bf16_kernel<_Float16>, dim3((unsigned)grid), dim3(kThreads), smem, stream, P);
+  else
+    hipLaunchKernelGGL(mla_decode_bf16_kernel<float>, dim3((unsigned)grid), dim3(kThreads), smem, stream, P);
   return hipGetLastError();
 }
 

@@ -16,45 +16,110 @@ namespace mla {
 namespace {
 
 // ---------------------------------------------------------------------------
-// merge: one workgroup per (query, head); threads sweep d_c four floats at a time.
+// merge: one wave per (query, head); lane l owns 8 consecutive outputs of each 512-wide
+// stripe, read as 16 bytes (fp16 partials) or 2 x 16 bytes (fp32).  The split weights
+// depend only on the (query, head), so every lane computes them from the same lse values.
 // ---------------------------------------------------------------------------
-constexpr int kMergeThreads = 128;
+constexpr int kMergeThreads = 256;
+constexpr int kMergeWaves = kMergeThreads / 64;
 
+template <typename PartT>
+__device__ __forceinline__ void load8(const PartT* p, float* v);
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* v) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+}
+template <>
+__device__ __forceinline__ void load8<_Float16>(const _Float16* p, float* v) {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  const f16x8 a = *(const f16x8*)p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
+}
+template <typename PartT>
+__device__ __forceinline__ float load1(const PartT* p) { return (float)*p; }
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// The lse values of up to 64 splits are held one per lane; the weights w_s = exp(lse_s - M)
+// are broadcast from lane s.  More splits go in chunks of 64.
+template <typename PartT>
 __global__ void __launch_bounds__(kMergeThreads)
-merge_splits_kernel(const float* __restrict__ o_part, const float* __restrict__ lse_part,
+merge_splits_kernel(const PartT* __restrict__ o_part, const float* __restrict__ lse_part,
                     float* __restrict__ o_lat, float* __restrict__ lse, int qh_count, int d_c,
                     int num_splits) {
-  const int qh = blockIdx.x;                      // n * n_h + i
+  const int qh = __builtin_amdgcn_readfirstlane(blockIdx.x * kMergeWaves + (threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  if (qh >= qh_count) return;
   float M = -INFINITY;
-  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, lse_part[(size_t)s * qh_count + qh]);
+  for (int s0 = 0; s0 < num_splits; s0 += 64) {
+    const int s = s0 + lane;
+    M = fmaxf(M, s < num_splits ? lse_part[(size_t)s * qh_count + qh] : -INFINITY);
+  }
+  M = wave_max(M);
   float* out = o_lat + (size_t)qh * d_c;
   if (M == -INFINITY) {                           // no split saw a row
-    for (int c = threadIdx.x; c < d_c; c += kMergeThreads) out[c] = 0.f;
-    if (threadIdx.x == 0) lse[qh] = -INFINITY;
+    for (int c = lane; c < d_c; c += 64) out[c] = 0.f;
+    if (lane == 0) lse[qh] = -INFINITY;
     return;
   }
   float z = 0.f;
-  for (int s = 0; s < num_splits; ++s) z += expf(lse_part[(size_t)s * qh_count + qh] - M);
+  for (int s0 = 0; s0 < num_splits; s0 += 64) {
+    const int s = s0 + lane;
+    z += s < num_splits ? expf(lse_part[(size_t)s * qh_count + qh] - M) : 0.f;
+  }
+  z = wave_sum(z);
   const float inv_z = 1.0f / z;
-  if ((d_c & 3) == 0) {
-    for (int c = 4 * threadIdx.x; c < d_c; c += 4 * kMergeThreads) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int s = 0; s < num_splits; ++s) {
-        const float w = expf(lse_part[(size_t)s * qh_count + qh] - M);
-        const f32x4 v = *(const f32x4*)(o_part + ((size_t)s * qh_count + qh) * d_c + c);
-        acc += w * v;
+  const bool vec = (d_c & 7) == 0;
+  for (int c = vec ? 8 * lane : lane; c < d_c; c += vec ? 8 * 64 : 64) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < num_splits; s0 += 64) {
+      const int sl = s0 + lane;
+      const float wl = sl < num_splits ? expf(lse_part[(size_t)sl * qh_count + qh] - M) : 0.f;
+      const int cnt = num_splits - s0 < 64 ? num_splits - s0 : 64;
+      int u = 0;
+      for (; u + 8 <= cnt; u += 8) {               // eight splits' loads in flight
+        float v[8][8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const PartT* p = o_part + ((size_t)(s0 + u + k) * qh_count + qh) * d_c + c;
+          if (vec) load8(p, v[k]);
+          else v[k][0] = load1(p);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float ws = __shfl(wl, u + k);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, v[k][e], acc[e]);
+        }
       }
-      *(f32x4*)(out + c) = acc * inv_z;
+      for (; u < cnt; ++u) {
+        float v[8];
+        const PartT* p = o_part + ((size_t)(s0 + u) * qh_count + qh) * d_c + c;
+        if (vec) load8(p, v);
+        else v[0] = load1(p);
+        const float ws = __shfl(wl, u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, v[e], acc[e]);
+      }
     }
-  } else {
-    for (int c = threadIdx.x; c < d_c; c += kMergeThreads) {
-      float acc = 0.f;
-      for (int s = 0; s < num_splits; ++s)
-        acc += expf(lse_part[(size_t)s * qh_count + qh] - M) * o_part[((size_t)s * qh_count + qh) * d_c + c];
-      out[c] = acc * inv_z;
+    if (vec) {
+      *(f32x4*)(out + c) = f32x4{acc[0] * inv_z, acc[1] * inv_z, acc[2] * inv_z, acc[3] * inv_z};
+      *(f32x4*)(out + c + 4) = f32x4{acc[4] * inv_z, acc[5] * inv_z, acc[6] * inv_z, acc[7] * inv_z};
+    } else {
+      out[c] = acc[0] * inv_z;
     }
   }
-  if (threadIdx.x == 0) lse[qh] = M + logf(z);
+  if (lane == 0) lse[qh] = M + logf(z);
 }
 
 // ---------------------------------------------------------------------------
@@ -204,11 +269,16 @@ unsigned grid_for(size_t total, int threads) {
 
 }  // namespace
 
-hipError_t launch_merge(const float* o_part, const float* lse_part, float* o_lat, float* lse, int n_q,
-                        int n_h, int d_c, int num_splits, hipStream_t stream) {
+hipError_t launch_merge(const void* o_part, bool f16_partials, const float* lse_part, float* o_lat,
+                        float* lse, int n_q, int n_h, int d_c, int num_splits, hipStream_t stream) {
   const int qh = n_q * n_h;
-  hipLaunchKernelGGL(merge_splits_kernel, dim3(qh), dim3(kMergeThreads), 0, stream, o_part, lse_part,
-                     o_lat, lse, qh, d_c, num_splits);
+  const dim3 grid((qh + kMergeWaves - 1) / kMergeWaves);
+  if (f16_partials)
+    hipLaunchKernelGGL(merge_splits_kernel<_Float16>, grid, dim3(kMergeThreads), 0, stream,
+                       (const _Float16*)o_part, lse_part, o_lat, lse, qh, d_c, num_splits);
+  else
+    hipLaunchKernelGGL(merge_splits_kernel<float>, grid, dim3(kMergeThreads), 0, stream,
+                       (const float*)o_part, lse_part, o_lat, lse, qh, d_c, num_splits);
   return hipGetLastError();
 }
 

@@ -70,6 +70,21 @@ __device__ __forceinline__ void global_to_lds16(const void* gptr, uint32_t lds_b
       : "memory");
 }
 
+// As global_to_lds16, addressed as a wave-uniform 64-bit base plus a per-lane 32-bit
+// byte offset (the saddr form), so no per-lane 64-bit address arithmetic is needed.
+__device__ __forceinline__ void global_to_lds16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved_m0;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved_m0)
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory");
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

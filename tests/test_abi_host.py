@@ -37,7 +37,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert set(names) == set(B.SIGNATURES), names
     for n in names:
         assert hasattr(lib, n)
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -56,14 +56,17 @@ def dims(**kw):
 
 
 def decode(lib, d, batch=2, q_per_seq=1, q_abs=FAKE, c_kv=FAKE, c_stride=576, k_r=FAKE + 1024,
-           r_stride=576, offsets=FAKE, num_splits=1, split_rows=0, o_part=FAKE, lse_part=FAKE):
+           r_stride=576, offsets=FAKE, num_splits=1, split_rows=0, o_part=FAKE, lse_part=FAKE,
+           partial=B.MLA_F32):
     return lib.mla_decode(ctypes.byref(d), batch, q_per_seq, q_abs, c_kv, c_stride, k_r, r_stride,
-                          offsets, num_splits, split_rows, o_part, lse_part, None)
+                          offsets, num_splits, split_rows, partial, o_part, lse_part, None)
 
 
 def test_decode_argument_checks(lib):
     d = dims()
-    assert lib.mla_decode(None, 2, 1, FAKE, FAKE, 576, FAKE, 576, FAKE, 1, 0, FAKE, FAKE, None) == B.MLA_ERR_NULL
+    assert lib.mla_decode(None, 2, 1, FAKE, FAKE, 576, FAKE, 576, FAKE, 1, 0, 0, FAKE, FAKE, None) == B.MLA_ERR_NULL
+    assert decode(lib, d, partial=B.MLA_BF16) == B.MLA_ERR_DTYPE      # partials: fp32 or fp16
+    assert decode(lib, dims(dtype=B.MLA_F32), partial=B.MLA_F16) == B.MLA_ERR_UNSUPPORTED
     assert decode(lib, d, batch=0) == B.MLA_OK                      # empty batch: no-op
     assert decode(lib, d, batch=-1) == B.MLA_ERR_SHAPE
     assert decode(lib, d, q_per_seq=0) == B.MLA_ERR_SHAPE
@@ -94,10 +97,11 @@ def test_absorb_merge_out_proj_argument_checks(lib):
     assert lib.mla_absorb_q(byref(d), 4, FAKE, None, FAKE, FAKE, None) == B.MLA_ERR_NULL
     assert lib.mla_absorb_q(byref(d), 4, FAKE + 1, FAKE, FAKE, FAKE, None) == B.MLA_ERR_ALIGN
     assert lib.mla_absorb_q(byref(dims(d_c=200)), 4, FAKE, FAKE, FAKE, FAKE, None) == B.MLA_ERR_UNSUPPORTED
-    assert lib.mla_merge_splits(byref(d), 4, 0, FAKE, FAKE, FAKE, FAKE, None) == B.MLA_ERR_SHAPE
-    assert lib.mla_merge_splits(byref(d), 4, 2, FAKE, FAKE, None, FAKE, None) == B.MLA_ERR_NULL
-    assert lib.mla_merge_splits(byref(d), 4, 2, FAKE + 4, FAKE, FAKE, FAKE, None) == B.MLA_ERR_ALIGN
-    assert lib.mla_merge_splits(byref(d), 0, 2, None, None, None, None, None) == B.MLA_OK
+    assert lib.mla_merge_splits(byref(d), 4, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == B.MLA_ERR_SHAPE
+    assert lib.mla_merge_splits(byref(d), 4, 2, 0, FAKE, FAKE, None, FAKE, None) == B.MLA_ERR_NULL
+    assert lib.mla_merge_splits(byref(d), 4, 2, 0, FAKE + 4, FAKE, FAKE, FAKE, None) == B.MLA_ERR_ALIGN
+    assert lib.mla_merge_splits(byref(d), 4, 2, 5, FAKE, FAKE, FAKE, FAKE, None) == B.MLA_ERR_DTYPE
+    assert lib.mla_merge_splits(byref(d), 0, 2, 0, None, None, None, None, None) == B.MLA_OK
     assert lib.mla_out_proj(byref(d), 4, FAKE, FAKE, None, None) == B.MLA_ERR_NULL
     assert lib.mla_out_proj(byref(d), 4, FAKE + 2, FAKE, FAKE, None) == B.MLA_ERR_ALIGN
     assert lib.mla_out_proj(byref(dims(d_h=100)), 4, FAKE, FAKE, FAKE, None) == B.MLA_ERR_UNSUPPORTED
@@ -106,9 +110,11 @@ def test_absorb_merge_out_proj_argument_checks(lib):
 
 def test_partial_bytes(lib):
     d = dims()
-    assert lib.mla_partial_bytes(ctypes.byref(d), 32, 8) == 8 * 32 * 128 * 512 * 4
-    assert lib.mla_partial_bytes(ctypes.byref(d), 32, 0) == 0
-    assert lib.mla_partial_bytes(None, 32, 1) == 0
+    assert lib.mla_partial_bytes(ctypes.byref(d), 32, 8, B.MLA_F32) == 8 * 32 * 128 * 512 * 4
+    assert lib.mla_partial_bytes(ctypes.byref(d), 32, 8, B.MLA_F16) == 8 * 32 * 128 * 512 * 2
+    assert lib.mla_partial_bytes(ctypes.byref(d), 32, 8, B.MLA_BF16) == 0
+    assert lib.mla_partial_bytes(ctypes.byref(d), 32, 0, B.MLA_F32) == 0
+    assert lib.mla_partial_bytes(None, 32, 1, B.MLA_F32) == 0
 
 
 def test_check_offsets(lib):

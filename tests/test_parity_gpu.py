@@ -113,9 +113,11 @@ def test_decode(torch, name):
     qa = W.draw_q_abs(w)
     t = D.to_device(w)
     qa_t = D._tensor(qa, w.dtype, "cuda")
-    for S, R in PLANS[name]:
-        say(f"[decode] {name} splits={S} split_rows={R}")
-        op, lp = B.decode(d, qa_t, t["c_kv"], t["k_r"], t["offsets"], w.batch, w.q_per_seq, S, R)
+    partials = [B.MLA_F32, B.MLA_F16] if w.dtype == W.BF16 else [B.MLA_F32]
+    for (S, R), pd in [(plan, pd) for plan in PLANS[name] for pd in partials]:
+        say(f"[decode] {name} splits={S} split_rows={R} partials={'f16' if pd == B.MLA_F16 else 'f32'}")
+        op, lp = B.decode(d, qa_t, t["c_kv"], t["k_r"], t["offsets"], w.batch, w.q_per_seq, S, R,
+                          partial_dtype=pd)
         torch.cuda.synchronize()
         ro, rl = O.split_partials(W.to_f64(qa, w.dtype), w.f64("c_kv"), w.f64("k_r"), w.offsets,
                                   w.q_per_seq, S, R, O.default_scale(w.d_h, w.d_r))
@@ -123,11 +125,13 @@ def test_decode(torch, name):
         assert_close("lse_part", D.to_numpy_f64(lp), rl, w, lse=True)
 
 
-@pytest.mark.parametrize("S", [1, 2, 7, 64])
-def test_merge(torch, S):
+@pytest.mark.parametrize("S,f16", [(1, False), (2, False), (7, False), (64, False), (3, True), (64, True)])
+def test_merge(torch, S, f16):
     n_q, n_h, d_c = 5, 128, 512
-    say(f"[merge] splits={S}")
+    say(f"[merge] splits={S} partials={'f16' if f16 else 'f32'}")
     o, l = W.draw_partials(S, n_q, n_h, d_c, seed=S)
+    if f16:
+        o = o.astype(np.float16)       # the partials the GPU consumes; the oracle widens the same values
     d = B.dims(n_h, 128, d_c, 64, B.MLA_BF16)
     ol, ll = B.merge_splits(d, torch.from_numpy(o).cuda(), torch.from_numpy(l).cuda())
     torch.cuda.synchronize()
@@ -249,7 +253,8 @@ def test_split_plans_agree_and_runs_repeat_bitwise(torch):
     assert np.array_equal(again["o_c"], outs[1]["o_c"]) and np.array_equal(again["lse"], outs[1]["lse"])
 
 
-def test_outputs_stay_inside_their_buffers(torch):
+@pytest.mark.parametrize("f16", [False, True])
+def test_outputs_stay_inside_their_buffers(torch, f16):
     """Guard bands of NaN around every output are untouched after a step."""
     w = workload("dsv2_small_mtp")
     d = dims_of(w)
@@ -265,13 +270,13 @@ def test_outputs_stay_inside_their_buffers(torch):
     bufs = {}
     raw = {}
     for k, shape, dt in [("q_abs", (w.n_q, w.n_h, 576), torch.bfloat16),
-                         ("o_part", (S, w.n_q, w.n_h, 512), torch.float32),
+                         ("o_part", (S, w.n_q, w.n_h, 512), torch.float16 if f16 else torch.float32),
                          ("lse_part", (S, w.n_q, w.n_h), torch.float32),
                          ("o_lat", (w.n_q, w.n_h, 512), torch.float32),
                          ("lse", (w.n_q, w.n_h), torch.float32),
                          ("o_c", (w.n_q, w.n_h, 128), torch.bfloat16)]:
         raw[k], bufs[k] = guarded(shape, dt)
-    say("[edge] guard bands")
+    say(f"[edge] guard bands, partials={'f16' if f16 else 'f32'}")
     B.decode_step(d, t["q_c"], t["q_r"], t["w_uk"], t["w_uv"], t["cache"], t["offsets"], w.batch,
                   w.q_per_seq, S, R, bufs=bufs)
     torch.cuda.synchronize()
