@@ -63,7 +63,11 @@ def measured_traffic(workload: str):
 
 
 def cpu_baseline(w, budget_s: float):
-    """Time the oracle's defining (materialized K/V) form on a bounded sample of the workload."""
+    """Time the oracle's defining (materialized K/V) form on a bounded sample of the workload.
+
+    Sequences are taken in order, each head by head, until the time budget is spent; the
+    rate is cached rows covered (a partly done sequence counts by its head fraction) per second.
+    """
     import oracle as O
     from mla_latent_kv_20_amd import workloads as W
     try:
@@ -71,28 +75,43 @@ def cpu_baseline(w, budget_s: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl missing
         threads = os.cpu_count() or 1
-    b = 0
-    lo, hi = int(w.offsets[b]), int(w.offsets[b + 1])
-    rows = np.arange(lo, hi)
-    a = dict(c_kv=W.to_f64(w.c_kv[rows], w.dtype), k_r=W.to_f64(w.k_r[rows], w.dtype),
-             offsets=np.array([0, hi - lo], np.int64),
-             q_c=W.to_f64(w.q_c[:w.q_per_seq], w.dtype), q_r=W.to_f64(w.q_r[:w.q_per_seq], w.dtype),
-             w_uk=w.f64("w_uk"), w_uv=w.f64("w_uv"), q_per_seq=w.q_per_seq)
-    heads_done, t0 = 0, time.perf_counter()
-    # heads one at a time until the budget is spent (at least one head)
-    while heads_done < w.n_h:
-        sub = dict(a, q_c=a["q_c"][:, heads_done:heads_done + 1], q_r=a["q_r"][:, heads_done:heads_done + 1],
-                   w_uk=a["w_uk"][heads_done:heads_done + 1], w_uv=a["w_uv"][heads_done:heads_done + 1])
-        O.naive_decode(**sub)
-        heads_done += 1
+    w_uk, w_uv = w.f64("w_uk"), w.f64("w_uv")
+    appended = w.q_per_seq if w.note == "appended" else 0
+    covered, seqs, heads_last, t0 = 0.0, 0, 0, time.perf_counter()
+    for b in range(w.batch):
+        lo, hi = int(w.offsets[b]), int(w.offsets[b + 1])
+        qs = slice(b * w.q_per_seq, (b + 1) * w.q_per_seq)
+        c_kv, k_r = W.to_f64(w.c_kv[lo:hi], w.dtype), W.to_f64(w.k_r[lo:hi], w.dtype)
+        q_c, q_r = W.to_f64(w.q_c[qs], w.dtype), W.to_f64(w.q_r[qs], w.dtype)
+        heads = 0
+        while heads < w.n_h:
+            h = slice(heads, heads + 1)
+            O.naive_decode(c_kv=c_kv, k_r=k_r, offsets=np.array([0, hi - lo], np.int64), q_c=q_c[:, h],
+                           q_r=q_r[:, h], w_uk=w_uk[h], w_uv=w_uv[h], q_per_seq=w.q_per_seq)
+            heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        covered += (hi - lo - appended) * heads / w.n_h
+        seqs, heads_last = b + 1, heads
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    cached = (hi - lo) - (w.q_per_seq if w.note == "appended" else 0)
-    value = cached * (heads_done / w.n_h) / dt
-    return {"value": value, "unit": UNIT, "cores": int(threads), "kind": "oracle",
-            "sample": f"sequence 0 ({hi - lo} rows), {heads_done} of {w.n_h} heads, naive fp64 "
-                      f"form (materialized k^C, v^C); {dt:.1f} s; tokens/s scaled by the head fraction"}
+    return {"value": covered / dt, "unit": UNIT, "cores": int(threads), "kind": "oracle",
+            "sample": f"sequences 0..{seqs - 1} of {w.batch} in order ({heads_last} of {w.n_h} heads of "
+                      f"the last), naive fp64 form (materialized k^C, v^C), {covered:.0f} cached rows "
+                      f"in {dt:.1f} s; tokens/s over that sample"}
+
+
+def copy_calibration(mib: int, reps: int) -> None:
+    """A plain device copy of known size, to scale HBM byte counters read under a profiler."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "reps": reps}), flush=True)
 
 
 def main():
@@ -108,12 +127,19 @@ def main():
                     help="storage of split results (auto: fp16 when there is a merge)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replay")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the decode shards by sequence with no exchange; see the design notes).", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 5)
+        return
 
     import torch
     from mla_latent_kv_20_amd import binding as B
@@ -150,50 +176,85 @@ def main():
                 lse=torch.empty((n_q, w.n_h), dtype=torch.float32, device=dev),
                 o_c=torch.empty((n_q, w.n_h, w.d_h), dtype=base["q_c"].dtype, device=dev))
 
-    def step(i, ev=None):
+    def step(i):
         L = layers[i % copies]
-        if ev is not None:
-            ev[0].record()
         qa = B.absorb_q(d, L["q_c"], L["q_r"], L["w_uk"], bufs["q_abs"])
-        if ev is not None:
-            ev[1].record()
         op, lp = B.decode(d, qa, L["cache"][:, :w.d_c], L["cache"][:, w.d_c:], L["offsets"], w.batch,
                           w.q_per_seq, S, R, bufs["o_part"], bufs["lse_part"])
-        if ev is not None:
-            ev[2].record()
         if S > 1 or part != B.MLA_F32:
             o_lat, _ = B.merge_splits(d, op, lp, bufs["o_lat"], bufs["lse"])
         else:
             o_lat = op[0]
-        if ev is not None:
-            ev[3].record()
         B.out_proj(d, o_lat, L["w_uv"], bufs["o_c"])
-        if ev is not None:
-            ev[4].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-
     K = args.steps
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(i, events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
-    names = ["absorb_q", "decode", "merge", "out_proj"]
-    per = {n: np.array([events[i][j].elapsed_time(events[i][j + 1]) for i in range(K)])
-           for j, n in enumerate(names)}
-    step_ms = np.array([events[i][0].elapsed_time(events[i][4]) for i in range(K)])
-    span_ms = events[0][0].elapsed_time(events[K - 1][4])
-    ms_per_step = span_ms / K
+    # Whole-step throughput: each layer copy's step is captured once as a HIP graph and the
+    # graphs are replayed round-robin, as a serving loop does (no host launch gaps).
+    graphs = []
+    if not args.no_graph:
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        g0.record()
+        for i in range(K):
+            graphs[i % copies].replay()
+        g1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        graph_ms = g0.elapsed_time(g1) / K
+
+    if args.no_graph:
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        g0.record()
+        for i in range(K):
+            step(i)
+        g1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        graph_ms = g0.elapsed_time(g1) / K
+    ms_per_step = graph_ms
     cached = w.cached_rows()
     value = cached / (ms_per_step * 1e-3)
 
-    dec_ms = float(per["decode"].mean())
+    # Each kernel alone, launched K times back to back over the layer copies, between one
+    # pair of HIP events on its stream: the mean launch duration, dispatch gaps included.
+    # The decode's is the roofline's duration.
+    calls = {
+        "absorb_q": lambda L: B.absorb_q(d, L["q_c"], L["q_r"], L["w_uk"], bufs["q_abs"]),
+        "decode": lambda L: B.decode(d, bufs["q_abs"], L["cache"][:, :w.d_c], L["cache"][:, w.d_c:],
+                                     L["offsets"], w.batch, w.q_per_seq, S, R, bufs["o_part"],
+                                     bufs["lse_part"]),
+        "merge": (lambda L: B.merge_splits(d, bufs["o_part"], bufs["lse_part"], bufs["o_lat"], bufs["lse"]))
+        if (S > 1 or part != B.MLA_F32) else None,
+        "out_proj": lambda L: B.out_proj(d, bufs["o_lat"], L["w_uv"], bufs["o_c"]),
+    }
+    per = {}
+    for name, fn in calls.items():
+        if fn is None:
+            continue
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(K):
+            fn(layers[i % copies])
+        e1.record()
+        torch.cuda.synchronize()
+        per[name] = e0.elapsed_time(e1) / K
+
+    dec_ms = per["decode"]
     dec_bytes = cached * ROW_BYTES + (w.rows - cached) * ROW_BYTES
     flops = float(FLOP_PER_ROW_HEAD) * w.n_h * sum(
         (int(L) - w.q_per_seq + r + 1) for L in w.lengths for r in range(w.q_per_seq))
@@ -222,9 +283,9 @@ def main():
                    "d_c": w.d_c, "d_r": w.d_r, "num_splits": S, "split_rows": R, "layer_copies": copies,
                    "partials": {B.MLA_F32: "f32", B.MLA_F16: "f16"}[part]},
         "roofline": roof,
-        "kernels_ms": {n: round(float(v.mean()), 5) for n, v in per.items()},
-        "decode_merge_tokens_per_s": round(cached / ((per["decode"].mean() + per["merge"].mean()) * 1e-3), 1),
-        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
+        "kernels_ms_mean": {n: round(v, 5) for n, v in per.items()},
+        "decode_merge_tokens_per_s": round(cached / ((dec_ms + per.get("merge", 0.0)) * 1e-3), 1),
+        "timing": "hip graph replay of the step" if not args.no_graph else "eager launches",
         "mfma_frac_decode": round(flops / (dec_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
     }

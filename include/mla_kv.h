@@ -37,7 +37,7 @@
  *  - dtype MLA_BF16 runs the MFMA kernels (bf16 operands, fp32 accumulation):
  *    mla_decode needs d_c == 512, d_r == 64 and n_h % 32 == 0; mla_absorb_q
  *    needs d_c % 128 == 0, d_h % 16 == 0, d_h <= 256, d_r % 8 == 0;
- *    mla_out_proj needs d_h % 32 == 0, d_c % 16 == 0, d_c <= 512 (the
+ *    mla_out_proj needs d_h % 32 == 0, d_c % 64 == 0, d_c <= 512 (the
  *    DeepSeek-V2 attention shape fits all) and 16-byte aligned rows; other
  *    shapes return MLA_ERR_UNSUPPORTED.  dtype MLA_F32 runs plain fp32
  *    kernels for any shape (no bf16 rounding anywhere).

@@ -69,6 +69,18 @@ absorb_q_bf16_kernel(AbsorbParams P) {
     }
   }
 
+  // A operands of the first query block, loaded before the weight slice so that the two
+  // memory latencies overlap.
+  const int ksteps = P.d_h / 16;                  // <= 16 (d_h <= 256)
+  bf16x8 qa[16];
+  {
+    const int m = lane & 31;
+    const bf16_bits* q = P.q_c + ((size_t)(m < P.n_q ? m : 0) * P.n_h + i) * P.d_h + 8 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s < ksteps) qa[s] = *(const bf16x8*)(q + 16 * s);
+  }
+
   // Stage W^UK_i[:, cb:cb+128] in LDS (16-byte chunks, 16 per row): all loads of a
   // thread are issued before its LDS writes, so their latencies overlap.
   const bf16_bits* w = P.w_uk + (size_t)i * P.d_h * P.d_c + cb;
@@ -89,7 +101,6 @@ absorb_q_bf16_kernel(AbsorbParams P) {
   __syncthreads();
 
   // B operands for every k-step: lane l gets W[16s + 8(l/32) + j][32w + l%32], j = 0..7.
-  const int ksteps = P.d_h / 16;                  // <= 16 (d_h <= 256)
   bf16x8 wb[16];
   {
     const int g = lane >> 4;                      // 16-lane group
@@ -112,14 +123,18 @@ absorb_q_bf16_kernel(AbsorbParams P) {
     const int m = mb + (lane & 31);
     const bool mrow = m < P.n_q;
     const bf16_bits* q = P.q_c + ((size_t)(mrow ? m : 0) * P.n_h + i) * P.d_h + 8 * (lane >> 5);
+    if (mb > 0) {
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        if (s < ksteps) qa[s] = *(const bf16x8*)(q + 16 * s);
+    }
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       if (s < ksteps) {
-        bf16x8 a = *(const bf16x8*)(q + 16 * s);
-        if (!mrow) a = bf16x8{};
+        const bf16x8 a = mrow ? qa[s] : bf16x8{};
         acc = mfma32x32x16(a, wb[s], acc);
       }
     }
@@ -134,11 +149,11 @@ absorb_q_bf16_kernel(AbsorbParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// out_proj: workgroup = head i; wave w owns output columns [32w, 32w+32) of d_h (waves
-// loop when d_h > 128) and runs the whole d_c reduction.  W^UV_i rows are [d_h][d_c] with
-// d_c (the reduction index) contiguous, so B operands load straight from global memory
-// and stay in VGPRs; the o_lat rows (fp32, rounded to bf16 as A operands) are read once
-// per wave and shared by the waves through L1.
+// out_proj: workgroup = (head i, block of 32 output columns of d_h); wave w runs a quarter
+// of the d_c reduction and the four partial 32 x 32 products are summed through LDS.
+// W^UV_i rows are [d_h][d_c] with d_c (the reduction index) contiguous, so B operands load
+// straight from global memory into VGPRs; the o_lat rows (fp32) are rounded to bf16 as A
+// operands.  Every load of a query block is issued before its first MFMA.
 // ---------------------------------------------------------------------------
 struct OutProjParams {
   const float* o_lat;     // [n_q, n_h, d_c]
@@ -147,77 +162,67 @@ struct OutProjParams {
   int n_q, n_h, d_h, d_c;
 };
 
-constexpr int kOutMaxSteps = 32;   // k-steps of 16: d_c <= 512
-constexpr int kOutRows = 64;       // query rows staged in LDS per round
-constexpr int kOutPitch = 512 * 2 + 16;   // bf16 row of d_c <= 512, plus padding against bank conflicts
+constexpr int kOutMaxSteps = 8;    // k-steps of 16 per wave: d_c <= 4 * 8 * 16 = 512
 
 __global__ void __launch_bounds__(kThreads)
 out_proj_bf16_kernel(OutProjParams P) {
-  __shared__ __attribute__((aligned(16))) char a_lds[kOutRows * kOutPitch];
-  const int i = blockIdx.x;
+  __shared__ f32x16 red[kWaves][64];
+  // Workgroups are dealt round-robin over the 8 XCDs: workgroup L runs on XCD L % 8.  All
+  // column blocks of head i go to XCD i % 8, so the head's o_lat rows are fetched into one
+  // L2 once and shared by its blocks.
+  const int nblk = P.d_h / 32;
+  const int xcd = blockIdx.x & 7;
+  const int kq = blockIdx.x >> 3;
+  const int i = (kq / nblk) * 8 + xcd;
+  const int nb = (kq % nblk) * 32;
+  if (i >= P.n_h) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int steps = P.d_c / 16;
-  const int q4 = P.d_c / 4;                      // float4 chunks per o_lat row
+  const int steps = P.d_c / 64;                   // k-steps of this wave
+  const int k0 = wave * steps * 16 + 8 * (lane >> 5);
 
-  for (int mb0 = 0; mb0 < P.n_q; mb0 += kOutRows) {
-    // stage rows mb0 .. mb0+63 of o_lat[:, i, :] as bf16: every load of a thread in flight first
-    const int rows = P.n_q - mb0 < kOutRows ? P.n_q - mb0 : kOutRows;
-    const int total = rows * q4;
-    __syncthreads();                               // the previous round's reads are done
-    for (int e0 = 0; e0 < total; e0 += 8 * kThreads) {
-      f32x4 v[8];
+  // B operands: lane l holds W^UV_i[nb + l%32][k0 + 16s .. +7]
+  bf16x8 wb[kOutMaxSteps];
+  const bf16_bits* w = P.w_uv + ((size_t)i * P.d_h + nb + (lane & 31)) * P.d_c + k0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * kThreads + tid;
-        if (e < total)
-          v[u] = *(const f32x4*)(P.o_lat + ((size_t)(mb0 + e / q4) * P.n_h + i) * P.d_c + (e % q4) * 4);
-      }
+  for (int s = 0; s < kOutMaxSteps; ++s)
+    if (s < steps) wb[s] = *(const bf16x8*)(w + 16 * s);
+
+  for (int mb = 0; mb < P.n_q; mb += 32) {
+    const int m = mb + (lane & 31);
+    const float* a = P.o_lat + ((size_t)(m < P.n_q ? m : P.n_q - 1) * P.n_h + i) * P.d_c + k0;
+    f32x4 av[kOutMaxSteps][2];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * kThreads + tid;
-        if (e < total) {
-          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-          *(u32x2*)(a_lds + (e / q4) * kOutPitch + (e % q4) * 8) =
-              u32x2{pack_bf16x2(v[u][0], v[u][1]), pack_bf16x2(v[u][2], v[u][3])};
-        }
+    for (int s = 0; s < kOutMaxSteps; ++s) {
+      if (s < steps) {
+        av[s][0] = *(const f32x4*)(a + 16 * s);
+        av[s][1] = *(const f32x4*)(a + 16 * s + 4);
       }
     }
-    __syncthreads();
-
-    for (int nb = 32 * wave; nb < P.d_h; nb += 32 * kWaves) {
-      // B operands: lane l holds W^UV_i[nb + l%32][16s + 8(l/32) .. +7]
-      bf16x8 wb[kOutMaxSteps];
-      const bf16_bits* w = P.w_uv + ((size_t)i * P.d_h + nb + (lane & 31)) * P.d_c + 8 * (lane >> 5);
+    f32x16 acc;
 #pragma unroll
-      for (int s = 0; s < kOutMaxSteps; ++s)
-        if (s < steps) wb[s] = *(const bf16x8*)(w + 16 * s);
-      for (int mb = 0; mb < rows; mb += 32) {
-        const int m = mb + (lane & 31);
-        const char* a = a_lds + (m < rows ? m : 0) * kOutPitch + 16 * (lane >> 5);
-        f32x16 acc, acc1;
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          acc[r] = 0.f;
-          acc1[r] = 0.f;
-        }
-#pragma unroll
-        for (int s = 0; s < kOutMaxSteps; ++s) {
-          if (s < steps) {
-            const bf16x8 av = *(const bf16x8*)(a + 32 * s);
-            if (s & 1) acc1 = mfma32x32x16(av, wb[s], acc1);
-            else acc = mfma32x32x16(av, wb[s], acc);
-          }
-        }
-        // D[m][n]: lane l, reg r -> query mb0 + mb + 8(r/4) + 4(l/32) + r%4, column nb + l%32
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int mm = mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (mm < rows)
-            P.o_c[((size_t)(mb0 + mm) * P.n_h + i) * P.d_h + nb + (lane & 31)] = f32_to_bf16(acc[r] + acc1[r]);
-        }
+    for (int s = 0; s < kOutMaxSteps; ++s) {
+      if (s < steps) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 pk = {pack_bf16x2(av[s][0][0], av[s][0][1]), pack_bf16x2(av[s][0][2], av[s][0][3]),
+                          pack_bf16x2(av[s][1][0], av[s][1][1]), pack_bf16x2(av[s][1][2], av[s][1][3])};
+        acc = mfma32x32x16(__builtin_bit_cast(bf16x8, pk), wb[s], acc);
       }
+    }
+    if (mb > 0) __syncthreads();                  // the previous block's sums are read
+    red[wave][lane] = acc;
+    __syncthreads();
+    // wave w sums accumulator registers 4w .. 4w+3 of the four waves.
+    // D[m][n]: lane l, reg r -> query mb + 8(r/4) + 4(l/32) + r%4, column nb + l%32
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 4 * wave + q;
+      const float v = red[0][lane][r] + red[1][lane][r] + red[2][lane][r] + red[3][lane][r];
+      const int mm = mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (mm < P.n_q) P.o_c[((size_t)mm * P.n_h + i) * P.d_h + nb + (lane & 31)] = f32_to_bf16(v);
     }
   }
 }
@@ -228,7 +233,7 @@ bool absorb_bf16_supported(int d_h, int d_c) {
   return d_h % 16 == 0 && d_h <= 256 && d_c % kAbsCols == 0;
 }
 bool out_proj_bf16_supported(int d_h, int d_c) {
-  return d_h % 32 == 0 && d_c % 16 == 0 && d_c <= 16 * kOutMaxSteps;   // rows staged as <= 512 bf16
+  return d_h % 32 == 0 && d_c % 64 == 0 && d_c <= 4 * 16 * kOutMaxSteps;
 }
 
 hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, const bf16_bits* w_uk,
@@ -243,7 +248,8 @@ hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, cons
 hipError_t launch_out_proj_bf16(const float* o_lat, const bf16_bits* w_uv, bf16_bits* o_c, int n_q,
                                 int n_h, int d_h, int d_c, hipStream_t stream) {
   OutProjParams P{o_lat, w_uv, o_c, n_q, n_h, d_h, d_c};
-  hipLaunchKernelGGL(out_proj_bf16_kernel, dim3(n_h), dim3(kThreads), 0, stream, P);
+  const int grid = 8 * ((n_h + 7) / 8) * (d_h / 32);
+  hipLaunchKernelGGL(out_proj_bf16_kernel, dim3(grid), dim3(kThreads), 0, stream, P);
   return hipGetLastError();
 }
 

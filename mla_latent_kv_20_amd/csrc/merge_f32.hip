@@ -22,6 +22,7 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 256;
 constexpr int kMergeWaves = kMergeThreads / 64;
+constexpr int kFastSplits = 8;
 
 template <typename PartT>
 __device__ __forceinline__ void load8(const PartT* p, float* v);
@@ -60,6 +61,39 @@ merge_splits_kernel(const PartT* __restrict__ o_part, const float* __restrict__ 
   const int qh = __builtin_amdgcn_readfirstlane(blockIdx.x * kMergeWaves + (threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   if (qh >= qh_count) return;
+  if (num_splits <= kFastSplits && d_c == 8 * 64) {
+    // One 512-wide stripe and at most 8 splits: every load (the lse values and all partial
+    // rows) is issued before the first reduction, so the wave waits on one memory latency.
+    const float lse_l = lane < num_splits ? lse_part[(size_t)lane * qh_count + qh] : -INFINITY;
+    float v[kFastSplits][8];
+#pragma unroll
+    for (int k = 0; k < kFastSplits; ++k)
+      if (k < num_splits) load8(o_part + ((size_t)k * qh_count + qh) * d_c + 8 * lane, v[k]);
+    const float M = wave_max(lse_l);
+    float* out = o_lat + (size_t)qh * d_c + 8 * lane;
+    if (M == -INFINITY) {                         // no split saw a row
+      *(f32x4*)out = f32x4{0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)(out + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (lane == 0) lse[qh] = -INFINITY;
+      return;
+    }
+    const float w_l = expf(lse_l - M);            // 0 for lanes past the last split
+    const float z = wave_sum(w_l);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kFastSplits; ++k) {
+      if (k < num_splits) {
+        const float ws = __shfl(w_l, k);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, v[k][e], acc[e]);
+      }
+    }
+    const float inv_z = 1.0f / z;
+    *(f32x4*)out = f32x4{acc[0] * inv_z, acc[1] * inv_z, acc[2] * inv_z, acc[3] * inv_z};
+    *(f32x4*)(out + 4) = f32x4{acc[4] * inv_z, acc[5] * inv_z, acc[6] * inv_z, acc[7] * inv_z};
+    if (lane == 0) lse[qh] = M + logf(z);
+    return;
+  }
   float M = -INFINITY;
   for (int s0 = 0; s0 < num_splits; s0 += 64) {
     const int s = s0 + lane;
