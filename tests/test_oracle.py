@@ -335,6 +335,31 @@ def test_merge_of_any_partition_equals_the_unsplit_result(num_splits, split_rows
     assert np.all(op[empty] == 0)
 
 
+@pytest.mark.parametrize("mutant", ["uniform_weights", "lse_without_sum", "weights_not_normalised"])
+def test_planted_merge_mistakes_are_caught(mutant):
+    """Plausible mistakes in the split merge fail the unsplit-result pin."""
+    w = tiny_mtp()
+    a = args_of(w)
+    scale = O.default_scale(w.d_h, w.d_r)
+    qa = O.absorb_q(a["q_c"], a["q_r"], a["w_uk"])
+    o1, l1 = O.attend_latent(qa, a["c_kv"], a["k_r"], w.offsets, w.q_per_seq, scale)
+    op, lp = O.split_partials(qa, a["c_kv"], a["k_r"], w.offsets, w.q_per_seq, 3, 4, scale)
+    M = np.max(lp, axis=0)
+    wt = np.exp(lp - M)
+    z = np.sum(wt, axis=0)
+    if mutant == "uniform_weights":
+        live = np.isfinite(lp).astype(np.float64)
+        o2 = np.einsum("snh,snhc->nhc", live, op) / np.sum(live, axis=0)[..., None]
+        l2 = M + np.log(z)
+    elif mutant == "lse_without_sum":
+        o2 = np.einsum("snh,snhc->nhc", wt, op) / z[..., None]
+        l2 = M
+    else:
+        o2 = np.einsum("snh,snhc->nhc", wt, op)
+        l2 = M + np.log(z)
+    assert rel(o2, o1) > 1e-6 or np.max(np.abs(l2 - l1)) > 1e-6
+
+
 def test_split_bounds_cover_every_visible_row_once():
     for vis in [1, 5, 31, 32, 33, 200]:
         for S, R in [(1, 0), (2, 32), (3, 7), (10, 32), (4, 100)]:
