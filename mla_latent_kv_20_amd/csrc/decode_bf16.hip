@@ -11,8 +11,11 @@
 //
 // One workgroup = one (query token, split of rows, group of 128 heads); 4 waves,
 // wave w owns heads [32w, 32w+32) of the group, one wave per SIMD.  Per 32-row tile:
-//   * the tile streams HBM -> LDS as 16-byte direct-to-LDS loads, kStages deep; the
-//     loads of tile t+kStages-1 are interleaved with the score MFMAs of tile t;
+//   * the tile streams HBM -> LDS as 16-byte direct-to-LDS loads, double buffered: the
+//     nine loads of tile t+1 leave together right after the barrier that opens tile t.
+//     (A direct-to-LDS load stalls the issuing wave while the memory pipeline is backed
+//     up, so the loads go out in one burst with the previous tile's already landed, and
+//     only one tile is in flight.)
 //   * S^T[32 rows x 32 heads] = K_tile[32 x 576] . Q^T (36 MFMA 32x32x16), with the
 //     wave's queries resident in VGPRs as MFMA B operands;
 //   * online softmax in registers: lane l owns head l%32 (16 of the 32 rows; lane
@@ -37,7 +40,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kHeadsPerWg = kWaves * 32;
 constexpr int kLoads = kTile * kChunks / kThreads;            // 9 loads of 1 KiB per wave per tile
-constexpr int kStages = 3;
+constexpr int kStages = 2;
 constexpr int kKSteps = kDqk / 16;       // 36 MFMA k-steps for the scores
 constexpr int kKReg = kDc / 16;          // 32 k-steps with the query operand in VGPRs (latent part)
 constexpr int kQRopeBytes = kHeadsPerWg * kDr * 2;            // RoPE part of the queries, in LDS
@@ -281,18 +284,21 @@ mla_decode_bf16_kernel(DecodeParams P) {
     asm volatile("" : "+v"(dd0), "+v"(dd1), "+v"(ln16), "+v"(lane_v));
 
     const char* tile = smem + (t % kStages) * kTileBytes;
-    const int tn = t + kStages - 1;              // tile whose loads go out during this one
-    const bool next_fast = tn < ntiles && contiguous && (tn < ntiles - 1 || last_full);
-    const char* next_src = first_row + (int64_t)tn * kTile * stride_bytes;
-    char* next_stage = smem + (tn % kStages) * kTileBytes;
-    if (tn < ntiles && !next_fast) {             // general loads (odd stride, partial tile): up front
-      const int rmax = last_rel - tn * kTile < kTile - 1 ? last_rel - tn * kTile : kTile - 1;
+    const int tn = t + kStages - 1;              // tile whose loads go out now
+    if (tn < ntiles) {
+      const char* next_src = first_row + (int64_t)tn * kTile * stride_bytes;
+      char* next_stage = smem + (tn % kStages) * kTileBytes;
+      if (contiguous && (tn < ntiles - 1 || last_full)) {
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) load_clamped(next_src, stride_bytes, rmax, next_stage, wave, i, lane_v);
+        for (int i = 0; i < kLoads; ++i) load_fast(next_src, next_stage, wave, i, dd0, dd1, ln16);
+      } else {                                   // any stride or a partial tile
+        const int rmax = last_rel - tn * kTile < kTile - 1 ? last_rel - tn * kTile : kTile - 1;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) load_clamped(next_src, stride_bytes, rmax, next_stage, wave, i, lane_v);
+      }
     }
 
-    // ---- scores S^T = K . Q^T; K operands kKAhead steps ahead; one next-tile load per
-    // 4 steps
+    // ---- scores S^T = K . Q^T; K operands kKAhead steps ahead;
     // two accumulation chains (even / odd k-steps): a dependent MFMA chain issues at about
     // 60 cycles per step, two interleaved chains at the MFMA rate (about 37)
     f32x16 st, st1;
@@ -321,7 +327,6 @@ mla_decode_bf16_kernel(DecodeParams P) {
       }
       if (ks & 1) st1 = mfma32x32x16(ka[ks], qop, st1);
       else st = mfma32x32x16(ka[ks], qop, st);
-      if ((ks & 3) == 3 && next_fast) load_fast(next_src, next_stage, wave, ks >> 2, dd0, dd1, ln16);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -344,7 +349,7 @@ mla_decode_bf16_kernel(DecodeParams P) {
         mt = fmaxf(mt, st[i]);
       }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = pair_max(mt);
     const bool grow = mt > m_ref + kRescaleSlack;
     if (__any(grow)) {
       const float m_new = grow ? mt : m_ref;

@@ -97,6 +97,14 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// max(x[l], x[l ^ 32]) over the two halves of the wave, through v_permlane32_swap:
+// swapping a register with itself leaves x[l] in one result and x[l ^ 32] in the other.
+__device__ __forceinline__ float pair_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // a *= alpha for an MFMA accumulator that lives in AGPRs.  VALU arithmetic cannot
