@@ -203,15 +203,19 @@ def merge_splits(o_part, lse_part):
     """Combine split results: softmax over a disjoint union of row sets.
 
     With M = max_s lse_s and w_s = exp(lse_s - M): o = sum_s w_s o_s / sum_s w_s and
-    lse = M + ln sum_s w_s.  Splits with lse_s = -inf get w_s = 0.
+    lse = M + ln sum_s w_s.  Splits with lse_s = -inf get w_s = 0; a query head that
+    no split saw (every lse_s = -inf) gets o = 0 and lse = -inf.
     """
     o_part = np.asarray(o_part, np.float64)
     lse_part = np.asarray(lse_part, np.float64)
     M = np.max(lse_part, axis=0)
-    w = np.exp(lse_part - M)                      # [S, n_q, n_h]
+    none = np.isneginf(M)                         # no split saw a row: o = 0, lse = -inf
+    Ms = np.where(none, 0.0, M)
+    w = np.exp(lse_part - Ms)                     # [S, n_q, n_h]; exp(-inf) = 0
     z = np.sum(w, axis=0)
-    o = np.einsum("snh,snhc->nhc", w, o_part) / z[..., None]
-    return o, M + np.log(z)
+    zs = np.where(none, 1.0, z)
+    o = np.einsum("snh,snhc->nhc", w, o_part) / zs[..., None]
+    return o, np.where(none, -np.inf, M + np.log(zs))
 
 
 def attend_latent(q_abs, c_kv, k_r, offsets, q_per_seq: int, scale: float):

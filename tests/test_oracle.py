@@ -335,6 +335,17 @@ def test_merge_of_any_partition_equals_the_unsplit_result(num_splits, split_rows
     assert np.all(op[empty] == 0)
 
 
+def test_merge_of_a_query_head_no_split_saw():
+    """Every split empty: the merge gives o = 0 and lse = -inf (the union of no rows)."""
+    o = np.zeros((3, 1, 2, 4))
+    lse = np.full((3, 1, 2), -np.inf)
+    o[1, 0, 1] = [1.0, 2.0, 3.0, 4.0]
+    lse[1, 0, 1] = 0.5                       # head 1 has one non-empty split, head 0 none
+    mo, ml = O.merge_splits(o, lse)
+    assert np.all(mo[0, 0] == 0.0) and ml[0, 0] == -np.inf
+    assert np.array_equal(mo[0, 1], o[1, 0, 1]) and ml[0, 1] == 0.5
+
+
 @pytest.mark.parametrize("mutant", ["uniform_weights", "lse_without_sum", "weights_not_normalised"])
 def test_planted_merge_mistakes_are_caught(mutant):
     """Plausible mistakes in the split merge fail the unsplit-result pin."""
