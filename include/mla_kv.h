@@ -19,6 +19,8 @@
  *   mla_merge_splits  log-sum-exp weighted combination of the splits
  *   mla_out_proj      o^C_i = W^UV_i o_lat_i                     (value absorption)
  *
+ * mla_merge_out_proj does the last two in one call, with the same results.
+ *
  * Together they compute, for query t and head i,
  *   o_{t,i} = sum_j softmax_j(q_{t,i}^T k_{j,i} * scale) v^C_{j,i}
  * with k_{j,i} = [W^UK_i c^KV_j ; k^R_j], v^C_{j,i} = W^UV_i c^KV_j and
@@ -38,7 +40,8 @@
  *    mla_decode needs d_c == 512, d_r == 64 and n_h % 32 == 0; mla_absorb_q
  *    needs d_c % 128 == 0, d_h % 16 == 0, d_h <= 256, d_r % 8 == 0;
  *    mla_out_proj needs d_h % 32 == 0, d_c % 64 == 0, d_c <= 512 (the
- *    DeepSeek-V2 attention shape fits all) and 16-byte aligned rows; other
+ *    DeepSeek-V2 attention shape fits all) and 16-byte aligned rows;
+ *    mla_merge_out_proj needs d_c == 512 and d_h % 64 == 0; other
  *    shapes return MLA_ERR_UNSUPPORTED.  dtype MLA_F32 runs plain fp32
  *    kernels for any shape (no bf16 rounding anywhere).
  */
@@ -54,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -196,6 +199,26 @@ mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t n_q, int32_t num_s
  */
 mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t n_q, const float* o_lat,
                           const void* w_uv, void* o_c, hipStream_t stream);
+
+/*
+ * mla_merge_out_proj - mla_merge_splits followed by mla_out_proj in one call
+ * (the merge as defined above, then [notes] "Value에 대한 수식 전개").  For
+ * dtype MLA_BF16 the merged latent never goes to memory: it is rounded to bf16
+ * on chip and projected there, and every output equals, bit for bit, what the
+ * two separate calls write.  Arguments as for those calls:
+ *
+ *   o_part, lse_part, partial_dtype, num_splits   as for mla_merge_splits
+ *   w_uv  [n_h, d_h, d_c] dtype,  o_c [n_q, n_h, d_h] dtype out
+ *   lse   [n_q, n_h] fp32 out, or NULL when not wanted
+ *   o_lat [n_q, n_h, d_c] fp32 out, or NULL when not wanted
+ * dtype MLA_F32 runs the two fp32 kernels in turn and needs lse and o_lat
+ * (both written).  MLA_BF16 needs d_c == 512, d_h % 64 == 0, 16-byte aligned
+ * o_part, w_uv and o_lat.
+ */
+mla_status_t mla_merge_out_proj(const mla_dims_t* dims, int32_t n_q, int32_t num_splits,
+                                int32_t partial_dtype, const void* o_part, const float* lse_part,
+                                const void* w_uv, void* o_c, float* lse, float* o_lat,
+                                hipStream_t stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

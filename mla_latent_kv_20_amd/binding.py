@@ -46,6 +46,7 @@ SIGNATURES = {
     "mla_decode": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _I64, _P, _I64, _P, _I32, _I32, _I32, _P, _P, _P]),
     "mla_merge_splits": (_I32, [_DIMS_P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "mla_out_proj": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P]),
+    "mla_merge_out_proj": (_I32, [_DIMS_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -185,6 +186,24 @@ def out_proj(d: MlaDims, o_lat, w_uv, o_c=None, out_dtype=None, stream=None):
     return o_c
 
 
+def merge_out_proj(d: MlaDims, o_part, lse_part, w_uv, o_c=None, lse=None, o_lat=None,
+                   want_lse: bool = True, want_o_lat: bool = False, stream=None):
+    """mla_merge_splits then mla_out_proj in one call -> (o_c, lse or None, o_lat or None)."""
+    import torch
+    S, n_q = o_part.shape[0], o_part.shape[1]
+    dev = o_part.device
+    if o_c is None:
+        o_c = torch.empty((n_q, d.n_h, d.d_h), dtype=w_uv.dtype, device=dev)
+    if lse is None and (want_lse or d.dtype == MLA_F32):
+        lse = torch.empty((n_q, d.n_h), dtype=torch.float32, device=dev)
+    if o_lat is None and (want_o_lat or d.dtype == MLA_F32):
+        o_lat = torch.empty((n_q, d.n_h, d.d_c), dtype=torch.float32, device=dev)
+    _check("mla_merge_out_proj", load().mla_merge_out_proj(
+        ctypes.byref(d), n_q, S, _dtype_code(o_part), _ptr(o_part), _ptr(lse_part), _ptr(w_uv), _ptr(o_c),
+        _ptr(lse), _ptr(o_lat), _stream(stream)))
+    return o_c, lse, o_lat
+
+
 def check_offsets(host_offsets, batch: int, q_per_seq: int, total_rows: int) -> int:
     """mla_check_offsets on a host int64 numpy array; returns the status code."""
     import numpy as np
@@ -199,11 +218,13 @@ def default_partial_dtype(d: MlaDims, num_splits: int) -> int:
 
 def decode_step(d: MlaDims, q_c, q_r, w_uk, w_uv, cache, offsets, batch: int, q_per_seq: int = 1,
                 num_splits: int = 1, split_rows: int = 0, bufs: Optional[dict] = None, stream=None,
-                partial_dtype: Optional[int] = None):
-    """All four calls on one packed cache [rows, d_c + d_r]; returns the output buffers.
+                partial_dtype: Optional[int] = None, fused: bool = False):
+    """One decode step on a packed cache [rows, d_c + d_r]; returns the output buffers.
 
     ``bufs`` may hold preallocated q_abs / o_part / lse_part / o_lat / lse / o_c tensors.
-    With one split the decode writes fp32 results that are already o_lat and lse.
+    Unfused: the four calls; with one fp32 split the decode's results already are o_lat
+    and lse.  Fused: mla_absorb_q, mla_decode, mla_merge_out_proj (o_lat is written only
+    when ``bufs`` holds it).
     """
     if partial_dtype is None:
         partial_dtype = default_partial_dtype(d, num_splits)
@@ -213,6 +234,10 @@ def decode_step(d: MlaDims, q_c, q_r, w_uk, w_uv, cache, offsets, batch: int, q_
     k_r = cache[:, d.d_c:d.d_c + d.d_r]
     o_part, lse_part = decode(d, q_abs, c_kv, k_r, offsets, batch, q_per_seq, num_splits, split_rows,
                               b.get("o_part"), b.get("lse_part"), stream, partial_dtype)
+    if fused:
+        o_c, lse, o_lat = merge_out_proj(d, o_part, lse_part, w_uv, b.get("o_c"), b.get("lse"),
+                                         b.get("o_lat"), stream=stream)
+        return dict(q_abs=q_abs, o_part=o_part, lse_part=lse_part, o_lat=o_lat, lse=lse, o_c=o_c)
     if num_splits == 1 and _dtype_code(o_part) == MLA_F32:
         o_lat, lse = o_part[0], lse_part[0]
     else:

@@ -20,6 +20,10 @@ hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, cons
 hipError_t launch_out_proj_bf16(const float* o_lat, const bf16_bits* w_uv, bf16_bits* o_c, int n_q,
                                 int n_h, int d_h, int d_c, hipStream_t stream);
 bool absorb_bf16_supported(int d_h, int d_c);
+bool merge_out_proj_bf16_supported(int d_h, int d_c);
+hipError_t launch_merge_out_proj_bf16(const void* o_part, bool f16_partials, const float* lse_part,
+                                      const uint16_t* w_uv, uint16_t* o_c, float* lse, float* o_lat,
+                                      int n_q, int n_h, int d_h, int num_splits, hipStream_t stream);
 bool out_proj_bf16_supported(int d_h, int d_c);
 hipError_t launch_merge(const void* o_part, bool f16_partials, const float* lse_part, float* o_lat,
                         float* lse, int n_q, int n_h, int d_c, int num_splits, hipStream_t stream);
@@ -182,6 +186,36 @@ mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t n_q, int32_t num_s
     return MLA_ERR_ALIGN;
   return launched(mla::launch_merge(o_part, partial_dtype == MLA_F16, lse_part, o_lat, lse, n_q,
                                     dims->n_h, dims->d_c, num_splits, stream));
+}
+
+mla_status_t mla_merge_out_proj(const mla_dims_t* dims, int32_t n_q, int32_t num_splits,
+                                int32_t partial_dtype, const void* o_part, const float* lse_part,
+                                const void* w_uv, void* o_c, float* lse, float* o_lat,
+                                hipStream_t stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (partial_dtype != MLA_F32 && partial_dtype != MLA_F16) return MLA_ERR_DTYPE;
+  if (n_q < 0 || num_splits < 1) return MLA_ERR_SHAPE;
+  if (n_q == 0) return MLA_OK;
+  if (!o_part || !lse_part || !w_uv || !o_c) return MLA_ERR_NULL;
+  if ((int64_t)n_q * dims->n_h * dims->d_c >= kMaxElems ||
+      (int64_t)num_splits * n_q * dims->n_h * dims->d_c >= kMaxElems ||
+      (int64_t)dims->n_h * dims->d_h * dims->d_c >= kMaxElems)
+    return MLA_ERR_SHAPE;
+  if (dims->dtype == MLA_F32) {
+    // The plain fp32 kernels, one after the other, with o_lat and lse as the intermediate.
+    if (!o_lat || !lse) return MLA_ERR_NULL;
+    st = mla_merge_splits(dims, n_q, num_splits, partial_dtype, o_part, lse_part, o_lat, lse, stream);
+    if (st != MLA_OK) return st;
+    return mla_out_proj(dims, n_q, o_lat, w_uv, o_c, stream);
+  }
+  if (!mla::merge_out_proj_bf16_supported(dims->d_h, dims->d_c)) return MLA_ERR_UNSUPPORTED;
+  if (!aligned(o_part, 16) || !aligned(w_uv, 16) || !aligned(o_c, 2) || !aligned(lse_part, 4) ||
+      (lse && !aligned(lse, 4)) || (o_lat && !aligned(o_lat, 16)))
+    return MLA_ERR_ALIGN;
+  return launched(mla::launch_merge_out_proj_bf16(o_part, partial_dtype == MLA_F16, lse_part,
+                                                  (const uint16_t*)w_uv, (uint16_t*)o_c, lse, o_lat,
+                                                  n_q, dims->n_h, dims->d_h, num_splits, stream));
 }
 
 mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t n_q, const float* o_lat, const void* w_uv,

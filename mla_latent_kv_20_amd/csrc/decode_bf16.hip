@@ -351,7 +351,9 @@ mla_decode_bf16_kernel(DecodeParams P) {
     }
     mt = pair_max(mt);
     const bool grow = mt > m_ref + kRescaleSlack;
-    if (__any(grow)) {
+    if (t == 0) {
+      m_ref = mt;                      // accumulators and l_run are still zero: nothing to rescale
+    } else if (__any(grow)) {
       const float m_new = grow ? mt : m_ref;
       const float alpha = fast_exp2(m_ref - m_new);
       l_run *= alpha;

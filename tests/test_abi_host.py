@@ -37,7 +37,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert set(names) == set(B.SIGNATURES), names
     for n in names:
         assert hasattr(lib, n)
-    assert lib.mla_abi_version() == 2
+    assert lib.mla_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -106,6 +106,27 @@ def test_absorb_merge_out_proj_argument_checks(lib):
     assert lib.mla_out_proj(byref(d), 4, FAKE + 2, FAKE, FAKE, None) == B.MLA_ERR_ALIGN
     assert lib.mla_out_proj(byref(dims(d_h=100)), 4, FAKE, FAKE, FAKE, None) == B.MLA_ERR_UNSUPPORTED
     assert lib.mla_out_proj(byref(dims(dtype=3)), 4, FAKE, FAKE, FAKE, None) == B.MLA_ERR_DTYPE
+
+
+def test_merge_out_proj_argument_checks(lib):
+    d = dims()
+    f = lambda d, n_q=4, S=2, part=B.MLA_F16, o_part=FAKE, lse_part=FAKE, w=FAKE, o_c=FAKE, lse=FAKE, o_lat=None: \
+        lib.mla_merge_out_proj(ctypes.byref(d), n_q, S, part, o_part, lse_part, w, o_c, lse, o_lat, None)
+    assert f(d, n_q=0, o_part=None, lse_part=None, w=None, o_c=None, lse=None) == B.MLA_OK
+    assert f(d, n_q=-1) == B.MLA_ERR_SHAPE
+    assert f(d, S=0) == B.MLA_ERR_SHAPE
+    assert f(d, part=B.MLA_BF16) == B.MLA_ERR_DTYPE
+    assert f(d, o_part=None) == B.MLA_ERR_NULL
+    assert f(d, w=None) == B.MLA_ERR_NULL
+    assert f(d, o_c=None) == B.MLA_ERR_NULL
+    assert f(dims(dtype=B.MLA_F32), lse=None, o_lat=FAKE) == B.MLA_ERR_NULL   # fp32 needs both
+    assert f(dims(dtype=B.MLA_F32), lse=FAKE, o_lat=None) == B.MLA_ERR_NULL
+    assert f(dims(d_h=96)) == B.MLA_ERR_UNSUPPORTED                         # 64-column blocks
+    assert f(dims(d_c=256)) == B.MLA_ERR_UNSUPPORTED
+    assert f(d, o_part=FAKE + 8) == B.MLA_ERR_ALIGN
+    assert f(d, o_lat=FAKE + 4) == B.MLA_ERR_ALIGN
+    assert f(d, lse=FAKE + 2) == B.MLA_ERR_ALIGN
+    assert f(dims(dtype=9)) == B.MLA_ERR_DTYPE
 
 
 def test_partial_bytes(lib):

@@ -170,27 +170,77 @@ def test_out_proj(torch, name):
     assert_close("o_c", D.to_numpy_f64(oc), O.out_proj(o_lat.astype(np.float64), w.f64("w_uv")), w)
 
 
+@pytest.mark.parametrize("S,f16,n_q", [(1, True, 1), (3, True, 33), (8, True, 32), (8, False, 64),
+                                        (13, False, 40), (64, True, 7), (70, True, 3)])
+def test_merge_out_proj_equals_the_two_calls(torch, S, f16, n_q):
+    """The fused call writes exactly what mla_merge_splits + mla_out_proj write."""
+    n_h, d_h, d_c = 128, 128, 512
+    say(f"[merge_out_proj] splits={S} partials={'f16' if f16 else 'f32'} n_q={n_q}")
+    o, l = W.draw_partials(S, n_q, n_h, d_c, seed=100 + S + n_q)
+    l[:, 0, 5] = -np.inf                  # one query head that no split saw
+    o[:, 0, 5] = 0.0
+    if f16:
+        o = o.astype(np.float16)
+    rng = np.random.default_rng(S)
+    w_uv = W.round_to_storage(rng.standard_normal((n_h, d_h, d_c)) / np.sqrt(d_c), W.BF16)
+    d = B.dims(n_h, d_h, d_c, 64, B.MLA_BF16)
+    ot, lt = torch.from_numpy(o).cuda(), torch.from_numpy(l).cuda()
+    wt = D._tensor(w_uv, W.BF16, "cuda")
+    ol, ll = B.merge_splits(d, ot, lt)
+    oc = B.out_proj(d, ol, wt)
+    oc2, ll2, ol2 = B.merge_out_proj(d, ot, lt, wt, want_o_lat=True)
+    oc3, _, _ = B.merge_out_proj(d, ot, lt, wt, want_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(oc, oc2) and torch.equal(oc, oc3)
+    assert torch.equal(ll, ll2) and torch.equal(ol, ol2)
+    ro, rl = O.merge_splits(o.astype(np.float64), l.astype(np.float64))
+    ref = O.out_proj(ro, W.to_f64(w_uv, W.BF16))
+    assert_close("o_c", D.to_numpy_f64(oc2), ref, workload("dsv2_small"))
+    assert np.all(D.to_numpy_f64(oc2)[0, 5] == 0.0) and np.isneginf(D.to_numpy_f64(ll2)[0, 5])
+
+
+def test_merge_out_proj_fp32(torch):
+    say("[merge_out_proj] fp32 dims n_h=4 d_h=16 d_c=32, splits=3")
+    o, l = W.draw_partials(3, 6, 4, 32, seed=12)
+    rng = np.random.default_rng(13)
+    w_uv = (rng.standard_normal((4, 16, 32)) / np.sqrt(32)).astype(np.float32)
+    d = B.dims(4, 16, 32, 8, B.MLA_F32)
+    oc, ll, ol = B.merge_out_proj(d, torch.from_numpy(o).cuda(), torch.from_numpy(l).cuda(),
+                                  torch.from_numpy(w_uv).cuda())
+    torch.cuda.synchronize()
+    ro, rl = O.merge_splits(o.astype(np.float64), l.astype(np.float64))
+    w32 = W.make_config("tiny_f32")
+    assert_close("o_c", D.to_numpy_f64(oc), O.out_proj(ro, w_uv.astype(np.float64)), w32)
+    assert_close("o_lat", D.to_numpy_f64(ol), ro, w32)
+    assert_close("lse", D.to_numpy_f64(ll), rl, w32, lse=True)
+
+
 # ----------------------------------------------------------------------------
 # The four calls end to end, from raw inputs
 # ----------------------------------------------------------------------------
 
-def run_step(w, S, R):
+def run_step(w, S, R, fused=False):
     t = D.to_device(w)
+    bufs = None
+    if fused:
+        import torch
+        bufs = dict(o_lat=torch.empty((w.n_q, w.n_h, w.d_c), dtype=torch.float32, device="cuda"))
     out = B.decode_step(dims_of(w), t["q_c"], t["q_r"], t["w_uk"], t["w_uv"], t["cache"],
-                        t["offsets"], w.batch, w.q_per_seq, S, R)
+                        t["offsets"], w.batch, w.q_per_seq, S, R, bufs=bufs, fused=fused)
     import torch
     torch.cuda.synchronize()
     return {k: D.to_numpy_f64(v) for k, v in out.items() if k in ("o_c", "o_lat", "lse")}
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("name", SMALL)
-def test_end_to_end(torch, name):
+def test_end_to_end(torch, name, fused):
     w = workload(name)
     a = oracle_args(w)
     naive = O.naive_decode(**a, seqs=[0, w.batch - 1] if w.d_c == 512 else None)
     for S, R in PLANS[name]:
-        say(f"[end_to_end] {name} splits={S} split_rows={R}")
-        got = run_step(w, S, R)
+        say(f"[end_to_end] {name} splits={S} split_rows={R} fused={fused}")
+        got = run_step(w, S, R, fused)
         ref = O.absorbed_decode(**a, num_splits=S, split_rows=R)
         assert_close("o_c", got["o_c"], ref["o_c"], w)
         assert_close("o_lat", got["o_lat"], ref["o_lat"], w)
