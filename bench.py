@@ -2,8 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
-A step is one pass of the whole path -- absorb_q, decode, merge (when split), out_proj --
-over one batch of a seeded synthetic DeepSeek-V2-shaped latent cache.  The cache and the
+A step is one pass of the whole path -- absorb_q, decode, then the split merge and the value
+projection (one fused call by default; --unfused runs merge_splits and out_proj) -- over one batch of a seeded synthetic DeepSeek-V2-shaped latent cache.  The cache and the
 two weight matrices are held in several device copies ("layers") used round-robin, so a
 step's inputs come from HBM rather than from the 256 MB on-chip Infinity Cache, as when
 consecutive layers of a model run.  Inputs are resident on the device before timing.
@@ -128,6 +128,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replay")
+    ap.add_argument("--unfused", action="store_true",
+                    help="step with mla_merge_splits + mla_out_proj instead of mla_merge_out_proj")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -176,11 +178,16 @@ def main():
                 lse=torch.empty((n_q, w.n_h), dtype=torch.float32, device=dev),
                 o_c=torch.empty((n_q, w.n_h, w.d_h), dtype=base["q_c"].dtype, device=dev))
 
+    fused = not args.unfused
+
     def step(i):
         L = layers[i % copies]
         qa = B.absorb_q(d, L["q_c"], L["q_r"], L["w_uk"], bufs["q_abs"])
         op, lp = B.decode(d, qa, L["cache"][:, :w.d_c], L["cache"][:, w.d_c:], L["offsets"], w.batch,
                           w.q_per_seq, S, R, bufs["o_part"], bufs["lse_part"])
+        if fused:
+            B.merge_out_proj(d, op, lp, L["w_uv"], bufs["o_c"], bufs["lse"], None)
+            return
         if S > 1 or part != B.MLA_F32:
             o_lat, _ = B.merge_splits(d, op, lp, bufs["o_lat"], bufs["lse"])
         else:
@@ -240,6 +247,9 @@ def main():
         "merge": (lambda L: B.merge_splits(d, bufs["o_part"], bufs["lse_part"], bufs["o_lat"], bufs["lse"]))
         if (S > 1 or part != B.MLA_F32) else None,
         "out_proj": lambda L: B.out_proj(d, bufs["o_lat"], L["w_uv"], bufs["o_c"]),
+        "merge_out_proj": (lambda L: B.merge_out_proj(d, bufs["o_part"], bufs["lse_part"], L["w_uv"],
+                                                      bufs["o_c"], bufs["lse"], None))
+        if d.dtype == B.MLA_BF16 else None,
     }
     per = {}
     for name, fn in calls.items():
@@ -286,6 +296,7 @@ def main():
         "kernels_ms_mean": {n: round(v, 5) for n, v in per.items()},
         "decode_merge_tokens_per_s": round(cached / ((dec_ms + per.get("merge", 0.0)) * 1e-3), 1),
         "timing": "hip graph replay of the step" if not args.no_graph else "eager launches",
+        "step_calls": "absorb_q, decode, merge_out_proj" if fused else "absorb_q, decode, merge_splits, out_proj",
         "mfma_frac_decode": round(flops / (dec_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
     }

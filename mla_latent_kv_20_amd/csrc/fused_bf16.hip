@@ -145,6 +145,57 @@ __device__ __forceinline__ void merge_one(const PartT* o_part, const float* lse_
   for (int e = 0; e < 8; ++e) o[e] = acc[e] * inv_z;
 }
 
+// Fast path (num_splits <= 8) for kRows (query, head) rows at once: every load of the
+// rows (lse values and split results, kept as raw 16-byte vectors) is issued before the
+// first reduction, so the wave waits on one memory latency for all of them.  Per row the
+// arithmetic is that of merge_one.
+template <typename PartT, int kRows>
+__device__ __forceinline__ void merge_rows_fast(const PartT* o_part, const float* lse_part,
+                                                int qh_count, const int* qh, int nrows,
+                                                int num_splits, int lane, float (*o)[8], float* M,
+                                                float* z) {
+  constexpr int kVec = 16 / (int)sizeof(PartT);       // elements per 16-byte load
+  typedef PartT pvec __attribute__((ext_vector_type(kVec)));
+  float lse_l[kRows];
+  pvec raw[kRows][kFFast][8 / kVec];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const bool live = r < nrows;
+    lse_l[r] = live && lane < num_splits ? lse_part[(size_t)lane * qh_count + qh[r]] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kFFast; ++k)
+      if (live && k < num_splits)
+#pragma unroll
+        for (int h = 0; h < 8 / kVec; ++h)
+          raw[r][k][h] = *(const pvec*)(o_part + ((size_t)k * qh_count + qh[r]) * kFDc + 8 * lane + kVec * h);
+  }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    if (r >= nrows) break;
+    M[r] = fwave_max(lse_l[r]);
+    if (M[r] == -INFINITY) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
+      z[r] = 0.f;
+      continue;
+    }
+    const float w_l = expf(lse_l[r] - M[r]);
+    z[r] = fwave_sum(w_l);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kFFast; ++k) {
+      if (k < num_splits) {
+        const float ws = __shfl(w_l, k);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, (float)raw[r][k][e / kVec][e % kVec], acc[e]);
+      }
+    }
+    const float inv_z = 1.0f / z[r];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[r][e] = acc[e] * inv_z;
+  }
+}
+
 // Workgroup = (head i, block of 64 output columns); workgroups are dealt round-robin over
 // the 8 XCDs and the column blocks of head i all run on XCD i % 8, so the head's split
 // results are fetched into one L2.  Per round of 32 queries: each of the 8 waves merges
@@ -179,22 +230,40 @@ merge_out_proj_kernel(FusedParams P) {
 
   for (int mb = 0; mb < P.n_q; mb += kFQBlock) {
     const int rows = P.n_q - mb < kFQBlock ? P.n_q - mb : kFQBlock;
-    // ---- merge rows mb .. mb+rows-1 of head i into LDS as bf16
-    for (int r = wave; r < rows; r += kFWaves) {
-      const int qh = (mb + r) * P.n_h + i;
-      float o[8], M, z;
-      merge_one(o_part, P.lse_part, qh_count, qh, P.num_splits, lane, o, M, z);
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      *(u32x4*)(o_lds + r * kFPitch + 16 * lane) =
-          u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                pack_bf16x2(o[6], o[7])};
-      if (cb == 0) {
-        if (P.o_lat) {
-          float* dst = P.o_lat + (size_t)qh * kFDc + 8 * lane;
-          *(f32x4*)dst = f32x4{o[0], o[1], o[2], o[3]};
-          *(f32x4*)(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+    // ---- merge rows mb .. mb+rows-1 of head i into LDS as bf16; wave w takes rows
+    // w, w + 8, w + 16, w + 24 (kRowsFast at a time when every split's loads fit in flight)
+    constexpr int kRowsFast = 2;
+    for (int r0 = wave; r0 < rows; r0 += kFWaves * kRowsFast) {
+      int qh[kRowsFast];
+      int nr = 0;
+#pragma unroll
+      for (int j = 0; j < kRowsFast; ++j) {
+        const int r = r0 + j * kFWaves;
+        qh[j] = (mb + (r < rows ? r : r0)) * P.n_h + i;
+        nr += r < rows ? 1 : 0;
+      }
+      float o[kRowsFast][8], M[kRowsFast], z[kRowsFast];
+      if (P.num_splits <= kFFast) {
+        merge_rows_fast<PartT, kRowsFast>(o_part, P.lse_part, qh_count, qh, nr, P.num_splits, lane, o, M, z);
+      } else {
+        for (int j = 0; j < nr; ++j) merge_one(o_part, P.lse_part, qh_count, qh[j], P.num_splits, lane, o[j], M[j], z[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < kRowsFast; ++j) {
+        if (j >= nr) break;
+        const int r = r0 + j * kFWaves;
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        *(u32x4*)(o_lds + r * kFPitch + 16 * lane) =
+            u32x4{pack_bf16x2(o[j][0], o[j][1]), pack_bf16x2(o[j][2], o[j][3]),
+                  pack_bf16x2(o[j][4], o[j][5]), pack_bf16x2(o[j][6], o[j][7])};
+        if (cb == 0) {
+          if (P.o_lat) {
+            float* dst = P.o_lat + (size_t)qh[j] * kFDc + 8 * lane;
+            *(f32x4*)dst = f32x4{o[j][0], o[j][1], o[j][2], o[j][3]};
+            *(f32x4*)(dst + 4) = f32x4{o[j][4], o[j][5], o[j][6], o[j][7]};
+          }
+          if (P.lse && lane == 0) P.lse[qh[j]] = M[j] == -INFINITY ? -INFINITY : M[j] + logf(z[j]);
         }
-        if (P.lse && lane == 0) P.lse[qh] = M == -INFINITY ? -INFINITY : M + logf(z);
       }
     }
     __syncthreads();
