@@ -41,7 +41,7 @@
  *    needs d_c % 128 == 0, d_h % 16 == 0, d_h <= 256, d_r % 8 == 0;
  *    mla_out_proj needs d_h % 32 == 0, d_c % 64 == 0, d_c <= 512 (the
  *    DeepSeek-V2 attention shape fits all) and 16-byte aligned rows;
- *    mla_merge_out_proj needs d_c == 512 and d_h % 64 == 0; other
+ *    mla_merge_out_proj needs d_c == 512 and d_h == 128; other
  *    shapes return MLA_ERR_UNSUPPORTED.  dtype MLA_F32 runs plain fp32
  *    kernels for any shape (no bf16 rounding anywhere).
  */
@@ -212,7 +212,7 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t n_q, const float* o_la
  *   lse   [n_q, n_h] fp32 out, or NULL when not wanted
  *   o_lat [n_q, n_h, d_c] fp32 out, or NULL when not wanted
  * dtype MLA_F32 runs the two fp32 kernels in turn and needs lse and o_lat
- * (both written).  MLA_BF16 needs d_c == 512, d_h % 64 == 0, 16-byte aligned
+ * (both written).  MLA_BF16 needs d_c == 512, d_h == 128, 16-byte aligned
  * o_part, w_uv and o_lat.
  */
 mla_status_t mla_merge_out_proj(const mla_dims_t* dims, int32_t n_q, int32_t num_splits,

@@ -20,9 +20,7 @@ namespace {
 constexpr int kFThreads = 512;
 constexpr int kFWaves = kFThreads / 64;
 constexpr int kFDc = 512;                    // latent width handled (one 512-wide stripe)
-constexpr int kFQBlock = 32;                 // query rows per round (the MFMA M dimension)
 constexpr int kFPitch = kFDc * 2 + 16;       // bf16 o_lat row in LDS, padded against conflicts
-constexpr int kFCols = 64;                   // output columns (of d_h) per workgroup
 constexpr int kFSteps = kFDc / 64;           // k-steps of 16 per wave: a quarter of d_c
 constexpr int kFFast = 8;                    // splits whose loads all go out at once
 
@@ -196,112 +194,125 @@ __device__ __forceinline__ void merge_rows_fast(const PartT* o_part, const float
   }
 }
 
-// Workgroup = (head i, block of 64 output columns); workgroups are dealt round-robin over
-// the 8 XCDs and the column blocks of head i all run on XCD i % 8, so the head's split
-// results are fetched into one L2.  Per round of 32 queries: each of the 8 waves merges
-// 4 (query, head) rows into LDS; then wave w multiplies the block by W^UV for column
-// half (w & 1) over k quarter (w >> 1), and the four k quarters are summed through LDS.
+// Workgroup = (head i, block of 16 query rows); workgroups are dealt round-robin over the
+// 8 XCDs and all query blocks of head i run on XCD i % 8, so W^UV_i is fetched into one L2.
+// Each of the 8 waves merges 2 of the block's rows (every load in flight at once) into
+// LDS as bf16.  The projection then runs as in mla_out_proj: for each 32-column block of
+// d_h, four k quarters of 8 MFMA steps summed in quarter order; wave w computes column
+// block (w & 3) for quarters (w >> 2) and (w >> 2) + 2.  The MFMA M dimension is 32, so
+// rows 16-31 of each product repeat rows 0-15 and are not stored.
+constexpr int kFRows = 16;                   // query rows per workgroup
+constexpr int kFColBlocks = 4;               // 32-column blocks of d_h = 128
+
 template <typename PartT>
 __global__ void __launch_bounds__(kFThreads)
 merge_out_proj_kernel(FusedParams P) {
-  __shared__ __attribute__((aligned(16))) char o_lds[kFQBlock * kFPitch];
-  __shared__ f32x16 red[kFWaves][64];
-  const int nblk = P.d_h / kFCols;
+  __shared__ __attribute__((aligned(16))) char o_lds[kFRows * kFPitch];
+  __shared__ f32x16 red[4][kFColBlocks][64];     // [k quarter][column block][lane]
+  const int qblocks = (P.n_q + kFRows - 1) / kFRows;
   const int xcd = blockIdx.x & 7;
   const int kq = blockIdx.x >> 3;
-  const int i = (kq / nblk) * 8 + xcd;
-  const int cb = (kq % nblk) * kFCols;
+  const int i = (kq / qblocks) * 8 + xcd;
+  const int mb = (kq % qblocks) * kFRows;
   if (i >= P.n_h) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int qh_count = P.n_q * P.n_h;
   const PartT* o_part = (const PartT*)P.o_part;
+  const int rows = P.n_q - mb < kFRows ? P.n_q - mb : kFRows;
 
-  // B operands, loaded once: lane l holds W^UV_i[ncol + l%32][k0 + 16s .. +7]
-  const int half = wave & 1;
-  const int kqtr = wave >> 1;
-  const int ncol = cb + 32 * half;
-  const int k0 = kqtr * kFSteps * 16 + 8 * (lane >> 5);
-  bf16x8 wb[kFSteps];
-  const bf16_bits* w = P.w_uv + ((size_t)i * P.d_h + ncol + (lane & 31)) * kFDc + k0;
+  // B operands: lane l holds W^UV_i[32 cbk + l%32][16 (8 q + s) + 8 (l/32) .. +7] for the
+  // wave's two quarters q
+  const int cbk = wave & 3;
+  const int q0 = wave >> 2;
+  bf16x8 wb[2][kFSteps];
+  {
+    const bf16_bits* w = P.w_uv + ((size_t)i * P.d_h + 32 * cbk + (lane & 31)) * kFDc + 8 * (lane >> 5);
 #pragma unroll
-  for (int s = 0; s < kFSteps; ++s) wb[s] = *(const bf16x8*)(w + 16 * s);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int s = 0; s < kFSteps; ++s) wb[h][s] = *(const bf16x8*)(w + 16 * (kFSteps * (q0 + 2 * h) + s));
+  }
 
-  for (int mb = 0; mb < P.n_q; mb += kFQBlock) {
-    const int rows = P.n_q - mb < kFQBlock ? P.n_q - mb : kFQBlock;
-    // ---- merge rows mb .. mb+rows-1 of head i into LDS as bf16; wave w takes rows
-    // w, w + 8, w + 16, w + 24 (kRowsFast at a time when every split's loads fit in flight)
-    constexpr int kRowsFast = 2;
-    for (int r0 = wave; r0 < rows; r0 += kFWaves * kRowsFast) {
-      int qh[kRowsFast];
-      int nr = 0;
+  // ---- merge rows wave and wave + 8 of the block into LDS as bf16
+  {
+    int qh[2];
+    int nr = 0;
 #pragma unroll
-      for (int j = 0; j < kRowsFast; ++j) {
-        const int r = r0 + j * kFWaves;
-        qh[j] = (mb + (r < rows ? r : r0)) * P.n_h + i;
-        nr += r < rows ? 1 : 0;
-      }
-      float o[kRowsFast][8], M[kRowsFast], z[kRowsFast];
-      if (P.num_splits <= kFFast) {
-        merge_rows_fast<PartT, kRowsFast>(o_part, P.lse_part, qh_count, qh, nr, P.num_splits, lane, o, M, z);
-      } else {
-        for (int j = 0; j < nr; ++j) merge_one(o_part, P.lse_part, qh_count, qh[j], P.num_splits, lane, o[j], M[j], z[j]);
-      }
-#pragma unroll
-      for (int j = 0; j < kRowsFast; ++j) {
-        if (j >= nr) break;
-        const int r = r0 + j * kFWaves;
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        *(u32x4*)(o_lds + r * kFPitch + 16 * lane) =
-            u32x4{pack_bf16x2(o[j][0], o[j][1]), pack_bf16x2(o[j][2], o[j][3]),
-                  pack_bf16x2(o[j][4], o[j][5]), pack_bf16x2(o[j][6], o[j][7])};
-        if (cb == 0) {
-          if (P.o_lat) {
-            float* dst = P.o_lat + (size_t)qh[j] * kFDc + 8 * lane;
-            *(f32x4*)dst = f32x4{o[j][0], o[j][1], o[j][2], o[j][3]};
-            *(f32x4*)(dst + 4) = f32x4{o[j][4], o[j][5], o[j][6], o[j][7]};
-          }
-          if (P.lse && lane == 0) P.lse[qh[j]] = M[j] == -INFINITY ? -INFINITY : M[j] + logf(z[j]);
-        }
-      }
+    for (int j = 0; j < 2; ++j) {
+      const int r = wave + j * kFWaves;
+      qh[j] = (mb + (r < rows ? r : 0)) * P.n_h + i;
+      nr += r < rows ? 1 : 0;
     }
-    __syncthreads();
+    // rows past the block's last valid row: their LDS rows still get finite values
+    float o[2][8], M[2], z[2];
+    if (P.num_splits <= kFFast) {
+      merge_rows_fast<PartT, 2>(o_part, P.lse_part, qh_count, qh, nr, P.num_splits, lane, o, M, z);
+    } else {
+      for (int j = 0; j < nr; ++j) merge_one(o_part, P.lse_part, qh_count, qh[j], P.num_splits, lane, o[j], M[j], z[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = wave + j * kFWaves;
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      if (j >= nr) {                               // unused row: zeros in LDS, nothing stored
+        *(u32x4*)(o_lds + r * kFPitch + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+        continue;
+      }
+      *(u32x4*)(o_lds + r * kFPitch + 16 * lane) =
+          u32x4{pack_bf16x2(o[j][0], o[j][1]), pack_bf16x2(o[j][2], o[j][3]),
+                pack_bf16x2(o[j][4], o[j][5]), pack_bf16x2(o[j][6], o[j][7])};
+      if (P.o_lat) {
+        float* dst = P.o_lat + (size_t)qh[j] * kFDc + 8 * lane;
+        *(f32x4*)dst = f32x4{o[j][0], o[j][1], o[j][2], o[j][3]};
+        *(f32x4*)(dst + 4) = f32x4{o[j][4], o[j][5], o[j][6], o[j][7]};
+      }
+      if (P.lse && lane == 0) P.lse[qh[j]] = M[j] == -INFINITY ? -INFINITY : M[j] + logf(z[j]);
+    }
+  }
+  __syncthreads();
 
-    // ---- o_c block = o_lat block (bf16) . W^UV_i^T, this wave's k quarter
-    const int m = lane & 31;
-    const char* a = o_lds + (m < rows ? m : 0) * kFPitch + 2 * k0;
-    f32x16 acc;
+  // ---- o_c block = o_lat block (bf16) . W^UV_i^T
+  {
+    const char* a = o_lds + (lane & 15) * kFPitch + 16 * (lane >> 5);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int h = 0; h < 2; ++h) {
+      const int q = q0 + 2 * h;
+      f32x16 acc;
 #pragma unroll
-    for (int s = 0; s < kFSteps; ++s) acc = mfma32x32x16(*(const bf16x8*)(a + 32 * s), wb[s], acc);
-    red[wave][lane] = acc;
-    __syncthreads();
-    // wave (half, kqtr) sums registers 4 kqtr .. 4 kqtr + 3 of column half `half` over the
-    // four k quarters, in quarter order.  D[m][n]: lane l, reg r -> row 8(r/4) + 4(l/32) + r%4.
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 4 * kqtr + q;
-      const float v = red[half][lane][r] + red[half + 2][lane][r] + red[half + 4][lane][r] +
-                      red[half + 6][lane][r];
-      const int mm = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      for (int s = 0; s < kFSteps; ++s)
+        acc = mfma32x32x16(*(const bf16x8*)(a + 32 * (kFSteps * q + s)), wb[h][s], acc);
+      red[q][cbk][lane] = acc;
+    }
+  }
+  __syncthreads();
+  // wave w finishes column block (w & 3), registers 8 (w >> 2) .. +7: rows 16 (w >> 2)
+  // .. +15 of the D layout (lane l, reg r -> row 8 (r/4) + 4 (l/32) + r%4); only rows < 16
+  // are real, so waves 4-7 have nothing to store.
+  if (q0 == 0) {
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const float v = red[0][cbk][lane][rr] + red[1][cbk][lane][rr] + red[2][cbk][lane][rr] +
+                      red[3][cbk][lane][rr];
+      const int mm = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
       if (mm < rows)
-        P.o_c[((size_t)(mb + mm) * P.n_h + i) * P.d_h + ncol + (lane & 31)] = f32_to_bf16(v);
+        P.o_c[((size_t)(mb + mm) * P.n_h + i) * P.d_h + 32 * cbk + (lane & 31)] = f32_to_bf16(v);
     }
-    __syncthreads();                               // o_lds and red are reused next round
   }
 }
 
 }  // namespace
 
-bool merge_out_proj_bf16_supported(int d_h, int d_c) { return d_c == kFDc && d_h % kFCols == 0; }
+bool merge_out_proj_bf16_supported(int d_h, int d_c) { return d_c == kFDc && d_h == 32 * kFColBlocks; }
 
 hipError_t launch_merge_out_proj_bf16(const void* o_part, bool f16_partials, const float* lse_part,
                                       const bf16_bits* w_uv, bf16_bits* o_c, float* lse, float* o_lat,
                                       int n_q, int n_h, int d_h, int num_splits, hipStream_t stream) {
   FusedParams P{o_part, lse_part, w_uv, o_c, lse, o_lat, n_q, n_h, d_h, num_splits};
-  const int grid = 8 * ((n_h + 7) / 8) * (d_h / kFCols);
+  const int grid = 8 * ((n_h + 7) / 8) * ((n_q + kFRows - 1) / kFRows);
   if (f16_partials)
     hipLaunchKernelGGL(merge_out_proj_kernel<_Float16>, dim3(grid), dim3(kFThreads), 0, stream, P);
   else

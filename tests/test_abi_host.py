@@ -121,7 +121,7 @@ def test_merge_out_proj_argument_checks(lib):
     assert f(d, o_c=None) == B.MLA_ERR_NULL
     assert f(dims(dtype=B.MLA_F32), lse=None, o_lat=FAKE) == B.MLA_ERR_NULL   # fp32 needs both
     assert f(dims(dtype=B.MLA_F32), lse=FAKE, o_lat=None) == B.MLA_ERR_NULL
-    assert f(dims(d_h=96)) == B.MLA_ERR_UNSUPPORTED                         # 64-column blocks
+    assert f(dims(d_h=96)) == B.MLA_ERR_UNSUPPORTED                         # d_h = 128 only
     assert f(dims(d_c=256)) == B.MLA_ERR_UNSUPPORTED
     assert f(d, o_part=FAKE + 8) == B.MLA_ERR_ALIGN
     assert f(d, o_lat=FAKE + 4) == B.MLA_ERR_ALIGN
