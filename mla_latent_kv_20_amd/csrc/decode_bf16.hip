@@ -44,6 +44,8 @@ constexpr int kStages = 2;
 constexpr int kKSteps = kDqk / 16;       // 36 MFMA k-steps for the scores
 constexpr int kKReg = kDc / 16;          // 32 k-steps with the query operand in VGPRs (latent part)
 constexpr int kQRopeBytes = kHeadsPerWg * kDr * 2;            // RoPE part of the queries, in LDS
+constexpr int kQStageWave = 32 * 512;    // query staging per wave: 32 heads x 256 columns bf16
+constexpr int kQStageLoads = 2 * kQStageWave / 1024;          // 1 KiB loads per wave, both halves
 constexpr int kDvTiles = kDc / 32;       // 16 output tiles of 32 dv
 constexpr float kRescaleSlack = 8.0f;    // log2 units
 constexpr int kKAhead = 6;               // K operand reads in flight
@@ -208,45 +210,71 @@ mla_decode_bf16_kernel(DecodeParams P) {
   make_deltas(wave, lane, d0, d1);
   const uint32_t lane16 = (uint32_t)lane * 16;
 
-  // ---- prologue: start the first tiles, then fetch this wave's queries
-#pragma unroll
-  for (int t = 0; t < kStages - 1; ++t) {
-    if (t < ntiles) {
-      const char* src = first_row + (int64_t)t * kTile * stride_bytes;
-      char* stage = smem + t * kTileBytes;
-      if (contiguous && (t < ntiles - 1 || last_full)) {
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) load_fast(src, stage, wave, i, d0, d1, lane16);
-      } else {
-        const int rmax = last_rel - t * kTile < kTile - 1 ? last_rel - t * kTile : kTile - 1;
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) load_clamped(src, stride_bytes, rmax, stage, wave, i, lane);
-      }
-    }
-  }
-
-  // Queries: the latent part (k-steps 0..31) lives in VGPRs as MFMA B operands; the RoPE
-  // part (k-steps 32..35) of all 128 heads sits in LDS after the tile stages, 128 bytes
-  // per head with its 16-byte chunks swapped by (head & 7), and is read per tile.
+  // ---- prologue.  Queries: the latent part (k-steps 0..31) lives in VGPRs as MFMA B
+  // operands; the RoPE part (k-steps 32..35) of all 128 heads sits in LDS after the tile
+  // stages, 128 bytes per head with its 16-byte chunks swapped by (head & 7), and is read
+  // per tile.  The latent part comes in two halves of 256 columns through an LDS staging
+  // area with direct-to-LDS loads, each instruction reading two contiguous 512-byte
+  // half-rows (a register load of the MFMA layout would touch 32 rows per instruction).
+  // In the staging area, wave w owns heads 32w .. 32w+31 at 512 bytes each, chunk c of
+  // head h stored at chunk c ^ (h & 15).
   bf16x8 qb[kKReg];
   char* qrope = smem + kStages * kTileBytes;
+  char* qstage = qrope + kQRopeBytes + wave * kQStageWave;
+  const int hc = threadIdx.x & 7;
+  bf16x8 rope_v[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {                  // RoPE part: chunk t%8 of heads t/8 + 32g
+    int hq = hg * kHeadsPerWg + (threadIdx.x >> 3) + 32 * g;
+    hq = hq < P.n_h ? hq : P.n_h - 1;
+    rope_v[g] = *(const bf16x8*)(P.q_abs + ((size_t)n * P.n_h + hq) * kDqk + kDc + hc * 8);
+  }
+  const char* qbase = (const char*)(P.q_abs + ((size_t)n * P.n_h + hg * kHeadsPerWg) * kDqk);
+  uint32_t qoff[kQStageLoads / 2];               // per-lane source offsets, half 0 (half 1: +512)
+#pragma unroll
+  for (int j = 0; j < kQStageLoads / 2; ++j) {
+    const int hl = 2 * j + (lane >> 5);          // head of the wave filled by this lane
+    int hq = wave * 32 + hl;
+    hq = hg * kHeadsPerWg + hq < P.n_h ? hq : P.n_h - 1 - hg * kHeadsPerWg;
+    const int c = (lane & 31) ^ (hl & 15);
+    qoff[j] = (uint32_t)(hq * kRowBytes + c * 16);
+  }
+  const uint32_t qstage_lds = __builtin_amdgcn_readfirstlane(lds_addr(qstage));
+#pragma unroll
+  for (int j = 0; j < kQStageLoads / 2; ++j) global_to_lds16_sv(qbase, qoff[j], qstage_lds + j * 1024);
+
+  // first tile
   {
-    const bf16_bits* q = P.q_abs + ((size_t)n * P.n_h + head_ld) * kDqk + (lane >> 5) * 8;
+    const char* src = first_row;
+    char* stage = smem;
+    if (contiguous && (0 < ntiles - 1 || last_full)) {
 #pragma unroll
-    for (int ks = 0; ks < kKReg; ++ks) qb[ks] = *(const bf16x8*)(q + ks * 16);
-    // RoPE part: thread t copies chunk t%8 of head t/8 and of head t/8 + 32, 64, 96.
-    const int hc = threadIdx.x & 7;
+      for (int i = 0; i < kLoads; ++i) load_fast(src, stage, wave, i, d0, d1, lane16);
+    } else {
+      const int rmax = last_rel < kTile - 1 ? last_rel : kTile - 1;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int h = (threadIdx.x >> 3) + 32 * g;                 // head within the group
-      int hq = hg * kHeadsPerWg + h;
-      hq = hq < P.n_h ? hq : P.n_h - 1;
-      const bf16x8 v = *(const bf16x8*)(P.q_abs + ((size_t)n * P.n_h + hq) * kDqk + kDc + hc * 8);
-      *(bf16x8*)(qrope + h * 128 + 16 * (hc ^ (h & 7))) = v;
+      for (int i = 0; i < kLoads; ++i) load_clamped(src, stride_bytes, rmax, stage, wave, i, lane);
     }
   }
-  // All queries (and the prologue tiles) resident.  A builtin wait, so the compiler knows
-  // the queries have landed and places no vmcnt waits for them inside the tile loop,
+  const char* qrd = qstage + (lane & 31) * 512;  // this lane's head row in the staging area
+  const int qx = lane & 15;                      // its chunk swap (head & 15)
+  wait_vmcnt<kLoads>();                          // half 0 (and the RoPE loads) landed
+#pragma unroll
+  for (int ks = 0; ks < kKReg / 2; ++ks) qb[ks] = *(const bf16x8*)(qrd + 16 * ((2 * ks + (lane >> 5)) ^ qx));
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the area is refilled
+#pragma unroll
+  for (int j = 0; j < kQStageLoads / 2; ++j) global_to_lds16_sv(qbase, qoff[j] + 512, qstage_lds + j * 1024);
+  wait_vmcnt<0>();                               // half 1 and the first tile landed
+#pragma unroll
+  for (int ks = 0; ks < kKReg / 2; ++ks)
+    qb[kKReg / 2 + ks] = *(const bf16x8*)(qrd + 16 * ((2 * ks + (lane >> 5)) ^ qx));
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int h = (threadIdx.x >> 3) + 32 * g;   // head within the group
+    *(bf16x8*)(qrope + h * 128 + 16 * (hc ^ (h & 7))) = rope_v[g];
+  }
+  // All queries (and the first tile) resident.  A builtin wait, so the compiler knows
+  // the query loads have landed and places no vmcnt waits for them inside the tile loop,
   // where they would also stall on in-flight tile prefetches.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
@@ -445,7 +473,7 @@ hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* rows, int
   P.scale_log2 = (float)((double)scale * 1.4426950408889634);
   const long long grid = (long long)P.streams_per_xcd * 8 * P.group_size;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  size_t smem = (size_t)kStages * kTileBytes + kQRopeBytes;
+  size_t smem = (size_t)kStages * kTileBytes + kQRopeBytes + (size_t)kWaves * kQStageWave;
   const size_t out_stage = (size_t)kWaves * 32 * (f16_partials ? out_row_bytes<_Float16>() : out_row_bytes<float>());
   smem = smem > out_stage ? smem : out_stage;
   // Dynamic LDS above 64 KiB must be allowed once per kernel (thread-safe static init).
