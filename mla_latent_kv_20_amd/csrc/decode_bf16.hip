@@ -17,7 +17,8 @@
 //     up, so the loads go out in one burst with the previous tile's already landed, and
 //     only one tile is in flight.)
 //   * S^T[32 rows x 32 heads] = K_tile[32 x 576] . Q^T (36 MFMA 32x32x16), with the
-//     wave's queries resident in VGPRs as MFMA B operands;
+//     wave's queries resident in VGPRs as MFMA B operands and the scores accumulated in
+//     VGPRs;
 //   * online softmax in registers: lane l owns head l%32 (16 of the 32 rows; lane
 //     l^32 owns the other 16), max exchanged across the pair;
 //   * O^T[512 dv x 32 heads] += V_tile^T . P^T (32 MFMA), V^T operands read from the
@@ -328,7 +329,8 @@ mla_decode_bf16_kernel(DecodeParams P) {
 
     // ---- scores S^T = K . Q^T; K operands kKAhead steps ahead;
     // two accumulation chains (even / odd k-steps): a dependent MFMA chain issues at about
-    // 60 cycles per step, two interleaved chains at the MFMA rate (about 37)
+    // 60 cycles per step, two interleaved chains at the MFMA rate (about 37).  The score
+    // accumulators stay in VGPRs (inline-assembly MFMAs) so that the AGPRs hold all of acc.
     f32x16 st, st1;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -353,11 +355,13 @@ mla_decode_bf16_kernel(DecodeParams P) {
         const int c = 2 * (ks - kKReg) + (lane >> 5);
         qop = *(const bf16x8*)(qrope + hl * 128 + 16 * (c ^ (hl & 7)));
       }
-      if (ks & 1) st1 = mfma32x32x16(ka[ks], qop, st1);
-      else st = mfma32x32x16(ka[ks], qop, st);
+      if (ks & 1) mfma_acc_vgpr(st1, ka[ks], qop);
+      else mfma_acc_vgpr(st, ka[ks], qop);
       __builtin_amdgcn_sched_barrier(0);
     }
 
+    mfma_vgpr_drain(st);
+    mfma_vgpr_drain(st1);
     st += st1;
 
     // ---- online softmax (log2 domain)

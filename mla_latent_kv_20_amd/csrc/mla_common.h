@@ -105,6 +105,23 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// acc += A . B (v_mfma_f32_32x32x16_bf16) with the accumulator in VGPRs, issued from inline
+// assembly so that it stays in VGPRs while the compiler's own MFMAs keep their
+// accumulators in the AGPR file.  The compiler does not see this MFMA's latency:
+//  - back-to-back calls on the same accumulator need no wait (the MFMA forwards srcC);
+//  - a VALU write of the accumulator or operands needs 2 wait states before the call
+//    (keep such writes a few instructions away);
+//  - before any other instruction reads the accumulator, call mfma_vgpr_drain().
+__device__ __forceinline__ void mfma_acc_vgpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+// 12 wait states (what the compiler places between this MFMA and a VALU read of its
+// result on gfx950), with the accumulator as an operand so later reads stay behind it.
+__device__ __forceinline__ void mfma_vgpr_drain(f32x16& acc) {
+  asm volatile("s_nop 11" : "+v"(acc));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // a *= alpha for an MFMA accumulator that lives in AGPRs.  VALU arithmetic cannot
