@@ -131,8 +131,11 @@ size_t mla_partial_bytes(const mla_dims_t* dims, int32_t n_q, int32_t num_splits
  * x_j = q_abs[n,i,:] . row_j * scale over the split's rows:
  *   o_part[s, n, i, :] = sum_j softmax(x)_j * c_kv_j        (fp32)
  *   lse_part[s, n, i]  = ln sum_j exp(x_j)                  (fp32, natural log)
- * A split with no row gets o_part = 0 and lse_part = -inf.  With num_splits == 1
- * the outputs already are the final o_lat and lse.
+ * A split with no row gets lse_part = -inf and its o_part entries are not
+ * written (they keep whatever the buffer held); mla_merge_splits and
+ * mla_merge_out_proj give such a split weight zero and do not use its o_part.
+ * With num_splits == 1 (and no empty split) the outputs already are the final
+ * o_lat and lse.
  *
  *   q_abs       [batch*q_per_seq, n_h, d_c+d_r]  dtype   from mla_absorb_q
  *   c_kv        rows of d_c elements at a stride of c_stride elements  dtype
@@ -175,8 +178,9 @@ mla_status_t mla_check_offsets(const int64_t* host_offsets, int32_t batch,
  * mla_merge_splits - combine split results.  Softmax over a disjoint union of
  * row sets: with M = max_s lse_s and w_s = exp(lse_s - M),
  *   o_lat = sum_s w_s o_s / sum_s w_s,   lse = M + ln sum_s w_s.
- * Splits with lse_s = -inf get weight 0; a query head whose every split is
- * empty gets o_lat = 0 and lse = -inf.
+ * Splits with lse_s = -inf get weight 0 and their o_part values are not used
+ * (an empty split's o_part is never written by mla_decode); a query head whose
+ * every split is empty gets o_lat = 0 and lse = -inf.
  *
  *   o_part   [num_splits, n_q, n_h, d_c] in partial_dtype (MLA_F32 or MLA_F16)
  *   lse_part [num_splits, n_q, n_h] fp32

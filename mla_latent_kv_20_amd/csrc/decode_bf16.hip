@@ -192,11 +192,8 @@ mla_decode_bf16_kernel(DecodeParams P) {
   if (lo < 0) lo = 0;
 
   const size_t out_row = ((size_t)s * P.n_q + n) * P.n_h;
-  if (hi <= lo) {                      // empty split: zero output, lse = -inf
-    if (!active) return;
-    OutT* o = (OutT*)P.o_part + (out_row + head) * kDc;
-    for (int c = (lane >> 5) * 4; c < kDc; c += 8) put4(o + c, 0.f, 0.f, 0.f, 0.f);
-    if (lane < 32) P.lse_part[out_row + head] = -INFINITY;
+  if (hi <= lo) {                      // empty split: lse = -inf marks it; o_part is not written
+    if (active && lane < 32) P.lse_part[out_row + head] = -INFINITY;
     return;
   }
 

@@ -86,7 +86,7 @@ __device__ __forceinline__ void merge_one(const PartT* o_part, const float* lse_
       if (k < num_splits) {
         const float ws = __shfl(w_l, k);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, v[k][e], acc[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, v[k][e], acc[e]) : acc[e];
       }
     }
     const float inv_z = 1.0f / z;
@@ -128,7 +128,7 @@ __device__ __forceinline__ void merge_one(const PartT* o_part, const float* lse_
       for (int k = 0; k < 8; ++k) {
         const float ws = __shfl(wl, u + k);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, v[k][e], acc[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, v[k][e], acc[e]) : acc[e];
       }
     }
     for (; u < cnt; ++u) {
@@ -136,7 +136,7 @@ __device__ __forceinline__ void merge_one(const PartT* o_part, const float* lse_
       load8p(o_part + ((size_t)(s0 + u) * qh_count + qh) * kFDc + c, v);
       const float ws = __shfl(wl, u);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, v[e], acc[e]);
+      for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, v[e], acc[e]) : acc[e];
     }
   }
 #pragma unroll
@@ -185,7 +185,7 @@ __device__ __forceinline__ void merge_rows_fast(const PartT* o_part, const float
       if (k < num_splits) {
         const float ws = __shfl(w_l, k);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, (float)raw[r][k][e / kVec][e % kVec], acc[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, (float)raw[r][k][e / kVec][e % kVec], acc[e]) : acc[e];
       }
     }
     const float inv_z = 1.0f / z[r];

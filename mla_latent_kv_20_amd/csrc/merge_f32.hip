@@ -6,6 +6,8 @@
 //
 // merge: softmax over the union of disjoint row sets.  With M = max_s lse_s and
 // w_s = exp(lse_s - M), o = sum_s w_s o_s / sum_s w_s and lse = M + ln sum_s w_s.
+// A split of weight zero (an empty split, lse = -inf, whose o_s the decode does not
+// write) is left out of the sum, so whatever its o_s holds never enters it.
 //
 // The fp32 kernels compute the same four steps with no bf16 rounding, for any shape.
 // They are simple (one thread per output element, or one workgroup per query head)
@@ -85,7 +87,7 @@ merge_splits_kernel(const PartT* __restrict__ o_part, const float* __restrict__ 
       if (k < num_splits) {
         const float ws = __shfl(w_l, k);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, v[k][e], acc[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, v[k][e], acc[e]) : acc[e];
       }
     }
     const float inv_z = 1.0f / z;
@@ -133,7 +135,7 @@ merge_splits_kernel(const PartT* __restrict__ o_part, const float* __restrict__ 
         for (int k = 0; k < 8; ++k) {
           const float ws = __shfl(wl, u + k);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, v[k][e], acc[e]);
+          for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, v[k][e], acc[e]) : acc[e];
         }
       }
       for (; u < cnt; ++u) {
@@ -143,7 +145,7 @@ merge_splits_kernel(const PartT* __restrict__ o_part, const float* __restrict__ 
         else v[0] = load1(p);
         const float ws = __shfl(wl, u);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, v[e], acc[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, v[e], acc[e]) : acc[e];
       }
     }
     if (vec) {
@@ -267,8 +269,7 @@ decode_f32_kernel(const float* __restrict__ q_abs, const float* __restrict__ c_k
     __syncthreads();
   }
   const size_t out = (size_t)s * n_q * n_h + qh;
-  if (hi <= lo) {
-    for (int c = threadIdx.x; c < d_c; c += kDecThreads) o_part[out * d_c + c] = 0.f;
+  if (hi <= lo) {                                 // empty split: lse = -inf, o_part not written
     if (threadIdx.x == 0) lse_part[out] = -INFINITY;
     return;
   }

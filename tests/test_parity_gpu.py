@@ -116,12 +116,17 @@ def test_decode(torch, name):
     partials = [B.MLA_F32, B.MLA_F16] if w.dtype == W.BF16 else [B.MLA_F32]
     for (S, R), pd in [(plan, pd) for plan in PLANS[name] for pd in partials]:
         say(f"[decode] {name} splits={S} split_rows={R} partials={'f16' if pd == B.MLA_F16 else 'f32'}")
+        # NaN-filled: every non-empty split's row must be written; empty ones are left alone
+        op0 = torch.full((S, w.n_q, w.n_h, w.d_c), float("nan"), dtype=B._torch_dtype(pd), device="cuda")
         op, lp = B.decode(d, qa_t, t["c_kv"], t["k_r"], t["offsets"], w.batch, w.q_per_seq, S, R,
-                          partial_dtype=pd)
+                          o_part=op0)
         torch.cuda.synchronize()
         ro, rl = O.split_partials(W.to_f64(qa, w.dtype), w.f64("c_kv"), w.f64("k_r"), w.offsets,
                                   w.q_per_seq, S, R, O.default_scale(w.d_h, w.d_r))
-        assert_close("o_part", D.to_numpy_f64(op), ro, w)
+        live = ~np.isneginf(rl)
+        got_o = D.to_numpy_f64(op)
+        assert np.all(np.isnan(got_o[~live]))
+        assert_close("o_part", got_o[live], ro[live], w)
         assert_close("lse_part", D.to_numpy_f64(lp), rl, w, lse=True)
 
 
@@ -269,17 +274,30 @@ def test_empty_splits_and_ragged_tails(torch):
     qa = W.draw_q_abs(w, seed=7)
     t = D.to_device(w)
     say("[edge] empty splits and ragged tails, splits=6 split_rows=40")
+    op0 = torch.full((6, w.n_q, w.n_h, w.d_c), float("nan"), dtype=torch.float16, device="cuda")
     op, lp = B.decode(d, D._tensor(qa, w.dtype, "cuda"), t["c_kv"], t["k_r"], t["offsets"], w.batch,
-                      1, 6, 40)
+                      1, 6, 40, o_part=op0)
     torch.cuda.synchronize()
     ro, rl = O.split_partials(W.to_f64(qa, w.dtype), w.f64("c_kv"), w.f64("k_r"), w.offsets, 1, 6, 40,
                               O.default_scale(w.d_h, w.d_r))
     got_o, got_l = D.to_numpy_f64(op), D.to_numpy_f64(lp)
     empty = np.isneginf(rl)
     assert empty.any()
-    assert np.all(got_o[empty] == 0.0) and np.all(np.isneginf(got_l[empty]))
-    assert_close("o_part", got_o, ro, w)
+    # empty splits: lse = -inf, o_part untouched (still NaN)
+    assert np.all(np.isnan(got_o[empty])) and np.all(np.isneginf(got_l[empty]))
+    assert_close("o_part", got_o[~empty], ro[~empty], w)
     assert_close("lse_part", got_l, rl, w, lse=True)
+    # the merges never read an empty split's o_part: NaN there must not reach their outputs
+    mo, ml = O.merge_splits(ro, rl)
+    ol, ll = B.merge_splits(d, op, lp)
+    rng = np.random.default_rng(3)
+    w_uv = W.round_to_storage(rng.standard_normal((w.n_h, w.d_h, w.d_c)) / np.sqrt(w.d_c), W.BF16)
+    oc, ll2, ol2 = B.merge_out_proj(d, op, lp, D._tensor(w_uv, W.BF16, "cuda"), want_o_lat=True)
+    torch.cuda.synchronize()
+    assert_close("o_lat (merge)", D.to_numpy_f64(ol), mo, w)
+    assert_close("lse (merge)", D.to_numpy_f64(ll), ml, w, lse=True)
+    assert torch.equal(ol, ol2) and torch.equal(ll, ll2)
+    assert_close("o_c (merge_out_proj)", D.to_numpy_f64(oc), O.out_proj(mo, W.to_f64(w_uv, W.BF16)), w)
 
 
 @pytest.mark.parametrize("n_h", [96, 160])
@@ -330,9 +348,15 @@ def test_outputs_stay_inside_their_buffers(torch, f16):
     B.decode_step(d, t["q_c"], t["q_r"], t["w_uk"], t["w_uv"], t["cache"], t["offsets"], w.batch,
                   w.q_per_seq, S, R, bufs=bufs)
     torch.cuda.synchronize()
+    empty = torch.isneginf(bufs["lse_part"])
+    assert empty.any()                    # sequence 0 (7 rows) leaves its later splits empty
     for k, buf in raw.items():
         assert torch.isnan(buf[:G].float()).all() and torch.isnan(buf[-G:].float()).all(), k
-        assert not torch.isnan(bufs[k].float()).any(), k
+        if k == "o_part":                 # an empty split's row is never written
+            assert torch.isnan(bufs[k][empty].float()).all(), k
+            assert not torch.isnan(bufs[k][~empty].float()).any(), k
+        else:
+            assert not torch.isnan(bufs[k].float()).any(), k
 
 
 # ----------------------------------------------------------------------------
