@@ -417,6 +417,11 @@ mla_decode_bf16_kernel(DecodeParams P) {
   // ---- finalize: o = acc / l, lse = ln(sum exp).  The outputs go through LDS in two
   // rounds of 256 dv so that every store writes whole rows (1 KiB per instruction).
   lds_barrier();                                 // every wave is done with the tiles
+  // Lane-derived values of the epilogue come from a fresh copy of the lane id: sharing them
+  // with the prologue's identical expressions would keep those live (spilled) across the loop.
+  int lane_e = (int)threadIdx.x & 63;
+  asm volatile("" : "+v"(lane_e));
+  const int row_base_e = 4 * (lane_e >> 5);
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
   constexpr int kRowB = out_row_bytes<OutT>();
@@ -429,15 +434,15 @@ mla_decode_bf16_kernel(DecodeParams P) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x16& a = acc[half * (kDvTiles / 2) + mt2];
-        const int dv = 32 * mt2 + 8 * g + row_base;          // within the round
-        put4((OutT*)(ost + (lane & 31) * kRowB) + dv, a[4 * g] * inv, a[4 * g + 1] * inv,
+        const int dv = 32 * mt2 + 8 * g + row_base_e;        // within the round
+        put4((OutT*)(ost + (lane_e & 31) * kRowB) + dv, a[4 * g] * inv, a[4 * g + 1] * inv,
              a[4 * g + 2] * inv, a[4 * g + 3] * inv);
       }
     // read back whole rows: a row is kOutHalf * sizeof(OutT) bytes = 64 or 32 lanes x 16 bytes
     constexpr int kLanesPerRow = kOutHalf * (int)sizeof(OutT) / 16;
     constexpr int kRowsPerStore = 64 / kLanesPerRow;
-    const int rr = lane / kLanesPerRow;
-    const int cc = lane % kLanesPerRow;
+    const int rr = lane_e / kLanesPerRow;
+    const int cc = lane_e % kLanesPerRow;
 #pragma unroll
     for (int h0 = 0; h0 < 32; h0 += kRowsPerStore) {
       const int h = h0 + rr;
@@ -445,7 +450,8 @@ mla_decode_bf16_kernel(DecodeParams P) {
       if (active) *(f32x4*)((char*)(o + (size_t)h * kDc + half * kOutHalf) + cc * 16) = v;
     }
   }
-  if (active && lane < 32) P.lse_part[out_row + head] = (m_ref + __log2f(l_tot)) * kLn2;
+  if (active && lane_e < 32)
+    P.lse_part[out_row + hg * kHeadsPerWg + wave * 32 + lane_e] = (m_ref + __log2f(l_tot)) * kLn2;
 }
 
 }  // namespace
