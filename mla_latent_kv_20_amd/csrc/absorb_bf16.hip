@@ -40,8 +40,16 @@ struct AbsorbParams {
 __global__ void __launch_bounds__(kThreads)
 absorb_q_bf16_kernel(AbsorbParams P) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int i = blockIdx.y;                       // head
-  const int cb = blockIdx.x * kAbsCols;           // first latent column of this block
+  // Workgroups are dealt round-robin over the 8 XCDs: workgroup L runs on XCD L % 8.  All
+  // column blocks of head i go to XCD i % 8, so the head's queries are fetched into one
+  // L2 once and shared by its blocks.
+  const int nblk = P.d_c / kAbsCols;
+  const int xcd = blockIdx.x & 7;
+  const int kq = blockIdx.x >> 3;
+  const int i = (kq / nblk) * 8 + xcd;            // head
+  const int cbi = kq % nblk;
+  const int cb = cbi * kAbsCols;                  // first latent column of this block
+  if (i >= P.n_h) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -49,7 +57,7 @@ absorb_q_bf16_kernel(AbsorbParams P) {
 
   // RoPE part: copied once per head, by the first column block, 16 bytes per thread with
   // every load of a thread in flight before its stores.
-  if (blockIdx.x == 0) {
+  if (cbi == 0) {
     const int cpr = P.d_r / 8;                    // 16-byte chunks per query row (d_r % 8 == 0)
     const int total = P.n_q * cpr;
     for (int e0 = 0; e0 < total; e0 += 4 * kThreads) {
@@ -241,7 +249,8 @@ hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, cons
                                 hipStream_t stream) {
   AbsorbParams P{q_c, q_r, w_uk, q_abs, n_q, n_h, d_h, d_c, d_r};
   const size_t smem = (size_t)d_h * kAbsPitch;
-  hipLaunchKernelGGL(absorb_q_bf16_kernel, dim3(d_c / kAbsCols, n_h), dim3(kThreads), smem, stream, P);
+  const int grid = 8 * ((n_h + 7) / 8) * (d_c / kAbsCols);
+  hipLaunchKernelGGL(absorb_q_bf16_kernel, dim3(grid), dim3(kThreads), smem, stream, P);
   return hipGetLastError();
 }
 
