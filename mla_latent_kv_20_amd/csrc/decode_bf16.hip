@@ -357,26 +357,23 @@ mla_decode_bf16_kernel(DecodeParams P) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    mfma_vgpr_drain(st);
-    mfma_vgpr_drain(st1);
+    mfma_vgpr_drain2(st, st1);
     st += st1;
 
     // ---- online softmax (log2 domain)
-    float mt = -INFINITY;
     const int rem = last_rel - t * kTile;        // rows of this tile with index <= rem count
-    if (rem >= kTile - 1) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        st[i] *= P.scale_log2;
-        mt = fmaxf(mt, st[i]);
-      }
-    } else {
+    if (rem < kTile - 1) {                       // partial tile: drop the rows past the end
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 8 * (i >> 2) + row_base + (i & 3);
-        st[i] = row <= rem ? st[i] * P.scale_log2 : -INFINITY;
-        mt = fmaxf(mt, st[i]);
+        if (row > rem) st[i] = -INFINITY;
       }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      st[i] *= P.scale_log2;                     // -inf stays -inf (the scale is positive)
+      mt = fmaxf(mt, st[i]);
     }
     mt = pair_max(mt);
     const bool grow = mt > m_ref + kRescaleSlack;

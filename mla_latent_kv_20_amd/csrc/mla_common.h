@@ -20,18 +20,18 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// bf16 <-> fp32, round to nearest even (finite inputs).
+// bf16 <-> fp32.  The narrowing rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ float bf16_to_f32(bf16_bits b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 __device__ __forceinline__ bf16_bits f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_bits)(u >> 16);
+  return __builtin_bit_cast(bf16_bits, (__bf16)f);
 }
-// Two floats -> packed bf16 pair (low half = a), hardware RNE conversion.
+// Two floats -> packed bf16 pair (low half = a), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 // D = A x B + C for 32x32x16 bf16 MFMA (gfx950). Lane l holds A[l%32][8(l/32)+j],
@@ -120,6 +120,9 @@ __device__ __forceinline__ void mfma_acc_vgpr(f32x16& acc, const bf16x8& a, cons
 // result on gfx950), with the accumulator as an operand so later reads stay behind it.
 __device__ __forceinline__ void mfma_vgpr_drain(f32x16& acc) {
   asm volatile("s_nop 11" : "+v"(acc));
+}
+__device__ __forceinline__ void mfma_vgpr_drain2(f32x16& acc0, f32x16& acc1) {
+  asm volatile("s_nop 11" : "+v"(acc0), "+v"(acc1));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
