@@ -71,10 +71,17 @@ struct DecodeParams {
 };
 
 // LDS layout of a tile: row r at r * 1152 bytes; logical chunk c of the row (16 bytes)
-// stored at physical chunk c ^ (r & 7), a swap inside the row's aligned groups of 8.
-// The 32 rows read at one logical chunk, and the 4 rows x 32 bytes of a transpose
-// read, then fall on different banks.  Because LDS slot p of the tile holds a chunk of
-// row p / 72, loading the tile is a contiguous copy with a small per-lane swap.
+// stored at physical chunk c ^ tile_swz(r), a swap inside the row's aligned groups of 8.
+// LDS has 64 banks of 4 bytes; a 16-byte read serves 16 lanes per pass and an 8-byte
+// read 32 lanes.  Consecutive rows start 128 bytes apart modulo the 256-byte bank
+// space, so rows of equal parity share a bank alignment.  The swap gives:
+//  - the K operand (16 rows at one logical chunk per pass) 16 distinct 16-byte slots:
+//    among the 8 rows of each parity the swaps are distinct;
+//  - the transposing V^T read (rows 4k..4k+3, 4 chunks of one half-group, per pass)
+//    distinct slots: rows 4k and 4k+2 (and 4k+1, 4k+3) swap into opposite halves.
+// Because LDS slot p of the tile holds a chunk of row p / 72, loading the tile is a
+// contiguous copy with a small per-lane swap.
+__host__ __device__ constexpr int tile_swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
 // Per-lane chunk swaps of the 9 loads: load i of lane l fills LDS slot
 // p = 64 * (9w + i) + l with global chunk p + delta_i, delta_i in [-7, 7] (4-bit fields).
@@ -86,7 +93,7 @@ __device__ __forceinline__ void make_deltas(int wave, int lane, uint32_t& d0, ui
     const int p = 64 * (kLoads * wave + i) + lane;
     const int r = p / kChunks;
     const int pc = p - r * kChunks;
-    const int delta = (pc ^ (r & 7)) - pc;
+    const int delta = (pc ^ tile_swz(r)) - pc;
     if (i < 8) d0 |= (uint32_t)(delta & 15) << (4 * i);
     else d1 |= (uint32_t)(delta & 15) << (4 * (i - 8));
   }
@@ -109,7 +116,7 @@ __device__ __forceinline__ void load_clamped(const char* tile_src, int64_t strid
   const int p = 64 * blk + lane;
   const int r = p / kChunks;
   const int pc = p - r * kChunks;
-  const int lc = pc ^ (r & 7);
+  const int lc = pc ^ tile_swz(r);
   const int rr = r < rmax ? r : rmax;
   global_to_lds16_sv(tile_src, (uint32_t)(rr * stride_bytes + lc * 16),
                      __builtin_amdgcn_readfirstlane(lds_addr(stage + blk * 1024)));
@@ -117,12 +124,13 @@ __device__ __forceinline__ void load_clamped(const char* tile_src, int64_t strid
 
 // V^T operand for O^T step u (u < 16: rows 0-15, else rows 16-31; dv tile m = u % 16):
 // lane l gets rows {0..3, 8..11} + 4(l/32) (+16) of dv column 32m + l%32.  `vb` holds the
-// lane's address (row v_row, dv tile pair parity) for even and odd m.
-__device__ __forceinline__ bf16x8 load_vt(const char* tile, const int* vb, int u) {
+// lane's addresses for dv tile pair parity m & 1: [0] rows 0..7, [1] rows 8..15 (their
+// swaps differ; rows 16..31 repeat the swaps of rows 0..15).
+__device__ __forceinline__ bf16x8 load_vt(const char* tile, const int (*vb)[2], int u) {
   const int m = u % kDvTiles;
-  const char* p = tile + vb[m & 1] + (16 * (u / kDvTiles)) * kRowBytes + 128 * (m >> 1);
-  const i16x4 lo4 = lds_read_tr16(p);
-  const i16x4 hi4 = lds_read_tr16(p + 8 * kRowBytes);
+  const int off = (16 * (u / kDvTiles)) * kRowBytes + 128 * (m >> 1);
+  const i16x4 lo4 = lds_read_tr16(tile + vb[m & 1][0] + off);
+  const i16x4 hi4 = lds_read_tr16(tile + vb[m & 1][1] + off);
   const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
   return __builtin_bit_cast(bf16x8, v8);
 }
@@ -210,7 +218,8 @@ mla_decode_bf16_kernel(DecodeParams P) {
 
   // ---- prologue.  Queries: the latent part (k-steps 0..31) lives in VGPRs as MFMA B
   // operands; the RoPE part (k-steps 32..35) of all 128 heads sits in LDS after the tile
-  // stages, 128 bytes per head with its 16-byte chunks swapped by (head & 7), and is read
+  // stages, 128 bytes per head with its 16-byte chunks swapped by ((head >> 1) & 7), so
+  // that 16 consecutive heads hit distinct banks, and is read
   // per tile.  The latent part comes in two halves of 256 columns through an LDS staging
   // area with direct-to-LDS loads, each instruction reading two contiguous 512-byte
   // half-rows (a register load of the MFMA layout would touch 32 rows per instruction).
@@ -269,7 +278,7 @@ mla_decode_bf16_kernel(DecodeParams P) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int h = (threadIdx.x >> 3) + 32 * g;   // head within the group
-    *(bf16x8*)(qrope + h * 128 + 16 * (hc ^ (h & 7))) = rope_v[g];
+    *(bf16x8*)(qrope + h * 128 + 16 * (hc ^ ((h >> 1) & 7))) = rope_v[g];
   }
   // All queries (and the first tile) resident.  A builtin wait, so the compiler knows
   // the query loads have landed and places no vmcnt waits for them inside the tile loop,
@@ -288,13 +297,17 @@ mla_decode_bf16_kernel(DecodeParams P) {
   const int a_row = lane & 31;                 // K operand: tile row of this lane
   int kb[4];                                   // K operand address for k-steps 4q + j
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) kb[jj] = a_row * kRowBytes + 16 * ((2 * jj + (lane >> 5)) ^ (a_row & 7));
+  for (int jj = 0; jj < 4; ++jj) kb[jj] = a_row * kRowBytes + 16 * ((2 * jj + (lane >> 5)) ^ tile_swz(a_row));
   const int v_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int v_cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  int vb[2];
+  int vb[2][2];
 #pragma unroll
   for (int pp = 0; pp < 2; ++pp)
-    vb[pp] = v_row * kRowBytes + 16 * ((4 * pp + v_cl) ^ (v_row & 7)) + 8 * (lane & 1);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r = v_row + 8 * hh;
+      vb[pp][hh] = r * kRowBytes + 16 * ((4 * pp + v_cl) ^ tile_swz(r)) + 8 * (lane & 1);
+    }
   const int row_base = 4 * (lane >> 5);        // S^T rows held: 8(i/4) + row_base + i%4
 
   for (int t = 0; t < ntiles; ++t) {
@@ -350,7 +363,7 @@ mla_decode_bf16_kernel(DecodeParams P) {
       } else {                                   // RoPE k-step: chunk 2(ks-32) + l/32 of head l%32
         const int hl = wave * 32 + (lane & 31);
         const int c = 2 * (ks - kKReg) + (lane >> 5);
-        qop = *(const bf16x8*)(qrope + hl * 128 + 16 * (c ^ (hl & 7)));
+        qop = *(const bf16x8*)(qrope + hl * 128 + 16 * (c ^ ((hl >> 1) & 7)));
       }
       if (ks & 1) mfma_acc_vgpr(st1, ka[ks], qop);
       else mfma_acc_vgpr(st, ka[ks], qop);
