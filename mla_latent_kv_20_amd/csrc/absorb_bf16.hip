@@ -28,6 +28,7 @@ constexpr int kWaves = 4;
 // ---------------------------------------------------------------------------
 constexpr int kAbsCols = 128;
 constexpr int kAbsPitch = kAbsCols * 2 + 32;   // 288 B: 4 rows x 32 B of a transpose read hit distinct banks
+constexpr int kAbsOutPitch = kAbsCols * 2 + 16; // output staging row (bf16): rows r and r+4 of a 2-byte write on distinct banks
 
 struct AbsorbParams {
   const bf16_bits* q_c;   // [n_q, n_h, d_h]
@@ -55,27 +56,7 @@ absorb_q_bf16_kernel(AbsorbParams P) {
   const int lane = tid & 63;
   const int d_qk = P.d_c + P.d_r;
 
-  // RoPE part: copied once per head, by the first column block, 16 bytes per thread with
-  // every load of a thread in flight before its stores.
-  if (cbi == 0) {
-    const int cpr = P.d_r / 8;                    // 16-byte chunks per query row (d_r % 8 == 0)
-    const int total = P.n_q * cpr;
-    for (int e0 = 0; e0 < total; e0 += 4 * kThreads) {
-      bf16x8 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u * kThreads + tid;
-        if (e < total)
-          v[u] = *(const bf16x8*)(P.q_r + ((size_t)(e / cpr) * P.n_h + i) * P.d_r + (e % cpr) * 8);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u * kThreads + tid;
-        if (e < total)
-          *(bf16x8*)(P.q_abs + ((size_t)(e / cpr) * P.n_h + i) * d_qk + P.d_c + (e % cpr) * 8) = v[u];
-      }
-    }
-  }
+  char* ostage = smem + P.d_h * kAbsPitch;      // [32][kAbsOutPitch] output staging
 
   // A operands of the first query block, loaded before the weight slice so that the two
   // memory latencies overlap.
@@ -146,14 +127,49 @@ absorb_q_bf16_kernel(AbsorbParams P) {
         acc = mfma32x32x16(a, wb[s], acc);
       }
     }
-    // D[m][n]: lane l, reg r -> row 8(r/4) + 4(l/32) + r%4, column l%32
-    const int col = cb + 32 * wave + (lane & 31);
+    // D[m][n]: lane l, reg r -> row 8(r/4) + 4(l/32) + r%4, column l%32.  The 32 x 128
+    // block goes through LDS so that every global store writes 16 contiguous bytes.
+    if (mb > 0) __syncthreads();                  // the previous block's stores have read ostage
+    const int col = 32 * wave + (lane & 31);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int mm = mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (mm < P.n_q) P.q_abs[((size_t)mm * P.n_h + i) * d_qk + col] = f32_to_bf16(acc[r]);
+      const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      *(bf16_bits*)(ostage + row * kAbsOutPitch + col * 2) = f32_to_bf16(acc[r]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 32 * (kAbsCols / 8) / kThreads; ++u) {
+      const int e = u * kThreads + tid;
+      const int row = e / (kAbsCols / 8), c8 = e % (kAbsCols / 8);
+      if (mb + row < P.n_q)
+        *(bf16x8*)(P.q_abs + ((size_t)(mb + row) * P.n_h + i) * d_qk + cb + 8 * c8) =
+            *(const bf16x8*)(ostage + row * kAbsOutPitch + 16 * c8);
     }
   }
+
+  // RoPE part: copied once per head, by the first column block, 16 bytes per thread with
+  // every load of a thread in flight before its stores.  It comes last, so that its
+  // memory latency does not delay the weight loads above.
+  if (cbi == 0) {
+    const int cpr = P.d_r / 8;                    // 16-byte chunks per query row (d_r % 8 == 0)
+    const int total = P.n_q * cpr;
+    for (int e0 = 0; e0 < total; e0 += 4 * kThreads) {
+      bf16x8 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kThreads + tid;
+        if (e < total)
+          v[u] = *(const bf16x8*)(P.q_r + ((size_t)(e / cpr) * P.n_h + i) * P.d_r + (e % cpr) * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kThreads + tid;
+        if (e < total)
+          *(bf16x8*)(P.q_abs + ((size_t)(e / cpr) * P.n_h + i) * d_qk + P.d_c + (e % cpr) * 8) = v[u];
+      }
+    }
+  }
+
 }
 
 // ---------------------------------------------------------------------------
@@ -248,7 +264,7 @@ hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, cons
                                 bf16_bits* q_abs, int n_q, int n_h, int d_h, int d_c, int d_r,
                                 hipStream_t stream) {
   AbsorbParams P{q_c, q_r, w_uk, q_abs, n_q, n_h, d_h, d_c, d_r};
-  const size_t smem = (size_t)d_h * kAbsPitch;
+  const size_t smem = (size_t)d_h * kAbsPitch + 32 * kAbsOutPitch;
   const int grid = 8 * ((n_h + 7) / 8) * (d_c / kAbsCols);
   hipLaunchKernelGGL(absorb_q_bf16_kernel, dim3(grid), dim3(kThreads), smem, stream, P);
   return hipGetLastError();
