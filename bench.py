@@ -241,33 +241,56 @@ def main():
     cached = w.cached_rows()
     value = cached / (ms_per_step * 1e-3)
 
-    # Each kernel alone, launched K times back to back over the layer copies, between one
-    # pair of HIP events on its stream: the mean launch duration, dispatch gaps included.
-    # The decode's is the roofline's duration.
+    # Each kernel alone: launches over the layer copies captured as one HIP graph and replayed,
+    # so the mean is GPU time per launch (dispatch gaps included, no host launch cost).  The
+    # weight-only kernels cycle over enough weight copies to exceed twice the MALL, as their
+    # weights would come from HBM in a model's step.  The decode's mean is the roofline's
+    # duration.
+    w_bytes = w.n_h * w.d_h * w.d_c * esz
+    wcopies = max(copies, math.ceil(2 * MALL_BYTES / w_bytes))
+    w_uk_set = [L["w_uk"] for L in layers] + [base["w_uk"].clone() for _ in range(wcopies - copies)]
+    w_uv_set = [L["w_uv"] for L in layers] + [base["w_uv"].clone() for _ in range(wcopies - copies)]
     calls = {
-        "absorb_q": lambda L: B.absorb_q(d, L["q_c"], L["q_r"], L["w_uk"], bufs["q_abs"]),
-        "decode": lambda L: B.decode(d, bufs["q_abs"], L["cache"][:, :w.d_c], L["cache"][:, w.d_c:],
-                                     L["offsets"], w.batch, w.q_per_seq, S, R, bufs["o_part"],
-                                     bufs["lse_part"]),
-        "merge": (lambda L: B.merge_splits(d, bufs["o_part"], bufs["lse_part"], bufs["o_lat"], bufs["lse"]))
+        "absorb_q": (wcopies, lambda j: B.absorb_q(d, base["q_c"], base["q_r"], w_uk_set[j], bufs["q_abs"])),
+        "decode": (copies, lambda j: B.decode(d, bufs["q_abs"], layers[j]["cache"][:, :w.d_c],
+                                              layers[j]["cache"][:, w.d_c:], layers[j]["offsets"], w.batch,
+                                              w.q_per_seq, S, R, bufs["o_part"], bufs["lse_part"])),
+        "merge": (1, lambda j: B.merge_splits(d, bufs["o_part"], bufs["lse_part"], bufs["o_lat"], bufs["lse"]))
         if (S > 1 or part != B.MLA_F32) else None,
-        "out_proj": lambda L: B.out_proj(d, bufs["o_lat"], L["w_uv"], bufs["o_c"]),
-        "merge_out_proj": (lambda L: B.merge_out_proj(d, bufs["o_part"], bufs["lse_part"], L["w_uv"],
-                                                      bufs["o_c"], bufs["lse"], None))
+        "out_proj": (wcopies, lambda j: B.out_proj(d, bufs["o_lat"], w_uv_set[j], bufs["o_c"])),
+        "merge_out_proj": (wcopies, lambda j: B.merge_out_proj(d, bufs["o_part"], bufs["lse_part"], w_uv_set[j],
+                                                                bufs["o_c"], bufs["lse"], None))
         if d.dtype == B.MLA_BF16 else None,
     }
     per = {}
-    for name, fn in calls.items():
-        if fn is None:
+    for name, item in calls.items():
+        if item is None:
             continue
+        n, fn = item
+        for j in range(n):
+            fn(j)
+        torch.cuda.synchronize()
+        reps = max(1, K // n)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if args.no_graph:                  # eager launches (counter runs): host cost may show
+            e0.record()
+            for _ in range(reps):
+                for j in range(n):
+                    fn(j)
+            e1.record()
+        else:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for j in range(n):
+                    fn(j)
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
         torch.cuda.synchronize()
-        e0.record()
-        for i in range(K):
-            fn(layers[i % copies])
-        e1.record()
-        torch.cuda.synchronize()
-        per[name] = e0.elapsed_time(e1) / K
+        per[name] = e0.elapsed_time(e1) / (reps * n)
 
     dec_ms = per["decode"]
     dec_bytes = cached * ROW_BYTES + (w.rows - cached) * ROW_BYTES
