@@ -46,7 +46,7 @@ constexpr int kKSteps = kDqk / 16;       // 36 MFMA k-steps for the scores
 constexpr int kKReg = kDc / 16;          // 32 k-steps with the query operand in VGPRs (latent part)
 constexpr int kQRopeBytes = kHeadsPerWg * kDr * 2;            // RoPE part of the queries, in LDS
 constexpr int kQStageWave = 32 * 512;    // query staging per wave: 32 heads x 256 columns bf16
-constexpr int kQStageLoads = 2 * kQStageWave / 1024;          // 1 KiB loads per wave, both halves
+constexpr int kQStageLoads = 2 * kQStageWave / 1024;          // 1 KiB loads per wave, both halves' worth
 constexpr int kDvTiles = kDc / 32;       // 16 output tiles of 32 dv
 constexpr float kRescaleSlack = 8.0f;    // log2 units
 constexpr int kKAhead = 6;               // K operand reads in flight
@@ -219,12 +219,13 @@ mla_decode_bf16_kernel(DecodeParams P) {
   // ---- prologue.  Queries: the latent part (k-steps 0..31) lives in VGPRs as MFMA B
   // operands; the RoPE part (k-steps 32..35) of all 128 heads sits in LDS after the tile
   // stages, 128 bytes per head with its 16-byte chunks swapped by ((head >> 1) & 7), so
-  // that 16 consecutive heads hit distinct banks, and is read
-  // per tile.  The latent part comes in two halves of 256 columns through an LDS staging
+  // that 16 consecutive heads hit distinct banks, and is read per tile.  The latent part
+  // comes in two halves of 256 columns, issued together: half 0 through an LDS staging
   // area with direct-to-LDS loads, each instruction reading two contiguous 512-byte
-  // half-rows (a register load of the MFMA layout would touch 32 rows per instruction).
-  // In the staging area, wave w owns heads 32w .. 32w+31 at 512 bytes each, chunk c of
-  // head h stored at chunk c ^ (h & 15).
+  // half-rows, and half 1 straight into registers in the MFMA layout (32 rows per
+  // instruction; the staging area has room for one half only).  In the staging area,
+  // wave w owns heads 32w .. 32w+31 at 512 bytes each, chunk c of head h stored at chunk
+  // c ^ (h & 15).
   bf16x8 qb[kKReg];
   char* qrope = smem + kStages * kTileBytes;
   char* qstage = qrope + kQRopeBytes + wave * kQStageWave;
@@ -237,7 +238,7 @@ mla_decode_bf16_kernel(DecodeParams P) {
     rope_v[g] = *(const bf16x8*)(P.q_abs + ((size_t)n * P.n_h + hq) * kDqk + kDc + hc * 8);
   }
   const char* qbase = (const char*)(P.q_abs + ((size_t)n * P.n_h + hg * kHeadsPerWg) * kDqk);
-  uint32_t qoff[kQStageLoads / 2];               // per-lane source offsets, half 0 (half 1: +512)
+  uint32_t qoff[kQStageLoads / 2];               // per-lane source offsets of half 0
 #pragma unroll
   for (int j = 0; j < kQStageLoads / 2; ++j) {
     const int hl = 2 * j + (lane >> 5);          // head of the wave filled by this lane
@@ -263,18 +264,21 @@ mla_decode_bf16_kernel(DecodeParams P) {
       for (int i = 0; i < kLoads; ++i) load_clamped(src, stride_bytes, rmax, stage, wave, i, lane);
     }
   }
+  // Half 1 goes straight into its B-operand registers (lane l: head l%32, 16 bytes per
+  // k-step), so that its memory latency overlaps that of half 0 instead of following it.
+  {
+    int hq = wave * 32 + (lane & 31);
+    hq = hg * kHeadsPerWg + hq < P.n_h ? hq : P.n_h - 1 - hg * kHeadsPerWg;
+    const bf16_bits* qh = (const bf16_bits*)qbase + (size_t)hq * kDqk + kDc / 2 + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < kKReg / 2; ++ks) qb[kKReg / 2 + ks] = *(const bf16x8*)(qh + 16 * ks);
+  }
   const char* qrd = qstage + (lane & 31) * 512;  // this lane's head row in the staging area
   const int qx = lane & 15;                      // its chunk swap (head & 15)
-  wait_vmcnt<kLoads>();                          // half 0 (and the RoPE loads) landed
+  wait_vmcnt<kLoads + kKReg / 2>();              // half 0 (and the RoPE loads) landed
 #pragma unroll
   for (int ks = 0; ks < kKReg / 2; ++ks) qb[ks] = *(const bf16x8*)(qrd + 16 * ((2 * ks + (lane >> 5)) ^ qx));
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the area is refilled
-#pragma unroll
-  for (int j = 0; j < kQStageLoads / 2; ++j) global_to_lds16_sv(qbase, qoff[j] + 512, qstage_lds + j * 1024);
   wait_vmcnt<0>();                               // half 1 and the first tile landed
-#pragma unroll
-  for (int ks = 0; ks < kKReg / 2; ++ks)
-    qb[kKReg / 2 + ks] = *(const bf16x8*)(qrd + 16 * ((2 * ks + (lane >> 5)) ^ qx));
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int h = (threadIdx.x >> 3) + 32 * g;   // head within the group
