@@ -43,8 +43,7 @@ constexpr int kHeadsPerWg = kWaves * 32;
 constexpr int kLoads = kTile * kChunks / kThreads;            // 9 loads of 1 KiB per wave per tile
 constexpr int kStages = 2;
 constexpr int kKSteps = kDqk / 16;       // 36 MFMA k-steps for the scores
-constexpr int kKReg = kDc / 16;          // 32 k-steps with the query operand in VGPRs (latent part)
-constexpr int kQRopeBytes = kHeadsPerWg * kDr * 2;            // RoPE part of the queries, in LDS
+constexpr int kKReg = kDc / 16;          // 32 k-steps of the latent part (then 4 of the RoPE part)
 constexpr int kQStageWave = 32 * 512;    // query staging per wave: 32 heads x 256 columns bf16
 constexpr int kQStageLoads = 2 * kQStageWave / 1024;          // 1 KiB loads per wave, both halves' worth
 constexpr int kDvTiles = kDc / 32;       // 16 output tiles of 32 dv
@@ -216,27 +215,15 @@ mla_decode_bf16_kernel(DecodeParams P) {
   make_deltas(wave, lane, d0, d1);
   const uint32_t lane16 = (uint32_t)lane * 16;
 
-  // ---- prologue.  Queries: the latent part (k-steps 0..31) lives in VGPRs as MFMA B
-  // operands; the RoPE part (k-steps 32..35) of all 128 heads sits in LDS after the tile
-  // stages, 128 bytes per head with its 16-byte chunks swapped by ((head >> 1) & 7), so
-  // that 16 consecutive heads hit distinct banks, and is read per tile.  The latent part
-  // comes in two halves of 256 columns, issued together: half 0 through an LDS staging
-  // area with direct-to-LDS loads, each instruction reading two contiguous 512-byte
-  // half-rows, and half 1 straight into registers in the MFMA layout (32 rows per
-  // instruction; the staging area has room for one half only).  In the staging area,
-  // wave w owns heads 32w .. 32w+31 at 512 bytes each, chunk c of head h stored at chunk
-  // c ^ (h & 15).
-  bf16x8 qb[kKReg];
-  char* qrope = smem + kStages * kTileBytes;
-  char* qstage = qrope + kQRopeBytes + wave * kQStageWave;
-  const int hc = threadIdx.x & 7;
-  bf16x8 rope_v[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {                  // RoPE part: chunk t%8 of heads t/8 + 32g
-    int hq = hg * kHeadsPerWg + (threadIdx.x >> 3) + 32 * g;
-    hq = hq < P.n_h ? hq : P.n_h - 1;
-    rope_v[g] = *(const bf16x8*)(P.q_abs + ((size_t)n * P.n_h + hq) * kDqk + kDc + hc * 8);
-  }
+  // ---- prologue.  Queries: all 36 k-steps (latent and RoPE parts) live in VGPRs as MFMA
+  // B operands for the whole split.  The latent part comes in two halves of 256 columns,
+  // issued together: half 0 through an LDS staging area with direct-to-LDS loads, each
+  // instruction reading two contiguous 512-byte half-rows, and half 1 with the 64 RoPE
+  // columns straight into registers in the MFMA layout (32 rows per instruction; the
+  // staging area has room for one half only).  In the staging area, wave w owns heads
+  // 32w .. 32w+31 at 512 bytes each, chunk c of head h stored at chunk c ^ (h & 15).
+  bf16x8 qb[kKSteps];
+  char* qstage = smem + kStages * kTileBytes + wave * kQStageWave;
   const char* qbase = (const char*)(P.q_abs + ((size_t)n * P.n_h + hg * kHeadsPerWg) * kDqk);
   uint32_t qoff[kQStageLoads / 2];               // per-lane source offsets of half 0
 #pragma unroll
@@ -264,26 +251,23 @@ mla_decode_bf16_kernel(DecodeParams P) {
       for (int i = 0; i < kLoads; ++i) load_clamped(src, stride_bytes, rmax, stage, wave, i, lane);
     }
   }
-  // Half 1 goes straight into its B-operand registers (lane l: head l%32, 16 bytes per
-  // k-step), so that its memory latency overlaps that of half 0 instead of following it.
+  // Half 1 and the RoPE part go straight into their B-operand registers (lane l: head
+  // l%32, 16 bytes per k-step), so that their memory latency overlaps that of half 0.
   {
     int hq = wave * 32 + (lane & 31);
     hq = hg * kHeadsPerWg + hq < P.n_h ? hq : P.n_h - 1 - hg * kHeadsPerWg;
     const bf16_bits* qh = (const bf16_bits*)qbase + (size_t)hq * kDqk + kDc / 2 + 8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < kKReg / 2; ++ks) qb[kKReg / 2 + ks] = *(const bf16x8*)(qh + 16 * ks);
+#pragma unroll
+    for (int ks = 0; ks < kKSteps - kKReg; ++ks) qb[kKReg + ks] = *(const bf16x8*)(qh + kDc / 2 + 16 * ks);
   }
   const char* qrd = qstage + (lane & 31) * 512;  // this lane's head row in the staging area
   const int qx = lane & 15;                      // its chunk swap (head & 15)
-  wait_vmcnt<kLoads + kKReg / 2>();              // half 0 (and the RoPE loads) landed
+  wait_vmcnt<kLoads + kKReg / 2 + (kKSteps - kKReg)>();   // half 0 landed
 #pragma unroll
   for (int ks = 0; ks < kKReg / 2; ++ks) qb[ks] = *(const bf16x8*)(qrd + 16 * ((2 * ks + (lane >> 5)) ^ qx));
   wait_vmcnt<0>();                               // half 1 and the first tile landed
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int h = (threadIdx.x >> 3) + 32 * g;   // head within the group
-    *(bf16x8*)(qrope + h * 128 + 16 * (hc ^ ((h >> 1) & 7))) = rope_v[g];
-  }
   // All queries (and the first tile) resident.  A builtin wait, so the compiler knows
   // the query loads have landed and places no vmcnt waits for them inside the tile loop,
   // where they would also stall on in-flight tile prefetches.
@@ -361,14 +345,7 @@ mla_decode_bf16_kernel(DecodeParams P) {
         const int kn = ks + kKAhead;
         ka[kn] = *(const bf16x8*)(tile + kb[kn & 3] + 128 * (kn >> 2));
       }
-      bf16x8 qop;
-      if (ks < kKReg) {
-        qop = qb[ks];
-      } else {                                   // RoPE k-step: chunk 2(ks-32) + l/32 of head l%32
-        const int hl = wave * 32 + (lane & 31);
-        const int c = 2 * (ks - kKReg) + (lane >> 5);
-        qop = *(const bf16x8*)(qrope + hl * 128 + 16 * (c ^ ((hl >> 1) & 7)));
-      }
+      const bf16x8 qop = qb[ks];
       if (ks & 1) mfma_acc_vgpr(st1, ka[ks], qop);
       else mfma_acc_vgpr(st, ka[ks], qop);
       __builtin_amdgcn_sched_barrier(0);
@@ -494,7 +471,7 @@ hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* rows, int
   P.scale_log2 = (float)((double)scale * 1.4426950408889634);
   const long long grid = (long long)P.streams_per_xcd * 8 * P.group_size;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  size_t smem = (size_t)kStages * kTileBytes + kQRopeBytes + (size_t)kWaves * kQStageWave;
+  size_t smem = (size_t)kStages * kTileBytes + (size_t)kWaves * kQStageWave;
   const size_t out_stage = (size_t)kWaves * 32 * (f16_partials ? out_row_bytes<_Float16>() : out_row_bytes<float>());
   smem = smem > out_stage ? smem : out_stage;
   // Dynamic LDS above 64 KiB must be allowed once per kernel (thread-safe static init).
