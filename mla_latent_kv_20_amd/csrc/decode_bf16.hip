@@ -66,6 +66,8 @@ struct DecodeParams {
   int64_t stride;
   int n_q, n_h, q_per_seq, num_splits, split_rows;
   int head_groups, group_size, streams, streams_per_xcd;
+  int batch;
+  int seqs_per_xcd;             // > 0: sequences dealt to XCDs by length (see the work item)
   float scale_log2;             // softmax scale * log2(e)
 };
 
@@ -158,21 +160,70 @@ __global__ void __launch_bounds__(kThreads, 1)
 mla_decode_bf16_kernel(DecodeParams P) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-  // ---- work item.  Workgroups are dealt round-robin over the 8 XCDs; XCD x takes the
-  // contiguous stream range [x * streams_per_xcd, ...), so the splits of one sequence
-  // share an XCD's L2 (one fetch of the queries), and the members of a stream (query
-  // tokens, head groups: same rows) run side by side on it.
+  // ---- work item.  Workgroups are dealt round-robin over the 8 XCDs (workgroup L runs on
+  // XCD L % 8), and the members of a stream (query tokens, head groups: same rows) run
+  // side by side on one XCD, as do the splits of one sequence (one L2 fetch of its
+  // queries).
+  //  - Few sequences: XCD x takes the contiguous stream range [x * streams_per_xcd, ...).
+  //  - seqs_per_xcd > 0 (16 or more sequences): every workgroup ranks the sequences by
+  //    length (longest first, ties by index) and XCD x takes ranks x, 15-x, 16+x, 31-x, ...
+  //    (snake order), longest first.  Every XCD then gets the same number of sequences
+  //    and nearly the same number of tiles, however ragged the lengths.  Only non-empty
+  //    splits are enumerated (the split-0 workgroup marks the empty ones): the dispatcher
+  //    deals an XCD's workgroups to its shader engines in a fixed rotation, so empty
+  //    workgroups interleaved with real ones would load the engines unevenly.
   const int L = blockIdx.x;
   const int xcd = L & 7;
   const int k = L >> 3;
   const int member = k % P.group_size;
   const int j = k / P.group_size;
-  const int stream = xcd * P.streams_per_xcd + j;
-  if (j >= P.streams_per_xcd || stream >= P.streams) return;
+  if (j >= P.streams_per_xcd) return;
+  int b, s;
+  int used_splits = P.num_splits;                  // splits of sequence b that hold rows
+  if (P.seqs_per_xcd > 0) {
+    int* lens = (int*)smem;                        // [batch]; LDS is free until the first loads
+    int* by_rank = lens + P.batch;                 // [batch]: sequence of each rank
+    for (int i = threadIdx.x; i < P.batch; i += kThreads) lens[i] = (int)(P.offsets[i + 1] - P.offsets[i]);
+    __syncthreads();
+    for (int c = threadIdx.x; c < P.batch; c += kThreads) {
+      const int lc = lens[c];
+      int rank = 0;
+      for (int i = 0; i < P.batch; ++i) {
+        const int li = lens[i];
+        rank += (li > lc || (li == lc && i < c)) ? 1 : 0;
+      }
+      by_rank[rank] = c;                           // the ranks are a permutation of 0..batch-1
+    }
+    __syncthreads();
+    // this XCD's sequences in rank order, each with its non-empty splits: item j
+    int base = 0;
+    b = -1;
+    s = 0;
+    for (int m = 0; m < P.seqs_per_xcd; ++m) {
+      const int p = 8 * m + ((m & 1) ? 7 - xcd : xcd);
+      if (p >= P.batch) break;                     // p grows with m
+      const int bm = by_rank[p];
+      const int len = lens[bm];
+      int ns = P.split_rows > 0 ? (len + P.split_rows - 1) / P.split_rows : P.num_splits;
+      ns = ns < 1 ? 1 : (ns > P.num_splits ? P.num_splits : ns);
+      if (j < base + ns) {
+        b = bm;
+        s = j - base;
+        used_splits = ns;
+        break;
+      }
+      base += ns;
+    }
+    __syncthreads();                               // every wave has read LDS before it is reused
+    if (b < 0) return;                             // past this XCD's items (workgroup-uniform)
+  } else {
+    const int stream = xcd * P.streams_per_xcd + j;
+    if (stream >= P.streams) return;
+    b = stream / P.num_splits;
+    s = stream - b * P.num_splits;
+  }
   const int hg = member % P.head_groups;
   const int r = member / P.head_groups;
-  const int b = stream / P.num_splits;
-  const int s = stream - b * P.num_splits;
   const int n = b * P.q_per_seq + r;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -199,6 +250,9 @@ mla_decode_bf16_kernel(DecodeParams P) {
   if (lo < 0) lo = 0;
 
   const size_t out_row = ((size_t)s * P.n_q + n) * P.n_h;
+  if (s == 0 && used_splits < P.num_splits && active && lane < 32) {   // splits with no workgroup
+    for (int se = used_splits; se < P.num_splits; ++se) P.lse_part[((size_t)se * P.n_q + n) * P.n_h + head] = -INFINITY;
+  }
   if (hi <= lo) {                      // empty split: lse = -inf marks it; o_part is not written
     if (active && lane < 32) P.lse_part[out_row + head] = -INFINITY;
     return;
@@ -467,13 +521,21 @@ hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* rows, int
   P.head_groups = (n_h + kHeadsPerWg - 1) / kHeadsPerWg;
   P.group_size = P.head_groups * q_per_seq;
   P.streams = batch * num_splits;
-  P.streams_per_xcd = (P.streams + 7) / 8;
+  P.batch = batch;
+  // Sequences are dealt to XCDs by length once there are two per XCD; fewer sequences
+  // keep contiguous stream ranges, so that a long sequence's splits spread over XCDs.
+  P.seqs_per_xcd = batch >= 16 ? (batch + 7) / 8 : 0;
+  P.streams_per_xcd = P.seqs_per_xcd > 0 ? P.seqs_per_xcd * num_splits : (P.streams + 7) / 8;
   P.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  const long long grid = (long long)P.streams_per_xcd * 8 * P.group_size;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   size_t smem = (size_t)kStages * kTileBytes + (size_t)kWaves * kQStageWave;
   const size_t out_stage = (size_t)kWaves * 32 * (f16_partials ? out_row_bytes<_Float16>() : out_row_bytes<float>());
   smem = smem > out_stage ? smem : out_stage;
+  if (P.seqs_per_xcd > 0 && (size_t)(2 * batch) * sizeof(int) > smem) {   // lengths and ranks do not fit in LDS
+    P.seqs_per_xcd = 0;
+    P.streams_per_xcd = (P.streams + 7) / 8;
+  }
+  const long long grid = (long long)P.streams_per_xcd * 8 * P.group_size;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // Dynamic LDS above 64 KiB must be allowed once per kernel (thread-safe static init).
   static const hipError_t attr32 = hipFuncSetAttribute(
       (const void*)mla_decode_bf16_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);

@@ -314,6 +314,10 @@ CONFIGS: Dict[str, tuple] = {
     "dsv2_small": (
         "DeepSeek-V2 dims, B=3, T=(1, 77, 1000), bf16",
         dict(**DSV2, dtype=BF16, lengths=[1, 77, 1000], num_splits=3, split_rows=256)),
+    "dsv2_ragged_small": (
+        "DeepSeek-V2 dims, B=19, T~U{1..400}, queries x3, bf16 (sequences dealt to XCDs by length)",
+        dict(**DSV2, dtype=BF16, ragged_range=(1, 400), ragged_batch=19, q_mult=3.0,
+             num_splits=4, split_rows=96)),
     "dsv2_small_mtp": (
         "DeepSeek-V2 dims, B=2, T=(3, 250) + 4 new rows, 4 queries/seq, bf16",
         dict(**DSV2, dtype=BF16, lengths=[3, 250], q_per_seq=4, appended_rows=True,

@@ -82,9 +82,10 @@ def oracle_args(w):
                 q_r=w.f64("q_r"), w_uk=w.f64("w_uk"), w_uv=w.f64("w_uv"), q_per_seq=w.q_per_seq)
 
 
-SMALL = ["tiny_f32", "toy_p3", "dsv2_small", "dsv2_small_mtp"]
+SMALL = ["tiny_f32", "toy_p3", "dsv2_small", "dsv2_small_mtp", "dsv2_ragged_small"]
 PLANS = {"tiny_f32": [(1, 0), (3, 20)], "toy_p3": [(1, 0), (2, 4)],
-         "dsv2_small": [(1, 0), (3, 256), (5, 33)], "dsv2_small_mtp": [(1, 0), (2, 128), (9, 32)]}
+         "dsv2_small": [(1, 0), (3, 256), (5, 33)], "dsv2_small_mtp": [(1, 0), (2, 128), (9, 32)],
+         "dsv2_ragged_small": [(1, 0), (4, 96), (7, 40)]}
 
 
 # ----------------------------------------------------------------------------
