@@ -181,16 +181,22 @@ mla_decode_bf16_kernel(DecodeParams P) {
   int b, s;
   int used_splits = P.num_splits;                  // splits of sequence b that hold rows
   if (P.seqs_per_xcd > 0) {
-    int* lens = (int*)smem;                        // [batch]; LDS is free until the first loads
-    int* by_rank = lens + P.batch;                 // [batch]: sequence of each rank
-    for (int i = threadIdx.x; i < P.batch; i += kThreads) lens[i] = (int)(P.offsets[i + 1] - P.offsets[i]);
+    // lengths in LDS (free until the first loads), padded to a multiple of 4 with -1,
+    // which ranks below every length
+    const int bpad = (P.batch + 3) & ~3;
+    int* lens = (int*)smem;                        // [bpad]
+    int* by_rank = lens + bpad;                    // [batch]: sequence of each rank
+    for (int i = threadIdx.x; i < bpad; i += kThreads)
+      lens[i] = i < P.batch ? (int)(P.offsets[i + 1] - P.offsets[i]) : -1;
     __syncthreads();
     for (int c = threadIdx.x; c < P.batch; c += kThreads) {
       const int lc = lens[c];
       int rank = 0;
-      for (int i = 0; i < P.batch; ++i) {
-        const int li = lens[i];
-        rank += (li > lc || (li == lc && i < c)) ? 1 : 0;
+      for (int i = 0; i < bpad; i += 4) {
+        typedef int i32x4 __attribute__((ext_vector_type(4)));
+        const i32x4 v = *(const i32x4*)(lens + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rank += (v[e] > lc || (v[e] == lc && i + e < c)) ? 1 : 0;
       }
       by_rank[rank] = c;                           // the ranks are a permutation of 0..batch-1
     }
@@ -530,7 +536,7 @@ hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* rows, int
   size_t smem = (size_t)kStages * kTileBytes + (size_t)kWaves * kQStageWave;
   const size_t out_stage = (size_t)kWaves * 32 * (f16_partials ? out_row_bytes<_Float16>() : out_row_bytes<float>());
   smem = smem > out_stage ? smem : out_stage;
-  if (P.seqs_per_xcd > 0 && (size_t)(2 * batch) * sizeof(int) > smem) {   // lengths and ranks do not fit in LDS
+  if (P.seqs_per_xcd > 0 && (size_t)(2 * (batch + 3)) * sizeof(int) > smem) {   // lengths and ranks do not fit in LDS
     P.seqs_per_xcd = 0;
     P.streams_per_xcd = (P.streams + 7) / 8;
   }
