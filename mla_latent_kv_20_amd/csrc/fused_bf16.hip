@@ -94,49 +94,70 @@ __device__ __forceinline__ void merge_one(const PartT* o_part, const float* lse_
     for (int e = 0; e < 8; ++e) o[e] = acc[e] * inv_z;
     return;
   }
-  M = -INFINITY;
-  for (int s0 = 0; s0 < num_splits; s0 += 64) {
-    const int s = s0 + lane;
-    M = fmaxf(M, s < num_splits ? lse_part[(size_t)s * qh_count + qh] : -INFINITY);
+  // Up to 64 splits: lane s holds split s's lse (one load).  Splits of weight zero (empty
+  // ones) are not accumulated, and their rows are not fetched from memory.
+  const bool one_chunk = num_splits <= 64;
+  float lse_l = -INFINITY;
+  if (one_chunk) {
+    lse_l = lane < num_splits ? lse_part[(size_t)lane * qh_count + qh] : -INFINITY;
+    M = fwave_max(lse_l);
+  } else {
+    M = -INFINITY;
+    for (int s0 = 0; s0 < num_splits; s0 += 64) {
+      const int s = s0 + lane;
+      M = fmaxf(M, s < num_splits ? lse_part[(size_t)s * qh_count + qh] : -INFINITY);
+    }
+    M = fwave_max(M);
   }
-  M = fwave_max(M);
   if (M == -INFINITY) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
     z = 0.f;
     return;
   }
-  z = 0.f;
-  for (int s0 = 0; s0 < num_splits; s0 += 64) {
-    const int s = s0 + lane;
-    z += s < num_splits ? expf(lse_part[(size_t)s * qh_count + qh] - M) : 0.f;
+  const float w_own = expf(lse_l - M);             // one_chunk: this lane's split weight
+  if (one_chunk) {
+    z = fwave_sum(w_own);
+  } else {
+    z = 0.f;
+    for (int s0 = 0; s0 < num_splits; s0 += 64) {
+      const int s = s0 + lane;
+      z += s < num_splits ? expf(lse_part[(size_t)s * qh_count + qh] - M) : 0.f;
+    }
+    z = fwave_sum(z);
   }
-  z = fwave_sum(z);
   const float inv_z = 1.0f / z;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const int c = 8 * lane;
   for (int s0 = 0; s0 < num_splits; s0 += 64) {
     const int sl = s0 + lane;
-    const float wl = sl < num_splits ? expf(lse_part[(size_t)sl * qh_count + qh] - M) : 0.f;
+    const float wl = one_chunk ? w_own : (sl < num_splits ? expf(lse_part[(size_t)sl * qh_count + qh] - M) : 0.f);
     const int cnt = num_splits - s0 < 64 ? num_splits - s0 : 64;
     int u = 0;
     for (; u + 8 <= cnt; u += 8) {
+      float ws[8];
       float v[8][8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) load8p(o_part + ((size_t)(s0 + u + k) * qh_count + qh) * kFDc + c, v[k]);
+      for (int k = 0; k < 8; ++k) ws[k] = __shfl(wl, u + k);
+      // a split of weight zero re-reads the chunk's first row (a cache hit), so that all
+      // eight loads go out unconditionally and back to back
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        load8p(o_part + ((size_t)(s0 + u + (ws[k] != 0.f ? k : 0)) * qh_count + qh) * kFDc + c, v[k]);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float ws = __shfl(wl, u + k);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, v[k][e], acc[e]) : acc[e];
+        for (int e = 0; e < 8; ++e) acc[e] = ws[k] != 0.f ? fmaf(ws[k], v[k][e], acc[e]) : acc[e];
       }
     }
     for (; u < cnt; ++u) {
-      float v[8];
-      load8p(o_part + ((size_t)(s0 + u) * qh_count + qh) * kFDc + c, v);
       const float ws = __shfl(wl, u);
+      if (ws != 0.f) {
+        float v[8];
+        load8p(o_part + ((size_t)(s0 + u) * qh_count + qh) * kFDc + c, v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, v[e], acc[e]) : acc[e];
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, v[e], acc[e]);
+      }
     }
   }
 #pragma unroll

@@ -96,56 +96,78 @@ merge_splits_kernel(const PartT* __restrict__ o_part, const float* __restrict__ 
     if (lane == 0) lse[qh] = M + logf(z);
     return;
   }
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < num_splits; s0 += 64) {
-    const int s = s0 + lane;
-    M = fmaxf(M, s < num_splits ? lse_part[(size_t)s * qh_count + qh] : -INFINITY);
+  // Up to 64 splits: lane s holds split s's lse (one load).  Splits of weight zero (empty
+  // ones) are not accumulated, and their rows are not fetched from memory.
+  const bool one_chunk = num_splits <= 64;
+  float lse_l = -INFINITY;
+  float M;
+  if (one_chunk) {
+    lse_l = lane < num_splits ? lse_part[(size_t)lane * qh_count + qh] : -INFINITY;
+    M = wave_max(lse_l);
+  } else {
+    M = -INFINITY;
+    for (int s0 = 0; s0 < num_splits; s0 += 64) {
+      const int s = s0 + lane;
+      M = fmaxf(M, s < num_splits ? lse_part[(size_t)s * qh_count + qh] : -INFINITY);
+    }
+    M = wave_max(M);
   }
-  M = wave_max(M);
   float* out = o_lat + (size_t)qh * d_c;
   if (M == -INFINITY) {                           // no split saw a row
     for (int c = lane; c < d_c; c += 64) out[c] = 0.f;
     if (lane == 0) lse[qh] = -INFINITY;
     return;
   }
-  float z = 0.f;
-  for (int s0 = 0; s0 < num_splits; s0 += 64) {
-    const int s = s0 + lane;
-    z += s < num_splits ? expf(lse_part[(size_t)s * qh_count + qh] - M) : 0.f;
+  const float w_own = expf(lse_l - M);             // one_chunk: this lane's split weight
+  float z;
+  if (one_chunk) {
+    z = wave_sum(w_own);
+  } else {
+    z = 0.f;
+    for (int s0 = 0; s0 < num_splits; s0 += 64) {
+      const int s = s0 + lane;
+      z += s < num_splits ? expf(lse_part[(size_t)s * qh_count + qh] - M) : 0.f;
+    }
+    z = wave_sum(z);
   }
-  z = wave_sum(z);
   const float inv_z = 1.0f / z;
   const bool vec = (d_c & 7) == 0;
   for (int c = vec ? 8 * lane : lane; c < d_c; c += vec ? 8 * 64 : 64) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < num_splits; s0 += 64) {
       const int sl = s0 + lane;
-      const float wl = sl < num_splits ? expf(lse_part[(size_t)sl * qh_count + qh] - M) : 0.f;
+      const float wl = one_chunk ? w_own : (sl < num_splits ? expf(lse_part[(size_t)sl * qh_count + qh] - M) : 0.f);
       const int cnt = num_splits - s0 < 64 ? num_splits - s0 : 64;
       int u = 0;
       for (; u + 8 <= cnt; u += 8) {               // eight splits' loads in flight
+        float ws[8];
         float v[8][8];
 #pragma unroll
+        for (int k = 0; k < 8; ++k) ws[k] = __shfl(wl, u + k);
+        // a split of weight zero re-reads the chunk's first row (a cache hit), so that all
+        // eight loads go out unconditionally and back to back
+#pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const PartT* p = o_part + ((size_t)(s0 + u + k) * qh_count + qh) * d_c + c;
+          const PartT* p = o_part + ((size_t)(s0 + u + (ws[k] != 0.f ? k : 0)) * qh_count + qh) * d_c + c;
           if (vec) load8(p, v[k]);
           else v[k][0] = load1(p);
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const float ws = __shfl(wl, u + k);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, v[k][e], acc[e]) : acc[e];
+          for (int e = 0; e < 8; ++e) acc[e] = ws[k] != 0.f ? fmaf(ws[k], v[k][e], acc[e]) : acc[e];
         }
       }
       for (; u < cnt; ++u) {
-        float v[8];
-        const PartT* p = o_part + ((size_t)(s0 + u) * qh_count + qh) * d_c + c;
-        if (vec) load8(p, v);
-        else v[0] = load1(p);
         const float ws = __shfl(wl, u);
+        if (ws != 0.f) {
+          float v[8];
+          const PartT* p = o_part + ((size_t)(s0 + u) * qh_count + qh) * d_c + c;
+          if (vec) load8(p, v);
+          else v[0] = load1(p);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, v[e], acc[e]) : acc[e];
+          for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, v[e], acc[e]);
+        }
       }
     }
     if (vec) {
