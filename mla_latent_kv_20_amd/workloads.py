@@ -370,3 +370,36 @@ def draw_o_lat(n_q: int, n_h: int, d_c: int, seed: int = 3) -> np.ndarray:
     """Latent attention outputs [n_q, n_h, d_c] fp32 (scale of a softmax-weighted mean)."""
     rng = np.random.default_rng(seed)
     return (rng.standard_normal((n_q, n_h, d_c)) * 0.05).astype(np.float32)
+
+
+@dataclasses.dataclass
+class Prologue:
+    """Inputs of the decode prologue for n_new new tokens (storage type, drawn directly).
+
+    h [n_new, d_model] hidden states ~ N(0, 1); w_dkv [d_c, d_model] and w_kr [d_r, d_model]
+    ~ N(0, 1/d_model) (unit-variance outputs, as for the other weights); q_r_raw
+    [n_new, n_h, d_r] ~ N(0, 1), the query's RoPE part before rotation; positions [n_new]
+    and dst_rows [n_new] int64.
+    """
+    dtype: str
+    d_model: int
+    h: np.ndarray
+    w_dkv: np.ndarray
+    w_kr: np.ndarray
+    q_r_raw: np.ndarray
+    positions: np.ndarray
+    dst_rows: np.ndarray
+
+
+def draw_prologue(w: Workload, d_model: int, positions, dst_rows, seed: int = 4) -> Prologue:
+    """Prologue inputs for the new tokens of workload w (one per query token, n_q of them)."""
+    rng = np.random.default_rng(seed)
+    n = w.n_q
+    h = rng.standard_normal((n, d_model))
+    w_dkv = rng.standard_normal((w.d_c, d_model)) * math.sqrt(1.0 / d_model)
+    w_kr = rng.standard_normal((w.d_r, d_model)) * math.sqrt(1.0 / d_model)
+    q_r_raw = rng.standard_normal((n, w.n_h, w.d_r))
+    pos = np.asarray(positions, np.int64).reshape(n)
+    dst = np.asarray(dst_rows, np.int64).reshape(n)
+    return Prologue(w.dtype, d_model, round_to_storage(h, w.dtype), round_to_storage(w_dkv, w.dtype),
+                    round_to_storage(w_kr, w.dtype), round_to_storage(q_r_raw, w.dtype), pos, dst)

@@ -31,7 +31,9 @@ Two formulations are computed independently:
                    latents ([notes] "Key에 대한 수식 전개" and "Value에 대한 수식 전개";
                    [report] "Идея 1"): the form the GPU path computes.
 and the per-call pieces of the absorbed form (absorb_q, split_partials, merge_splits,
-out_proj) that the C-ABI entry points are compared against one by one.
+out_proj) that the C-ABI entry points are compared against one by one.  The decode
+prologue (kv_prologue, append_rows, absorb_q_rope) gives the new tokens' cache rows and
+the rotated queries from the hidden states.
 
 Readings where the pages are silent or garbled (each is listed in the design notes):
   * scale 1/sqrt(d_h + d_h^R) (three pages agree; one prints it without the root);
@@ -264,6 +266,47 @@ def rope_pairs(x, positions, theta: float = 10000.0) -> np.ndarray:
     ang = np.asarray(positions, np.float64)[..., None] * np.power(theta, -2.0 * k / d)
     z = z * np.exp(1j * ang)
     return np.concatenate([z.real, z.imag], axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# Decode prologue: the new tokens' latent rows and the rotated query part
+# ----------------------------------------------------------------------------
+
+def kv_prologue(h, w_dkv, w_kr, positions, theta: float = 10000.0):
+    """Latent row of each new token: c^KV = W^DKV h ([notes] eq. 9) and the decoupled RoPE
+    key k^R = RoPE(W^KR h) at the token's position ([notes] "Decoupled Rotary Position
+    Embedding", items 2-3; "MLA 코드 구현": the down-projections and the rotation apply to the
+    new tokens only, and the cache keeps k^R after rotation).
+
+    h [n, d_model]; w_dkv [d_c, d_model]; w_kr [d_r, d_model]; positions [n].
+    Returns (c_kv [n, d_c], k_r [n, d_r]) in fp64.
+    """
+    h = np.asarray(h, np.float64)
+    c_kv = h @ np.asarray(w_dkv, np.float64).T
+    k_r = rope_pairs(h @ np.asarray(w_kr, np.float64).T, np.asarray(positions), theta)
+    return c_kv, k_r
+
+
+def append_rows(rows, dst_rows, c_kv, k_r) -> np.ndarray:
+    """The cache after the new tokens' rows [c^KV ; k^R] are written at dst_rows; every other
+    row is unchanged ([notes] "MLA 코드 구현": the new latent rows are concatenated after the
+    cached ones)."""
+    out = np.array(rows, np.float64, copy=True)
+    c_kv = np.asarray(c_kv, np.float64)
+    k_r = np.asarray(k_r, np.float64)
+    d_c, d_r = c_kv.shape[1], k_r.shape[1]
+    for t, r in enumerate(np.asarray(dst_rows)):
+        out[int(r), :d_c] = c_kv[t]
+        out[int(r), d_c:d_c + d_r] = k_r[t]
+    return out
+
+
+def absorb_q_rope(q_c, q_r_raw, w_uk, positions, theta: float = 10000.0) -> np.ndarray:
+    """absorb_q with every head's RoPE part rotated at its token's position first ([notes]
+    "MLA 코드 구현": q^R is rotated head by head at the new tokens' positions; "Decoupled
+    Rotary Position Embedding", item 1).  positions [n_q]."""
+    q_r = rope_pairs(np.asarray(q_r_raw, np.float64), np.asarray(positions)[:, None], theta)
+    return absorb_q(q_c, q_r, w_uk)
 
 
 def cache_elems_per_token(kind: str, layers: int, n_h: int = 0, d_h: int = 0, n_g: int = 0,

@@ -459,6 +459,141 @@ def test_rope_on_compressed_keys_breaks_absorption():
 
 
 # ----------------------------------------------------------------------------
+# Decode prologue: new latent rows and rotated queries from the hidden states
+# ----------------------------------------------------------------------------
+
+def _rope_listing_form(x, pos, theta=10000.0):
+    """RoPE built as the listing in [notes] "MLA 코드 구현" builds it, with scalar loops:
+    angles pos * theta^(-2j/d) for j < d/2, repeated over both halves, and
+    out = x * cos + rotate_half(x) * sin with rotate_half([a, b]) = [-b, a]."""
+    d = len(x)
+    h = d // 2
+    out = []
+    for k in range(d):
+        ang = pos * theta ** (-2.0 * (k % h) / d)
+        partner = -x[k + h] if k < h else x[k - h]
+        out.append(x[k] * math.cos(ang) + partner * math.sin(ang))
+    return out
+
+
+def _prologue_brute(h, wd, wr, pos):
+    c, k = [], []
+    for t in range(len(h)):
+        c.append([sum(wd[i][m] * h[t][m] for m in range(len(h[t]))) for i in range(len(wd))])
+        raw = [sum(wr[i][m] * h[t][m] for m in range(len(h[t]))) for i in range(len(wr))]
+        k.append(_rope_listing_form(raw, pos[t]))
+    return np.array(c), np.array(k)
+
+
+def _prologue_inputs(seed=41, n=4, dm=12, d_c=8, d_r=6):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((n, dm)), rng.standard_normal((d_c, dm)), rng.standard_normal((d_r, dm)),
+            [0, 3, 4096, 131071][:n])
+
+
+def test_kv_prologue_brute_force():
+    h, wd, wr, pos = _prologue_inputs()
+    c, k = O.kv_prologue(h, wd, wr, pos)
+    cb, kb = _prologue_brute(h.tolist(), wd.tolist(), wr.tolist(), pos)
+    assert rel(c, cb) <= 1e-13
+    assert rel(k, kb) <= 1e-10          # angles up to 1.3e5 rad: pow and argument reduction
+
+
+def test_kv_prologue_at_position_zero_is_the_plain_projection():
+    h, wd, wr, _ = _prologue_inputs()
+    _, k = O.kv_prologue(h, wd, wr, [0] * len(h))
+    assert np.array_equal(k, h @ wr.T)
+
+
+@pytest.mark.parametrize("mutant", ["interleaved_pairs", "position_off_by_one", "angle_sign",
+                                    "frequency_without_two", "w_dkv_transposed"])
+def test_planted_prologue_mistakes_are_caught(mutant):
+    h, wd, wr, pos = _prologue_inputs(n=4, dm=8, d_c=8, d_r=6)    # square W^DKV: a transpose runs
+    if mutant == "interleaved_pairs":           # pairs (2j, 2j+1) instead of (j, j + d/2)
+        c, raw = O.kv_prologue(h, wd, wr, [0] * 4)
+        perm = np.concatenate([np.arange(0, 6, 2), np.arange(1, 6, 2)])
+        inv = np.argsort(perm)
+        k = O.rope_pairs(raw[:, perm], pos)[:, inv]
+    elif mutant == "position_off_by_one":
+        c, k = O.kv_prologue(h, wd, wr, np.asarray(pos) + 1)
+    elif mutant == "angle_sign":
+        c, k = O.kv_prologue(h, wd, wr, -np.asarray(pos))
+    elif mutant == "frequency_without_two":     # theta^(-j/d) for theta^(-2j/d)
+        c, _ = O.kv_prologue(h, wd, wr, pos)
+        k = O.rope_pairs(h @ wr.T, np.asarray(pos), theta=100.0)
+    else:
+        c, k = O.kv_prologue(h, wd.T, wr, pos)
+    cb, kb = _prologue_brute(h.tolist(), wd.tolist(), wr.tolist(), pos)
+    with pytest.raises(AssertionError):
+        assert rel(c, cb) <= 1e-13 and rel(k, kb) <= 1e-10
+
+
+def test_absorb_q_rope_brute_force():
+    rng = np.random.default_rng(43)
+    n_q, n_h, d_h, d_c, d_r = 3, 2, 4, 8, 6
+    q_c = rng.standard_normal((n_q, n_h, d_h))
+    q_r = rng.standard_normal((n_q, n_h, d_r))
+    w_uk = rng.standard_normal((n_h, d_h, d_c))
+    pos = [7, 0, 65536]
+    got = O.absorb_q_rope(q_c, q_r, w_uk, pos)
+    for n in range(n_q):
+        for i in range(n_h):
+            lat = [sum(w_uk[i][d][x] * q_c[n][i][d] for d in range(d_h)) for x in range(d_c)]
+            want = lat + _rope_listing_form(q_r[n][i].tolist(), pos[n])
+            assert rel(got[n, i], want) <= 1e-10
+
+
+def test_append_rows_writes_only_its_rows():
+    rng = np.random.default_rng(45)
+    rows = rng.standard_normal((10, 7))
+    c = rng.standard_normal((2, 5))
+    k = rng.standard_normal((2, 2))
+    out = O.append_rows(rows, [3, 8], c, k)
+    keep = [r for r in range(10) if r not in (3, 8)]
+    assert np.array_equal(out[keep], rows[keep])
+    assert np.array_equal(out[3], np.concatenate([c[0], k[0]]))
+    assert np.array_equal(out[8], np.concatenate([c[1], k[1]]))
+
+
+def _decode_from_hidden(shift, key_shift_only=False, seed=47):
+    """One sequence built token by token from hidden states, then decoded by its last token."""
+    rng = np.random.default_rng(seed)
+    L, dm, n_h, d_h, d_c, d_r = 9, 16, 2, 4, 8, 6
+    h = rng.standard_normal((L, dm))
+    wd, wr = rng.standard_normal((d_c, dm)) * 0.3, rng.standard_normal((d_r, dm)) * 0.3
+    w_uk, w_uv = rng.standard_normal((n_h, d_h, d_c)), rng.standard_normal((n_h, d_h, d_c))
+    q_c, q_r = rng.standard_normal((1, n_h, d_h)), rng.standard_normal((1, n_h, d_r))
+    kpos = np.arange(L) + shift
+    qpos = np.array([L - 1 + (0 if key_shift_only else shift)])
+    c, k = O.kv_prologue(h, wd, wr, kpos)
+    rows = O.append_rows(np.zeros((L, d_c + d_r)), np.arange(L), c, k)
+    qa = O.absorb_q_rope(q_c, q_r, w_uk, qpos)
+    res = O.absorbed_decode(rows[:, :d_c], rows[:, d_c:], np.array([0, L]), q_c,
+                            qa[:, :, d_c:], w_uk, w_uv, 1)
+    # scores straight from the hidden states: q^C . W^UK W^DKV h_j + RoPE(q^R) . RoPE(W^KR h_j)
+    s = np.array([[q_c[0, i] @ (w_uk[i] @ (wd @ h[j])) +
+                   O.rope_pairs(q_r[0, i], qpos[0]) @ O.rope_pairs(wr @ h[j], kpos[j]) for j in range(L)]
+                  for i in range(n_h)]) / math.sqrt(d_h + d_r)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    direct = np.array([sum(p[i, j] * (w_uv[i] @ (wd @ h[j])) for j in range(L)) for i in range(n_h)])
+    return res["o_c"][0], direct
+
+
+def test_prologue_then_decode_is_attention_over_the_hidden_states():
+    got, direct = _decode_from_hidden(0)
+    assert rel(got, direct) <= 1e-12
+
+
+def test_prologue_then_decode_depends_only_on_relative_positions():
+    base, _ = _decode_from_hidden(0)
+    moved, _ = _decode_from_hidden(100000)
+    assert rel(moved, base) <= 1e-9
+    keys_only, _ = _decode_from_hidden(100000, key_shift_only=True)
+    assert rel(keys_only, base) > 1e-3
+
+
+# ----------------------------------------------------------------------------
 # Cache-size numbers printed on the pages
 # ----------------------------------------------------------------------------
 
