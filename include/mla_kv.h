@@ -21,6 +21,10 @@
  *
  * mla_merge_out_proj does the last two in one call, with the same results.
  *
+ * The decode prologue builds this step's inputs from the hidden states:
+ *   mla_kv_append     new cache rows [W^DKV h ; RoPE(W^KR h)] at given rows
+ *   mla_absorb_q_rope mla_absorb_q with q^R rotated at the tokens' positions
+ *
  * Together they compute, for query t and head i,
  *   o_{t,i} = sum_j softmax_j(q_{t,i}^T k_{j,i} * scale) v^C_{j,i}
  * with k_{j,i} = [W^UK_i c^KV_j ; k^R_j], v^C_{j,i} = W^UV_i c^KV_j and
@@ -41,7 +45,9 @@
  *    needs d_c % 128 == 0, d_h % 16 == 0, d_h <= 256, d_r % 8 == 0;
  *    mla_out_proj needs d_h % 32 == 0, d_c % 64 == 0, d_c <= 512 (the
  *    DeepSeek-V2 attention shape fits all) and 16-byte aligned rows;
- *    mla_merge_out_proj needs d_c == 512 and d_h == 128; other
+ *    mla_merge_out_proj needs d_c == 512 and d_h == 128; mla_kv_append needs
+ *    d_model % 128 == 0, d_c % 32 == 0 and d_r == 64; mla_absorb_q_rope needs
+ *    mla_absorb_q's shapes and d_r % 16 == 0; other
  *    shapes return MLA_ERR_UNSUPPORTED.  dtype MLA_F32 runs plain fp32
  *    kernels for any shape (no bf16 rounding anywhere).
  */
@@ -57,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 3
+#define MLA_ABI_VERSION 4
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -107,6 +113,55 @@ const char* mla_status_string(mla_status_t status);
 mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t n_q,
                           const void* q_c, const void* q_r, const void* w_uk,
                           void* q_abs, hipStream_t stream);
+
+/*
+ * mla_absorb_q_rope - mla_absorb_q with the RoPE part rotated first: every head's
+ * q_r_raw[n, i, :] is rotated at positions[n] ([notes] "MLA 코드 구현": q^R is rotated
+ * head by head at the new tokens' positions; RoPE as in mla_kv_append), then
+ *   q_abs[n, i, 0:d_c]       = sum_d q_c[n, i, d] * w_uk[i, d, :]
+ *   q_abs[n, i, d_c:d_c+d_r] = RoPE(q_r_raw[n, i, :], positions[n])
+ *
+ *   q_r_raw    [n_q, n_h, d_r]   dtype   per-head RoPE query before rotation
+ *   positions  [n_q] int64, device memory: each query token's position
+ *   rope_theta > 0: the RoPE base; <= 0: 10000
+ * Other arguments and errors as mla_absorb_q; positions must be 8-byte aligned
+ * and non-NULL (MLA_ERR_NULL); bf16 needs d_r % 16 == 0 and 16-byte aligned
+ * q_r_raw and q_abs.
+ */
+mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t n_q, const void* q_c,
+                               const void* q_r_raw, const void* w_uk, const int64_t* positions,
+                               float rope_theta, void* q_abs, hipStream_t stream);
+
+/*
+ * mla_kv_append - the new tokens' latent rows, written into the cache ([notes]
+ * eq. 9 and "Decoupled Rotary Position Embedding", items 2-3; "MLA 코드 구현":
+ * the down-projections apply to the new tokens only and the cache keeps k^R
+ * after rotation).  For new token t:
+ *   c^KV_t = W^DKV h_t,   k^R_t = RoPE(W^KR h_t, positions[t])
+ *   rows[dst_rows[t] * stride + 0 : d_c]         = c^KV_t
+ *   rows[dst_rows[t] * stride + d_c : d_c + d_r] = k^R_t
+ * RoPE rotates the pairs (v_k, v_{k+d_r/2}), k < d_r/2, by the angle
+ * positions[t] * theta^(-2k/d_r): (v_k cos - v_{k+d_r/2} sin, v_{k+d_r/2} cos + v_k sin),
+ * the rotate-half form of the listing in "MLA 코드 구현"; angles and rotations are
+ * evaluated in fp64.  No other cache element is touched.
+ *
+ *   h          [n_new, d_model]      dtype   hidden states of the new tokens
+ *   w_dkv      [d_c, d_model]        dtype   W^DKV
+ *   w_kr       [d_r, d_model]        dtype   W^KR
+ *   positions  [n_new] int64, device memory: each token's position
+ *   dst_rows   [n_new] int64, device memory: each token's cache row; distinct rows,
+ *              each below the number of rows behind `rows` (not checked)
+ *   rows       cache rows [*, stride] in dtype, packed [c^KV | k^R] (stride >= d_c + d_r)
+ *   rope_theta > 0: the RoPE base; <= 0: 10000
+ * bf16: fp32 accumulation, each output rounded once to bf16 (the k^R outputs
+ * after the fp64 rotation of the fp32 sums); needs d_model % 128 == 0,
+ * d_c % 32 == 0, d_r == 64 (else MLA_ERR_UNSUPPORTED) and 16-byte aligned h,
+ * w_dkv and w_kr.  fp32: any shape.  positions and dst_rows 8-byte aligned.
+ */
+mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t n_new, int32_t d_model, const void* h,
+                           const void* w_dkv, const void* w_kr, const int64_t* positions,
+                           const int64_t* dst_rows, void* rows, int64_t stride, float rope_theta,
+                           hipStream_t stream);
 
 /* Bytes of o_part for (n_q, num_splits, partial_dtype):
  * num_splits * n_q * n_h * d_c * (4 for MLA_F32, 2 for MLA_F16).  lse_part holds

@@ -47,6 +47,8 @@ SIGNATURES = {
     "mla_merge_splits": (_I32, [_DIMS_P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "mla_out_proj": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P]),
     "mla_merge_out_proj": (_I32, [_DIMS_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]),
+    "mla_absorb_q_rope": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P, ctypes.c_float, _P, _P]),
+    "mla_kv_append": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _I64, ctypes.c_float, _P]),
 }
 
 _lib = None
@@ -134,6 +136,30 @@ def absorb_q(d: MlaDims, q_c, q_r, w_uk, q_abs=None, stream=None):
     _check("mla_absorb_q", load().mla_absorb_q(ctypes.byref(d), n_q, _ptr(q_c), _ptr(q_r), _ptr(w_uk),
                                                 _ptr(q_abs), _stream(stream)))
     return q_abs
+
+
+def absorb_q_rope(d: MlaDims, q_c, q_r_raw, w_uk, positions, q_abs=None, rope_theta: float = 10000.0,
+                  stream=None):
+    """q_abs[n, i] = [W^UK_i^T q_c[n, i] ; RoPE(q_r_raw[n, i], positions[n])]."""
+    import torch
+    n_q = q_c.shape[0]
+    if q_abs is None:
+        q_abs = torch.empty((n_q, d.n_h, d.d_c + d.d_r), dtype=q_c.dtype, device=q_c.device)
+    _check("mla_absorb_q_rope", load().mla_absorb_q_rope(ctypes.byref(d), n_q, _ptr(q_c), _ptr(q_r_raw),
+                                                          _ptr(w_uk), _ptr(positions), float(rope_theta),
+                                                          _ptr(q_abs), _stream(stream)))
+    return q_abs
+
+
+def kv_append(d: MlaDims, h, w_dkv, w_kr, positions, dst_rows, rows, rope_theta: float = 10000.0,
+              stream=None):
+    """Write [W^DKV h_t ; RoPE(W^KR h_t, positions[t])] into cache row dst_rows[t] of `rows`
+    ([*, stride] tensor, stride = rows.stride(0)); returns rows."""
+    n_new, d_model = h.shape
+    _check("mla_kv_append", load().mla_kv_append(ctypes.byref(d), n_new, d_model, _ptr(h), _ptr(w_dkv),
+                                                  _ptr(w_kr), _ptr(positions), _ptr(dst_rows), _ptr(rows),
+                                                  rows.stride(0), float(rope_theta), _stream(stream)))
+    return rows
 
 
 def decode(d: MlaDims, q_abs, c_kv, k_r, offsets, batch: int, q_per_seq: int = 1,

@@ -36,6 +36,8 @@ struct AbsorbParams {
   const bf16_bits* w_uk;  // [n_h, d_h, d_c]
   bf16_bits* q_abs;       // [n_q, n_h, d_c + d_r]
   int n_q, n_h, d_h, d_c, d_r;
+  const int64_t* pos;     // [n_q] token positions: rotate q_r there first; null: copy q_r as is
+  double log_theta;       // ln(RoPE theta)
 };
 
 __global__ void __launch_bounds__(kThreads)
@@ -149,8 +151,10 @@ absorb_q_bf16_kernel(AbsorbParams P) {
 
   // RoPE part: copied once per head, by the first column block, 16 bytes per thread with
   // every load of a thread in flight before its stores.  It comes last, so that its
-  // memory latency does not delay the weight loads above.
-  if (cbi == 0) {
+  // memory latency does not delay the weight loads above.  With token positions the pairs
+  // (k, k + d_r/2) are rotated on the way ([notes] "MLA 코드 구현": q^R is rotated head by
+  // head at the new tokens' positions); a thread then owns chunk c and chunk c + d_r/16.
+  if (cbi == 0 && P.pos == nullptr) {
     const int cpr = P.d_r / 8;                    // 16-byte chunks per query row (d_r % 8 == 0)
     const int total = P.n_q * cpr;
     for (int e0 = 0; e0 < total; e0 += 4 * kThreads) {
@@ -168,8 +172,32 @@ absorb_q_bf16_kernel(AbsorbParams P) {
           *(bf16x8*)(P.q_abs + ((size_t)(e / cpr) * P.n_h + i) * d_qk + P.d_c + (e % cpr) * 8) = v[u];
       }
     }
+  } else if (cbi == 0) {
+    const int half = P.d_r / 2;
+    const int hp = P.d_r / 16;                    // chunk pairs per query row (d_r % 16 == 0)
+    const int total = P.n_q * hp;
+    for (int e = tid; e < total; e += kThreads) {
+      const int n = e / hp, c = e % hp;
+      const bf16_bits* src = P.q_r + ((size_t)n * P.n_h + i) * P.d_r + 8 * c;
+      // elements as 16-bit lanes: indexing a __bf16 vector element by element is not used
+      typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+      const u16x8 a = *(const u16x8*)src;
+      const u16x8 b = *(const u16x8*)(src + half);
+      const int64_t pos = P.pos[n];
+      u16x8 oa, ob;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        double x = bf16_to_f32(a[j]);
+        double y = bf16_to_f32(b[j]);
+        rope_pair(x, y, pos, 8 * c + j, P.d_r, P.log_theta);
+        oa[j] = f32_to_bf16((float)x);
+        ob[j] = f32_to_bf16((float)y);
+      }
+      bf16_bits* dst = P.q_abs + ((size_t)n * P.n_h + i) * d_qk + P.d_c + 8 * c;
+      *(u16x8*)dst = oa;
+      *(u16x8*)(dst + half) = ob;
+    }
   }
-
 }
 
 // ---------------------------------------------------------------------------
@@ -262,8 +290,8 @@ bool out_proj_bf16_supported(int d_h, int d_c) {
 
 hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, const bf16_bits* w_uk,
                                 bf16_bits* q_abs, int n_q, int n_h, int d_h, int d_c, int d_r,
-                                hipStream_t stream) {
-  AbsorbParams P{q_c, q_r, w_uk, q_abs, n_q, n_h, d_h, d_c, d_r};
+                                const int64_t* positions, double theta, hipStream_t stream) {
+  AbsorbParams P{q_c, q_r, w_uk, q_abs, n_q, n_h, d_h, d_c, d_r, positions, positions ? log(theta) : 0.0};
   const size_t smem = (size_t)d_h * kAbsPitch + 32 * kAbsOutPitch;
   const int grid = 8 * ((n_h + 7) / 8) * (d_c / kAbsCols);
   hipLaunchKernelGGL(absorb_q_bf16_kernel, dim3(grid), dim3(kThreads), smem, stream, P);

@@ -16,7 +16,7 @@ hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* rows, int
                               int split_rows, float scale, hipStream_t stream);
 hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, const bf16_bits* w_uk,
                                 bf16_bits* q_abs, int n_q, int n_h, int d_h, int d_c, int d_r,
-                                hipStream_t stream);
+                                const int64_t* positions, double theta, hipStream_t stream);
 hipError_t launch_out_proj_bf16(const float* o_lat, const bf16_bits* w_uv, bf16_bits* o_c, int n_q,
                                 int n_h, int d_h, int d_c, hipStream_t stream);
 bool absorb_bf16_supported(int d_h, int d_c);
@@ -28,7 +28,13 @@ bool out_proj_bf16_supported(int d_h, int d_c);
 hipError_t launch_merge(const void* o_part, bool f16_partials, const float* lse_part, float* o_lat,
                         float* lse, int n_q, int n_h, int d_c, int num_splits, hipStream_t stream);
 hipError_t launch_absorb_q_f32(const float* q_c, const float* q_r, const float* w_uk, float* q_abs,
-                               int n_q, int n_h, int d_h, int d_c, int d_r, hipStream_t stream);
+                               int n_q, int n_h, int d_h, int d_c, int d_r, const int64_t* positions,
+                               double theta, hipStream_t stream);
+// prologue.hip
+bool kv_append_bf16_supported(int d_model, int d_c, int d_r);
+hipError_t launch_kv_append(bool bf16, const void* h, const void* w_dkv, const void* w_kr,
+                            const int64_t* positions, const int64_t* dst_rows, void* rows, int64_t stride,
+                            int n_new, int d_model, int d_c, int d_r, double theta, hipStream_t stream);
 size_t decode_f32_smem_bytes(int d_c, int d_r);
 hipError_t launch_decode_f32(const float* q_abs, const float* c_kv, int64_t c_stride, const float* k_r,
                              int64_t r_stride, const int64_t* offsets, float* o_part, float* lse_part,
@@ -104,8 +110,11 @@ mla_status_t mla_check_offsets(const int64_t* host_offsets, int32_t batch, int32
   return MLA_OK;
 }
 
-mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t n_q, const void* q_c, const void* q_r,
-                          const void* w_uk, void* q_abs, hipStream_t stream) {
+namespace {
+// Shared by mla_absorb_q and mla_absorb_q_rope: positions == nullptr copies q_r as is.
+mla_status_t absorb_common(const mla_dims_t* dims, int32_t n_q, const void* q_c, const void* q_r,
+                           const void* w_uk, const int64_t* positions, float rope_theta, void* q_abs,
+                           hipStream_t stream) {
   mla_status_t st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (n_q < 0) return MLA_ERR_SHAPE;
@@ -115,17 +124,58 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t n_q, const void* q_c, 
   if ((int64_t)n_q * dims->n_h * d_qk >= kMaxElems ||
       (int64_t)dims->n_h * dims->d_h * dims->d_c >= kMaxElems)
     return MLA_ERR_SHAPE;
+  const double theta = rope_theta > 0.f ? (double)rope_theta : 10000.0;
+  if (positions && !aligned(positions, 8)) return MLA_ERR_ALIGN;
   const uintptr_t a = esize(dims);
   if (!aligned(q_c, a) || !aligned(q_r, a) || !aligned(w_uk, a) || !aligned(q_abs, a)) return MLA_ERR_ALIGN;
   if (dims->dtype == MLA_F32)
     return launched(mla::launch_absorb_q_f32((const float*)q_c, (const float*)q_r, (const float*)w_uk,
                                              (float*)q_abs, n_q, dims->n_h, dims->d_h, dims->d_c,
-                                             dims->d_r, stream));
+                                             dims->d_r, positions, theta, stream));
   if (!mla::absorb_bf16_supported(dims->d_h, dims->d_c) || dims->d_r % 8) return MLA_ERR_UNSUPPORTED;
+  if (positions && dims->d_r % 16) return MLA_ERR_UNSUPPORTED;   // rotated in pairs of 16-byte chunks
   if (!aligned(q_c, 16) || !aligned(w_uk, 16)) return MLA_ERR_ALIGN;
+  if (positions && (!aligned(q_r, 16) || !aligned(q_abs, 16))) return MLA_ERR_ALIGN;
   return launched(mla::launch_absorb_q_bf16((const uint16_t*)q_c, (const uint16_t*)q_r,
                                             (const uint16_t*)w_uk, (uint16_t*)q_abs, n_q, dims->n_h,
-                                            dims->d_h, dims->d_c, dims->d_r, stream));
+                                            dims->d_h, dims->d_c, dims->d_r, positions, theta, stream));
+}
+}  // namespace
+
+mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t n_q, const void* q_c, const void* q_r,
+                          const void* w_uk, void* q_abs, hipStream_t stream) {
+  return absorb_common(dims, n_q, q_c, q_r, w_uk, nullptr, 0.f, q_abs, stream);
+}
+
+mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t n_q, const void* q_c, const void* q_r_raw,
+                               const void* w_uk, const int64_t* positions, float rope_theta, void* q_abs,
+                               hipStream_t stream) {
+  if (n_q > 0 && !positions) return MLA_ERR_NULL;
+  return absorb_common(dims, n_q, q_c, q_r_raw, w_uk, positions, rope_theta, q_abs, stream);
+}
+
+mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t n_new, int32_t d_model, const void* h,
+                           const void* w_dkv, const void* w_kr, const int64_t* positions,
+                           const int64_t* dst_rows, void* rows, int64_t stride, float rope_theta,
+                           hipStream_t stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_new < 0 || d_model < 1) return MLA_ERR_SHAPE;
+  if (n_new == 0) return MLA_OK;
+  if (!h || !w_dkv || !w_kr || !positions || !dst_rows || !rows) return MLA_ERR_NULL;
+  if (stride < (int64_t)dims->d_c + dims->d_r) return MLA_ERR_SHAPE;
+  if ((int64_t)n_new * d_model >= kMaxElems || (int64_t)dims->d_c * d_model >= kMaxElems) return MLA_ERR_SHAPE;
+  if (!aligned(positions, 8) || !aligned(dst_rows, 8)) return MLA_ERR_ALIGN;
+  const uintptr_t a = esize(dims);
+  if (!aligned(h, a) || !aligned(w_dkv, a) || !aligned(w_kr, a) || !aligned(rows, a)) return MLA_ERR_ALIGN;
+  const double theta = rope_theta > 0.f ? (double)rope_theta : 10000.0;
+  const bool bf16 = dims->dtype == MLA_BF16;
+  if (bf16) {
+    if (!mla::kv_append_bf16_supported(d_model, dims->d_c, dims->d_r)) return MLA_ERR_UNSUPPORTED;
+    if (!aligned(h, 16) || !aligned(w_dkv, 16) || !aligned(w_kr, 16)) return MLA_ERR_ALIGN;
+  }
+  return launched(mla::launch_kv_append(bf16, h, w_dkv, w_kr, positions, dst_rows, rows, stride, n_new,
+                                        d_model, dims->d_c, dims->d_r, theta, stream));
 }
 
 mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, int32_t q_per_seq, const void* q_abs,

@@ -185,7 +185,8 @@ merge_splits_kernel(const PartT* __restrict__ o_part, const float* __restrict__ 
 // ---------------------------------------------------------------------------
 __global__ void absorb_q_f32_kernel(const float* __restrict__ q_c, const float* __restrict__ q_r,
                                     const float* __restrict__ w_uk, float* __restrict__ q_abs,
-                                    int n_q, int n_h, int d_h, int d_c, int d_r) {
+                                    int n_q, int n_h, int d_h, int d_c, int d_r,
+                                    const int64_t* __restrict__ pos, double log_theta) {
   const int d_qk = d_c + d_r;
   const size_t total = (size_t)n_q * n_h * d_qk;
   for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total;
@@ -199,8 +200,15 @@ __global__ void absorb_q_f32_kernel(const float* __restrict__ q_c, const float* 
       float acc = 0.f;
       for (int d = 0; d < d_h; ++d) acc = fmaf(q[d], w[(size_t)d * d_c], acc);
       q_abs[e] = acc;
-    } else {
+    } else if (pos == nullptr) {
       q_abs[e] = q_r[ni * d_r + (c - d_c)];
+    } else {                                       // rotated at the token's position
+      const int half = d_r / 2;
+      const int k = c - d_c;
+      const int k0 = k < half ? k : k - half;
+      double x = q_r[ni * d_r + k0], y = q_r[ni * d_r + k0 + half];
+      rope_pair(x, y, pos[ni / n_h], k0, d_r, log_theta);
+      q_abs[e] = (float)(k < half ? x : y);
     }
   }
 }
@@ -340,10 +348,11 @@ hipError_t launch_merge(const void* o_part, bool f16_partials, const float* lse_
 }
 
 hipError_t launch_absorb_q_f32(const float* q_c, const float* q_r, const float* w_uk, float* q_abs,
-                               int n_q, int n_h, int d_h, int d_c, int d_r, hipStream_t stream) {
+                               int n_q, int n_h, int d_h, int d_c, int d_r, const int64_t* positions,
+                               double theta, hipStream_t stream) {
   const size_t total = (size_t)n_q * n_h * (d_c + d_r);
   hipLaunchKernelGGL(absorb_q_f32_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream, q_c, q_r,
-                     w_uk, q_abs, n_q, n_h, d_h, d_c, d_r);
+                     w_uk, q_abs, n_q, n_h, d_h, d_c, d_r, positions, positions ? log(theta) : 0.0);
   return hipGetLastError();
 }
 

@@ -24,6 +24,20 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float bf16_to_f32(bf16_bits b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
+
+// RoPE of one rotate-half pair (x, y) = (v_k, v_{k+d/2}) at `pos`: rotation by the angle
+// pos * theta^(-2k/d) ([notes] "MLA(Multi-head Latent Attention): DeepSeek-V2 논문정리",
+// "MLA 코드 구현"), with the angle and the rotation evaluated in fp64.
+__device__ __forceinline__ void rope_pair(double& x, double& y, int64_t pos, int k, int d,
+                                          double log_theta) {
+  const double ang = (double)pos * exp(-(2.0 * k / d) * log_theta);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  const double nx = x * cs - y * sn;
+  const double ny = y * cs + x * sn;
+  x = nx;
+  y = ny;
+}
 __device__ __forceinline__ bf16_bits f32_to_bf16(float f) {
   return __builtin_bit_cast(bf16_bits, (__bf16)f);
 }

@@ -392,9 +392,9 @@ class Prologue:
 
 
 def draw_prologue(w: Workload, d_model: int, positions, dst_rows, seed: int = 4) -> Prologue:
-    """Prologue inputs for the new tokens of workload w (one per query token, n_q of them)."""
+    """Prologue inputs for len(positions) new tokens with the dimensions of workload w."""
     rng = np.random.default_rng(seed)
-    n = w.n_q
+    n = len(positions)
     h = rng.standard_normal((n, d_model))
     w_dkv = rng.standard_normal((w.d_c, d_model)) * math.sqrt(1.0 / d_model)
     w_kr = rng.standard_normal((w.d_r, d_model)) * math.sqrt(1.0 / d_model)

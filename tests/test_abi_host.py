@@ -37,7 +37,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert set(names) == set(B.SIGNATURES), names
     for n in names:
         assert hasattr(lib, n)
-    assert lib.mla_abi_version() == 3
+    assert lib.mla_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -127,6 +127,36 @@ def test_merge_out_proj_argument_checks(lib):
     assert f(d, o_lat=FAKE + 4) == B.MLA_ERR_ALIGN
     assert f(d, lse=FAKE + 2) == B.MLA_ERR_ALIGN
     assert f(dims(dtype=9)) == B.MLA_ERR_DTYPE
+
+
+def test_prologue_argument_checks(lib):
+    """mla_kv_append and mla_absorb_q_rope reject bad arguments before any launch."""
+    d = dims()
+    app = lambda d, n=4, dm=5120, h=FAKE, wd=FAKE, wr=FAKE, pos=FAKE, dst=FAKE, rows=FAKE, stride=576: \
+        lib.mla_kv_append(ctypes.byref(d), n, dm, h, wd, wr, pos, dst, rows, stride, ctypes.c_float(0.0), None)
+    assert app(d, n=0, h=None, wd=None, wr=None, pos=None, dst=None, rows=None) == B.MLA_OK
+    assert app(d, n=-1) == B.MLA_ERR_SHAPE
+    assert app(d, dm=0) == B.MLA_ERR_SHAPE
+    assert app(d, stride=575) == B.MLA_ERR_SHAPE                  # a row must hold d_c + d_r
+    for k in ("h", "wd", "wr", "pos", "dst", "rows"):
+        assert app(d, **{k: None}) == B.MLA_ERR_NULL
+    assert app(d, pos=FAKE + 4) == B.MLA_ERR_ALIGN
+    assert app(d, dst=FAKE + 2) == B.MLA_ERR_ALIGN
+    assert app(d, h=FAKE + 8) == B.MLA_ERR_ALIGN                   # bf16 operands: 16-byte rows
+    assert app(d, rows=FAKE + 1) == B.MLA_ERR_ALIGN
+    assert app(d, dm=5000) == B.MLA_ERR_UNSUPPORTED                # bf16: d_model % 128 == 0
+    assert app(dims(d_r=32)) == B.MLA_ERR_UNSUPPORTED              # bf16: d_r == 64
+    assert app(dims(d_r=63)) == B.MLA_ERR_SHAPE                    # RoPE pairs need an even d_r
+    rope = lambda d, n=4, qc=FAKE, qr=FAKE, w=FAKE, pos=FAKE, out=FAKE: \
+        lib.mla_absorb_q_rope(ctypes.byref(d), n, qc, qr, w, pos, ctypes.c_float(0.0), out, None)
+    assert rope(d, n=0, qc=None, qr=None, w=None, pos=None, out=None) == B.MLA_OK
+    assert rope(d, n=-2) == B.MLA_ERR_SHAPE
+    assert rope(d, pos=None) == B.MLA_ERR_NULL
+    assert rope(d, qr=None) == B.MLA_ERR_NULL
+    assert rope(d, pos=FAKE + 4) == B.MLA_ERR_ALIGN
+    assert rope(d, qr=FAKE + 8) == B.MLA_ERR_ALIGN                 # rotated 16 bytes at a time
+    assert rope(dims(d_r=8)) == B.MLA_ERR_UNSUPPORTED              # bf16: d_r % 16 == 0
+    assert rope(dims(dtype=7)) == B.MLA_ERR_DTYPE
 
 
 def test_partial_bytes(lib):
