@@ -36,6 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 ROW_BYTES = 1152               # one cached latent row [c_KV 512 ; k_R 64] in bf16
 FLOP_PER_ROW_HEAD = 2 * 576 + 2 * 512   # score + weighted sum, per (row, query head)
 MALL_BYTES = 256 << 20
+D_MODEL = 5120                 # DeepSeek-V2 hidden width: input of the decode prologue
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "mla_latent_kv_20_amd", "csrc", f)
                   for f in ("decode_bf16.hip", "mla_common.h")]
@@ -262,6 +263,24 @@ def main():
                                                                 bufs["o_c"], bufs["lse"], None))
         if d.dtype == B.MLA_BF16 else None,
     }
+    # Decode prologue (one new token per query, DeepSeek-V2 hidden width): the new rows go to
+    # a buffer of their own so that the measured caches stay as drawn.
+    prologue = d.dtype == B.MLA_BF16 and (w.d_c + w.d_r) % 32 == 0
+    if prologue:
+        pw_bytes = (w.d_c + w.d_r) * D_MODEL * esz
+        pcopies = math.ceil(2 * MALL_BYTES / pw_bytes)
+        gen = torch.Generator(device=dev).manual_seed(7)
+        h_new = (torch.randn((n_q, D_MODEL), generator=gen, device=dev)).to(base["q_c"].dtype)
+        w_down = [(torch.randn((w.d_c + w.d_r, D_MODEL), generator=gen, device=dev) / math.sqrt(D_MODEL))
+                  .to(base["q_c"].dtype) for _ in range(pcopies)]
+        pos_new = torch.from_numpy(np.diff(w.offsets).astype(np.int64)).to(dev).repeat_interleave(w.q_per_seq)
+        new_rows = torch.empty((n_q, w.d_c + w.d_r), dtype=base["q_c"].dtype, device=dev)
+        dst_new = torch.arange(n_q, dtype=torch.int64, device=dev)
+        ws_new = torch.empty(max(1, B.kv_append_workspace_bytes(d, n_q)), dtype=torch.uint8, device=dev)
+        calls["kv_append"] = (pcopies, lambda j: B.kv_append(d, h_new, w_down[j][:w.d_c], w_down[j][w.d_c:],
+                                                              pos_new, dst_new, new_rows, workspace=ws_new))
+        calls["absorb_q_rope"] = (wcopies, lambda j: B.absorb_q_rope(d, base["q_c"], base["q_r"], w_uk_set[j],
+                                                                      pos_new, bufs["q_abs"]))
     per = {}
     for name, item in calls.items():
         if item is None:
@@ -322,6 +341,13 @@ def main():
                    "partials": {B.MLA_F32: "f32", B.MLA_F16: "f16"}[part]},
         "roofline": roof,
         "kernels_ms_mean": {n: round(v, 5) for n, v in per.items()},
+        "prologue": ({"kv_append": {"n_new": n_q, "d_model": D_MODEL,
+                                    "algorithmic_bytes": (w.d_c + w.d_r) * D_MODEL * esz + n_q * D_MODEL * esz
+                                    + n_q * (w.d_c + w.d_r) * esz + 16 * n_q,
+                                    "GB_per_s": round(((w.d_c + w.d_r) * D_MODEL * esz + n_q * D_MODEL * esz
+                                                       + n_q * (w.d_c + w.d_r) * esz + 16 * n_q)
+                                                      / (per["kv_append"] * 1e-3) / 1e9, 1)},
+                      "absorb_q_rope_ms": round(per["absorb_q_rope"], 5)} if prologue else None),
         "decode_merge_tokens_per_s": round(cached / ((dec_ms + per.get("merge", 0.0)) * 1e-3), 1),
         "timing": "hip graph replay (one graph per pass over the layer copies)" if not args.no_graph else "eager launches",
         "step_calls": "absorb_q, decode, merge_out_proj" if fused else "absorb_q, decode, merge_splits, out_proj",

@@ -46,8 +46,8 @@
  *    mla_out_proj needs d_h % 32 == 0, d_c % 64 == 0, d_c <= 512 (the
  *    DeepSeek-V2 attention shape fits all) and 16-byte aligned rows;
  *    mla_merge_out_proj needs d_c == 512 and d_h == 128; mla_kv_append needs
- *    d_model % 128 == 0, d_c % 32 == 0 and d_r == 64; mla_absorb_q_rope needs
- *    mla_absorb_q's shapes and d_r % 16 == 0; other
+ *    d_model % 512 == 0, d_model <= 8192 and (d_c + d_r) % 32 == 0; mla_absorb_q_rope needs
+ *    mla_absorb_q's shapes and d_r <= 512; other
  *    shapes return MLA_ERR_UNSUPPORTED.  dtype MLA_F32 runs plain fp32
  *    kernels for any shape (no bf16 rounding anywhere).
  */
@@ -125,8 +125,8 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t n_q,
  *   positions  [n_q] int64, device memory: each query token's position
  *   rope_theta > 0: the RoPE base; <= 0: 10000
  * Other arguments and errors as mla_absorb_q; positions must be 8-byte aligned
- * and non-NULL (MLA_ERR_NULL); bf16 needs d_r % 16 == 0 and 16-byte aligned
- * q_r_raw and q_abs.
+ * and non-NULL (MLA_ERR_NULL); bf16 needs d_r <= 512.  The angle is fp64, reduced
+ * to [-pi, pi] in fp64; its sine and cosine are fp32 (relative error ~1e-7).
  */
 mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t n_q, const void* q_c,
                                const void* q_r_raw, const void* w_uk, const int64_t* positions,
@@ -142,8 +142,9 @@ mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t n_q, const void* 
  *   rows[dst_rows[t] * stride + d_c : d_c + d_r] = k^R_t
  * RoPE rotates the pairs (v_k, v_{k+d_r/2}), k < d_r/2, by the angle
  * positions[t] * theta^(-2k/d_r): (v_k cos - v_{k+d_r/2} sin, v_{k+d_r/2} cos + v_k sin),
- * the rotate-half form of the listing in "MLA 코드 구현"; angles and rotations are
- * evaluated in fp64.  No other cache element is touched.
+ * the rotate-half form of the listing in "MLA 코드 구현"; the angle is fp64, reduced
+ * to [-pi, pi] in fp64, with fp32 sine and cosine and an fp64 rotation (relative error
+ * ~1e-7).  No other cache element is touched.
  *
  *   h          [n_new, d_model]      dtype   hidden states of the new tokens
  *   w_dkv      [d_c, d_model]        dtype   W^DKV
@@ -153,15 +154,21 @@ mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t n_q, const void* 
  *              each below the number of rows behind `rows` (not checked)
  *   rows       cache rows [*, stride] in dtype, packed [c^KV | k^R] (stride >= d_c + d_r)
  *   rope_theta > 0: the RoPE base; <= 0: 10000
- * bf16: fp32 accumulation, each output rounded once to bf16 (the k^R outputs
- * after the fp64 rotation of the fp32 sums); needs d_model % 128 == 0,
- * d_c % 32 == 0, d_r == 64 (else MLA_ERR_UNSUPPORTED) and 16-byte aligned h,
- * w_dkv and w_kr.  fp32: any shape.  positions and dst_rows 8-byte aligned.
+ *   workspace  device scratch of at least mla_kv_append_workspace_bytes(dims, n_new)
+ *              bytes (bf16: fp32 partial sums over slices of d_model; fp32 needs none and
+ *              may pass NULL, 0); its contents on entry do not matter, on return they are
+ *              undefined.  Calls that share a workspace must not overlap.
+ * bf16: fp32 accumulation (slices of d_model summed in a fixed order), each output
+ * rounded once to bf16 (the k^R outputs after the rotation of the fp32 sums);
+ * needs d_model % 512 == 0, d_model <= 8192, (d_c + d_r) % 32 == 0 (else
+ * MLA_ERR_UNSUPPORTED) and 16-byte aligned h, w_dkv and w_kr.  fp32: any shape.
+ * positions and dst_rows 8-byte aligned, workspace 4-byte aligned.
  */
+size_t mla_kv_append_workspace_bytes(const mla_dims_t* dims, int32_t n_new);
 mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t n_new, int32_t d_model, const void* h,
                            const void* w_dkv, const void* w_kr, const int64_t* positions,
                            const int64_t* dst_rows, void* rows, int64_t stride, float rope_theta,
-                           hipStream_t stream);
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of o_part for (n_q, num_splits, partial_dtype):
  * num_splits * n_q * n_h * d_c * (4 for MLA_F32, 2 for MLA_F16).  lse_part holds

@@ -48,7 +48,8 @@ SIGNATURES = {
     "mla_out_proj": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P]),
     "mla_merge_out_proj": (_I32, [_DIMS_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]),
     "mla_absorb_q_rope": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P, ctypes.c_float, _P, _P]),
-    "mla_kv_append": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _I64, ctypes.c_float, _P]),
+    "mla_kv_append": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _I64, ctypes.c_float, _P, _SZ, _P]),
+    "mla_kv_append_workspace_bytes": (_SZ, [_DIMS_P, _I32]),
 }
 
 _lib = None
@@ -151,14 +152,26 @@ def absorb_q_rope(d: MlaDims, q_c, q_r_raw, w_uk, positions, q_abs=None, rope_th
     return q_abs
 
 
+def kv_append_workspace_bytes(d: MlaDims, n_new: int) -> int:
+    return int(load().mla_kv_append_workspace_bytes(ctypes.byref(d), n_new))
+
+
 def kv_append(d: MlaDims, h, w_dkv, w_kr, positions, dst_rows, rows, rope_theta: float = 10000.0,
-              stream=None):
+              workspace=None, stream=None):
     """Write [W^DKV h_t ; RoPE(W^KR h_t, positions[t])] into cache row dst_rows[t] of `rows`
-    ([*, stride] tensor, stride = rows.stride(0)); returns rows."""
+    ([*, stride] tensor, stride = rows.stride(0)); returns rows.  The workspace (bytes from
+    kv_append_workspace_bytes) is allocated here when not given."""
+    import torch
     n_new, d_model = h.shape
+    need = kv_append_workspace_bytes(d, n_new)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=h.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("mla_kv_append", load().mla_kv_append(ctypes.byref(d), n_new, d_model, _ptr(h), _ptr(w_dkv),
                                                   _ptr(w_kr), _ptr(positions), _ptr(dst_rows), _ptr(rows),
-                                                  rows.stride(0), float(rope_theta), _stream(stream)))
+                                                  rows.stride(0), float(rope_theta),
+                                                  _ptr(workspace) if workspace is not None else None,
+                                                  ws_bytes, _stream(stream)))
     return rows
 
 

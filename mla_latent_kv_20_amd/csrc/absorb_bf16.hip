@@ -153,7 +153,7 @@ absorb_q_bf16_kernel(AbsorbParams P) {
   // every load of a thread in flight before its stores.  It comes last, so that its
   // memory latency does not delay the weight loads above.  With token positions the pairs
   // (k, k + d_r/2) are rotated on the way ([notes] "MLA 코드 구현": q^R is rotated head by
-  // head at the new tokens' positions); a thread then owns chunk c and chunk c + d_r/16.
+  // head at the new tokens' positions).
   if (cbi == 0 && P.pos == nullptr) {
     const int cpr = P.d_r / 8;                    // 16-byte chunks per query row (d_r % 8 == 0)
     const int total = P.n_q * cpr;
@@ -173,29 +173,21 @@ absorb_q_bf16_kernel(AbsorbParams P) {
       }
     }
   } else if (cbi == 0) {
+    // thread (k, query slot): one inverse frequency per thread, the queries strided
     const int half = P.d_r / 2;
-    const int hp = P.d_r / 16;                    // chunk pairs per query row (d_r % 16 == 0)
-    const int total = P.n_q * hp;
-    for (int e = tid; e < total; e += kThreads) {
-      const int n = e / hp, c = e % hp;
-      const bf16_bits* src = P.q_r + ((size_t)n * P.n_h + i) * P.d_r + 8 * c;
-      // elements as 16-bit lanes: indexing a __bf16 vector element by element is not used
-      typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
-      const u16x8 a = *(const u16x8*)src;
-      const u16x8 b = *(const u16x8*)(src + half);
-      const int64_t pos = P.pos[n];
-      u16x8 oa, ob;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        double x = bf16_to_f32(a[j]);
-        double y = bf16_to_f32(b[j]);
-        rope_pair(x, y, pos, 8 * c + j, P.d_r, P.log_theta);
-        oa[j] = f32_to_bf16((float)x);
-        ob[j] = f32_to_bf16((float)y);
+    const int slots = kThreads / half;            // query slots per pair index (d_r <= 512)
+    if (tid < half * slots) {
+      const int k = tid % half;
+      const double inv = rope_inv_freq(k, P.d_r, P.log_theta);
+      for (int n = tid / half; n < P.n_q; n += slots) {
+        const bf16_bits* src = P.q_r + ((size_t)n * P.n_h + i) * P.d_r;
+        double x = bf16_to_f32(src[k]);
+        double y = bf16_to_f32(src[k + half]);
+        rope_rotate(x, y, P.pos[n], inv);
+        bf16_bits* dst = P.q_abs + ((size_t)n * P.n_h + i) * d_qk + P.d_c;
+        dst[k] = f32_to_bf16((float)x);
+        dst[k + half] = f32_to_bf16((float)y);
       }
-      bf16_bits* dst = P.q_abs + ((size_t)n * P.n_h + i) * d_qk + P.d_c + 8 * c;
-      *(u16x8*)dst = oa;
-      *(u16x8*)(dst + half) = ob;
     }
   }
 }

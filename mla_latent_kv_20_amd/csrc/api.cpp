@@ -32,9 +32,11 @@ hipError_t launch_absorb_q_f32(const float* q_c, const float* q_r, const float* 
                                double theta, hipStream_t stream);
 // prologue.hip
 bool kv_append_bf16_supported(int d_model, int d_c, int d_r);
+size_t kv_append_workspace_bytes(bool bf16, int n_new, int d_c, int d_r);
 hipError_t launch_kv_append(bool bf16, const void* h, const void* w_dkv, const void* w_kr,
                             const int64_t* positions, const int64_t* dst_rows, void* rows, int64_t stride,
-                            int n_new, int d_model, int d_c, int d_r, double theta, hipStream_t stream);
+                            float* workspace, int n_new, int d_model, int d_c, int d_r, double theta,
+                            hipStream_t stream);
 size_t decode_f32_smem_bytes(int d_c, int d_r);
 hipError_t launch_decode_f32(const float* q_abs, const float* c_kv, int64_t c_stride, const float* k_r,
                              int64_t r_stride, const int64_t* offsets, float* o_part, float* lse_part,
@@ -133,9 +135,8 @@ mla_status_t absorb_common(const mla_dims_t* dims, int32_t n_q, const void* q_c,
                                              (float*)q_abs, n_q, dims->n_h, dims->d_h, dims->d_c,
                                              dims->d_r, positions, theta, stream));
   if (!mla::absorb_bf16_supported(dims->d_h, dims->d_c) || dims->d_r % 8) return MLA_ERR_UNSUPPORTED;
-  if (positions && dims->d_r % 16) return MLA_ERR_UNSUPPORTED;   // rotated in pairs of 16-byte chunks
+  if (positions && dims->d_r > 512) return MLA_ERR_UNSUPPORTED;  // a pair index per thread of 256
   if (!aligned(q_c, 16) || !aligned(w_uk, 16)) return MLA_ERR_ALIGN;
-  if (positions && (!aligned(q_r, 16) || !aligned(q_abs, 16))) return MLA_ERR_ALIGN;
   return launched(mla::launch_absorb_q_bf16((const uint16_t*)q_c, (const uint16_t*)q_r,
                                             (const uint16_t*)w_uk, (uint16_t*)q_abs, n_q, dims->n_h,
                                             dims->d_h, dims->d_c, dims->d_r, positions, theta, stream));
@@ -154,10 +155,15 @@ mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t n_q, const void* 
   return absorb_common(dims, n_q, q_c, q_r_raw, w_uk, positions, rope_theta, q_abs, stream);
 }
 
+size_t mla_kv_append_workspace_bytes(const mla_dims_t* dims, int32_t n_new) {
+  if (check_dims(dims) != MLA_OK || n_new < 0) return 0;
+  return mla::kv_append_workspace_bytes(dims->dtype == MLA_BF16, n_new, dims->d_c, dims->d_r);
+}
+
 mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t n_new, int32_t d_model, const void* h,
                            const void* w_dkv, const void* w_kr, const int64_t* positions,
                            const int64_t* dst_rows, void* rows, int64_t stride, float rope_theta,
-                           hipStream_t stream) {
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   mla_status_t st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (n_new < 0 || d_model < 1) return MLA_ERR_SHAPE;
@@ -173,9 +179,12 @@ mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t n_new, int32_t d_mode
   if (bf16) {
     if (!mla::kv_append_bf16_supported(d_model, dims->d_c, dims->d_r)) return MLA_ERR_UNSUPPORTED;
     if (!aligned(h, 16) || !aligned(w_dkv, 16) || !aligned(w_kr, 16)) return MLA_ERR_ALIGN;
+    if (!workspace) return MLA_ERR_NULL;
+    if (workspace_bytes < mla::kv_append_workspace_bytes(true, n_new, dims->d_c, dims->d_r)) return MLA_ERR_SHAPE;
+    if (!aligned(workspace, 4)) return MLA_ERR_ALIGN;
   }
-  return launched(mla::launch_kv_append(bf16, h, w_dkv, w_kr, positions, dst_rows, rows, stride, n_new,
-                                        d_model, dims->d_c, dims->d_r, theta, stream));
+  return launched(mla::launch_kv_append(bf16, h, w_dkv, w_kr, positions, dst_rows, rows, stride,
+                                        (float*)workspace, n_new, d_model, dims->d_c, dims->d_r, theta, stream));
 }
 
 mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, int32_t q_per_seq, const void* q_abs,

@@ -8,20 +8,23 @@
 //   row dst_t of the cache <- [c^KV_t ; k^R_t] ([notes] "MLA 코드 구현": the new latent rows
 //                                             follow the cached ones)
 // RoPE rotates the pairs (k, k + d_r/2) by position * theta^(-2k/d_r), the rotate-half form
-// of the listing in "MLA 코드 구현"; angles and the rotation are evaluated in fp64.
+// of the listing in "MLA 코드 구현" (rope_rotate: fp64 angle, fp32 sine and cosine).
 //
-// bf16: one workgroup per (32 tokens, 32 columns of c^KV) or (32 tokens, the 64 columns of
-// k^R, whose rotation pairs columns k and k+32 of the same lane).  The eight waves split
-// d_model; their 32x32 products meet in LDS.  The down-projection weights are streamed once
-// per token block; at decode batch sizes the call is bound by that weight traffic.
+// bf16, two kernels.  At decode batch sizes the call is bound by the down-projection
+// weights ((d_c + d_r) x d_model), so they are spread over many workgroups: workgroup =
+// (32 output columns, 32 tokens, one of kSplitK slices of d_model), four waves splitting
+// the slice, every load of a wave in flight at once.  Each workgroup writes its fp32 32x32
+// product to the caller's workspace; the finishing kernel sums the slices in order,
+// rotates the k^R pairs (columns k and k + d_r/2 of one token) and stores bf16 rows.
 #include "mla_common.h"
 
 namespace mla {
 namespace {
 
-constexpr int kAppWaves = 8;
+constexpr int kSplitK = 8;                    // slices of d_model over workgroups
+constexpr int kAppWaves = 4;
 constexpr int kAppThreads = kAppWaves * 64;
-constexpr int kAppUnroll = 4;                 // k-steps whose loads go out together
+constexpr int kMaxSteps = 16;                 // k-steps of 16 per wave: d_model <= 8*4*16*16
 
 struct AppendParams {
   const void* h;           // [n_new, d_model]
@@ -30,82 +33,90 @@ struct AppendParams {
   const int64_t* pos;      // [n_new]
   const int64_t* dst;      // [n_new]
   void* rows;              // cache rows, `stride` elements each
+  float* ws;               // bf16: [kSplitK][n_new][d_c + d_r] partial sums
   int64_t stride;
   int n_new, d_model, d_c, d_r;
   double log_theta;        // ln(theta)
 };
 
+// Kernel 1: partial products of one (column block, token block, K slice).
 __global__ void __launch_bounds__(kAppThreads)
-kv_append_bf16_kernel(AppendParams P) {
-  __shared__ f32x16 red[kAppWaves][2][64];        // [wave][tile][lane] partial products
-  const int nlat = P.d_c / 32;
-  const int cb = blockIdx.x;
-  const bool rope = cb == nlat;                   // the k^R block: two 32-column tiles
+kv_append_partial_kernel(AppendParams P) {
+  __shared__ f32x16 red[kAppWaves][64];
+  const int width = P.d_c + P.d_r;
+  const int cb = blockIdx.x;                      // 32-column block of [c^KV | k^R]
   const int tok0 = blockIdx.y * 32;
+  const int ks = blockIdx.z;                      // K slice
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int tok = tok0 + (lane & 31);
   const int tok_ld = tok < P.n_new ? tok : P.n_new - 1;
-
+  const int col = 32 * cb + (lane & 31);          // output column of this lane's W row
+  const bf16_bits* wrow = col < P.d_c ? (const bf16_bits*)P.w_dkv + (size_t)col * P.d_model
+                                      : (const bf16_bits*)P.w_kr + (size_t)(col - P.d_c) * P.d_model;
+  const int steps = P.d_model / (16 * kSplitK * kAppWaves);   // k-steps per wave
+  const int k0 = (ks * kAppWaves + wave) * steps * 16 + 8 * (lane >> 5);
+  const bf16_bits* hp = (const bf16_bits*)P.h + (size_t)tok_ld * P.d_model + k0;
+  const bf16_bits* wp = wrow + k0;
   // D[col][token] = sum_k W[col][k] h[token][k]: A = W rows (lane l: column l%32, 8
-  // consecutive k), B = h^T (lane l: token l%32, 8 consecutive k).
-  const bf16_bits* hrow = (const bf16_bits*)P.h + (size_t)tok_ld * P.d_model + 8 * (lane >> 5);
-  const bf16_bits* w0 = rope ? (const bf16_bits*)P.w_kr + (size_t)(lane & 31) * P.d_model
-                             : (const bf16_bits*)P.w_dkv + (size_t)(32 * cb + (lane & 31)) * P.d_model;
-  w0 += 8 * (lane >> 5);
-  const bf16_bits* w1 = w0 + (size_t)32 * P.d_model;   // rope: k^R columns 32..63
-
-  const int ksteps = P.d_model / 16;
-  const int per_wave = ksteps / kAppWaves;            // d_model % 128 == 0
-  const int s_begin = wave * per_wave;
-  f32x16 acc0, acc1;
+  // consecutive k), B = h^T (lane l: token l%32, 8 consecutive k)
+  bf16x8 a[kMaxSteps], b[kMaxSteps];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    acc0[r] = 0.f;
-    acc1[r] = 0.f;
-  }
-  for (int s0 = s_begin; s0 < s_begin + per_wave; s0 += kAppUnroll) {
-    bf16x8 hb[kAppUnroll], wa[kAppUnroll], wb[kAppUnroll];
-#pragma unroll
-    for (int u = 0; u < kAppUnroll; ++u) {
-      if (s0 + u < s_begin + per_wave) {
-        hb[u] = *(const bf16x8*)(hrow + 16 * (s0 + u));
-        wa[u] = *(const bf16x8*)(w0 + 16 * (s0 + u));
-        if (rope) wb[u] = *(const bf16x8*)(w1 + 16 * (s0 + u));
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kAppUnroll; ++u) {
-      if (s0 + u < s_begin + per_wave) {
-        acc0 = mfma32x32x16(wa[u], hb[u], acc0);
-        if (rope) acc1 = mfma32x32x16(wb[u], hb[u], acc1);
-      }
+  for (int s = 0; s < kMaxSteps; ++s) {
+    if (s < steps) {
+      a[s] = *(const bf16x8*)(wp + 16 * s);
+      b[s] = *(const bf16x8*)(hp + 16 * s);
     }
   }
-  red[wave][0][lane] = acc0;
-  if (rope) red[wave][1][lane] = acc1;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSteps; ++s)
+    if (s < steps) acc = mfma32x32x16(a[s], b[s], acc);
+  red[wave][lane] = acc;
   __syncthreads();
   if (wave != 0) return;
-
-  // Wave 0 sums the partials in wave order, then rotates (k^R block) and stores.
-  // D layout: lane l, reg r -> column 8(r/4) + 4(l/32) + r%4 of the tile, token l%32.
+  // D layout: lane l, reg r -> column 8(r/4) + 4(l/32) + r%4 of the block, token l%32
   if (tok >= P.n_new) return;
-  bf16_bits* dst = (bf16_bits*)P.rows + P.dst[tok] * P.stride;
+  float* out = P.ws + ((size_t)ks * P.n_new + tok) * width + 32 * cb;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int col = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    float x = 0.f, y = 0.f;
+    float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kAppWaves; ++w) x += red[w][0][lane][r];
-    if (!rope) {
-      dst[32 * cb + col] = f32_to_bf16(x);
+    for (int w = 0; w < kAppWaves; ++w) v += red[w][lane][r];
+    out[8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)] = v;
+  }
+}
+
+// Kernel 2: one thread per (token, c^KV column or k^R pair): slices summed in order,
+// the pair rotated, bf16 stored.
+__global__ void kv_append_finish_kernel(AppendParams P) {
+  const int width = P.d_c + P.d_r;
+  const int half = P.d_r / 2;
+  const int per_tok = P.d_c + half;
+  const size_t total = (size_t)P.n_new * per_tok;
+  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+    const int t = (int)(e / per_tok);
+    const int c = (int)(e % per_tok);
+    const float* src = P.ws + (size_t)t * width;
+    const size_t slice = (size_t)P.n_new * width;
+    bf16_bits* dst = (bf16_bits*)P.rows + P.dst[t] * P.stride;
+    if (c < P.d_c) {
+      float v = 0.f;
+      for (int s = 0; s < kSplitK; ++s) v += src[s * slice + c];
+      dst[c] = f32_to_bf16(v);
     } else {
-#pragma unroll
-      for (int w = 0; w < kAppWaves; ++w) y += red[w][1][lane][r];
+      const int k = c - P.d_c;
+      float x = 0.f, y = 0.f;
+      for (int s = 0; s < kSplitK; ++s) {
+        x += src[s * slice + P.d_c + k];
+        y += src[s * slice + P.d_c + k + half];
+      }
       double dx = x, dy = y;
-      rope_pair(dx, dy, P.pos[tok], col, P.d_r, P.log_theta);
-      dst[P.d_c + col] = f32_to_bf16((float)dx);
-      dst[P.d_c + 32 + col] = f32_to_bf16((float)dy);
+      rope_pair(dx, dy, P.pos[t], k, P.d_r, P.log_theta);
+      dst[P.d_c + k] = f32_to_bf16((float)dx);
+      dst[P.d_c + k + half] = f32_to_bf16((float)dy);
     }
   }
 }
@@ -142,23 +153,35 @@ __global__ void kv_append_f32_kernel(AppendParams P) {
   }
 }
 
+unsigned grid_of(size_t total) { return (unsigned)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536); }
+
 }  // namespace
 
 bool kv_append_bf16_supported(int d_model, int d_c, int d_r) {
-  return d_model % (16 * kAppWaves) == 0 && d_model > 0 && d_c % 32 == 0 && d_r == 64;
+  const int unit = 16 * kSplitK * kAppWaves;
+  return d_model > 0 && d_model % unit == 0 && d_model / unit <= kMaxSteps && (d_c + d_r) % 32 == 0 &&
+         d_r % 2 == 0;
+}
+
+size_t kv_append_workspace_bytes(bool bf16, int n_new, int d_c, int d_r) {
+  return bf16 ? (size_t)kSplitK * n_new * (d_c + d_r) * sizeof(float) : 0;
 }
 
 hipError_t launch_kv_append(bool bf16, const void* h, const void* w_dkv, const void* w_kr,
                             const int64_t* positions, const int64_t* dst_rows, void* rows, int64_t stride,
-                            int n_new, int d_model, int d_c, int d_r, double theta, hipStream_t stream) {
-  AppendParams P{h, w_dkv, w_kr, positions, dst_rows, rows, stride, n_new, d_model, d_c, d_r, log(theta)};
+                            float* workspace, int n_new, int d_model, int d_c, int d_r, double theta,
+                            hipStream_t stream) {
+  AppendParams P{h, w_dkv, w_kr, positions, dst_rows, rows, workspace, stride, n_new, d_model, d_c, d_r,
+                 log(theta)};
   if (bf16) {
-    hipLaunchKernelGGL(kv_append_bf16_kernel, dim3(d_c / 32 + 1, (n_new + 31) / 32), dim3(kAppThreads), 0,
+    hipLaunchKernelGGL(kv_append_partial_kernel, dim3((d_c + d_r) / 32, (n_new + 31) / 32, kSplitK),
+                       dim3(kAppThreads), 0, stream, P);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kv_append_finish_kernel, dim3(grid_of((size_t)n_new * (d_c + d_r / 2))), dim3(256), 0,
                        stream, P);
   } else {
-    const size_t total = (size_t)n_new * (d_c + d_r);
-    const unsigned grid = (unsigned)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
-    hipLaunchKernelGGL(kv_append_f32_kernel, dim3(grid), dim3(256), 0, stream, P);
+    hipLaunchKernelGGL(kv_append_f32_kernel, dim3(grid_of((size_t)n_new * (d_c + d_r))), dim3(256), 0, stream, P);
   }
   return hipGetLastError();
 }

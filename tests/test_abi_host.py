@@ -132,21 +132,29 @@ def test_merge_out_proj_argument_checks(lib):
 def test_prologue_argument_checks(lib):
     """mla_kv_append and mla_absorb_q_rope reject bad arguments before any launch."""
     d = dims()
-    app = lambda d, n=4, dm=5120, h=FAKE, wd=FAKE, wr=FAKE, pos=FAKE, dst=FAKE, rows=FAKE, stride=576: \
-        lib.mla_kv_append(ctypes.byref(d), n, dm, h, wd, wr, pos, dst, rows, stride, ctypes.c_float(0.0), None)
-    assert app(d, n=0, h=None, wd=None, wr=None, pos=None, dst=None, rows=None) == B.MLA_OK
+    app = lambda d, n=4, dm=5120, h=FAKE, wd=FAKE, wr=FAKE, pos=FAKE, dst=FAKE, rows=FAKE, stride=576, \
+        ws=FAKE, wsb=1 << 30: \
+        lib.mla_kv_append(ctypes.byref(d), n, dm, h, wd, wr, pos, dst, rows, stride, ctypes.c_float(0.0),
+                          ws, wsb, None)
+    assert app(d, n=0, h=None, wd=None, wr=None, pos=None, dst=None, rows=None, ws=None, wsb=0) == B.MLA_OK
     assert app(d, n=-1) == B.MLA_ERR_SHAPE
     assert app(d, dm=0) == B.MLA_ERR_SHAPE
     assert app(d, stride=575) == B.MLA_ERR_SHAPE                  # a row must hold d_c + d_r
-    for k in ("h", "wd", "wr", "pos", "dst", "rows"):
+    for k in ("h", "wd", "wr", "pos", "dst", "rows", "ws"):
         assert app(d, **{k: None}) == B.MLA_ERR_NULL
+    need = lib.mla_kv_append_workspace_bytes(ctypes.byref(d), 4)
+    assert need == 8 * 4 * 576 * 4                               # fp32 partial sums of 8 slices
+    assert app(d, wsb=need - 1) == B.MLA_ERR_SHAPE
     assert app(d, pos=FAKE + 4) == B.MLA_ERR_ALIGN
     assert app(d, dst=FAKE + 2) == B.MLA_ERR_ALIGN
     assert app(d, h=FAKE + 8) == B.MLA_ERR_ALIGN                   # bf16 operands: 16-byte rows
     assert app(d, rows=FAKE + 1) == B.MLA_ERR_ALIGN
-    assert app(d, dm=5000) == B.MLA_ERR_UNSUPPORTED                # bf16: d_model % 128 == 0
-    assert app(dims(d_r=32)) == B.MLA_ERR_UNSUPPORTED              # bf16: d_r == 64
+    assert app(d, ws=FAKE + 2) == B.MLA_ERR_ALIGN
+    assert app(d, dm=5000) == B.MLA_ERR_UNSUPPORTED                # bf16: d_model % 512 == 0
+    assert app(d, dm=9216) == B.MLA_ERR_UNSUPPORTED                # bf16: d_model <= 8192
     assert app(dims(d_r=63)) == B.MLA_ERR_SHAPE                    # RoPE pairs need an even d_r
+    f32 = dims(dtype=B.MLA_F32)
+    assert lib.mla_kv_append_workspace_bytes(ctypes.byref(f32), 4) == 0
     rope = lambda d, n=4, qc=FAKE, qr=FAKE, w=FAKE, pos=FAKE, out=FAKE: \
         lib.mla_absorb_q_rope(ctypes.byref(d), n, qc, qr, w, pos, ctypes.c_float(0.0), out, None)
     assert rope(d, n=0, qc=None, qr=None, w=None, pos=None, out=None) == B.MLA_OK
@@ -154,8 +162,8 @@ def test_prologue_argument_checks(lib):
     assert rope(d, pos=None) == B.MLA_ERR_NULL
     assert rope(d, qr=None) == B.MLA_ERR_NULL
     assert rope(d, pos=FAKE + 4) == B.MLA_ERR_ALIGN
-    assert rope(d, qr=FAKE + 8) == B.MLA_ERR_ALIGN                 # rotated 16 bytes at a time
-    assert rope(dims(d_r=8)) == B.MLA_ERR_UNSUPPORTED              # bf16: d_r % 16 == 0
+    assert rope(d, qr=FAKE + 1) == B.MLA_ERR_ALIGN
+    assert rope(dims(d_r=1024)) == B.MLA_ERR_UNSUPPORTED           # bf16: d_r <= 512
     assert rope(dims(dtype=7)) == B.MLA_ERR_DTYPE
 
 
