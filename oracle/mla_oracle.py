@@ -33,7 +33,9 @@ Two formulations are computed independently:
 and the per-call pieces of the absorbed form (absorb_q, split_partials, merge_splits,
 out_proj) that the C-ABI entry points are compared against one by one.  The decode
 prologue (kv_prologue, append_rows, absorb_q_rope) gives the new tokens' cache rows and
-the rotated queries from the hidden states.
+the rotated queries from the hidden states.  A quantized cache (e4m3_value, e4m3_encode,
+quantize_rows, dequantize_rows) stores each row as FP8 E4M3 codes with one scale per row;
+its decode is the decode above over the dequantized rows.
 
 Readings where the pages are silent or garbled (each is listed in the design notes):
   * scale 1/sqrt(d_h + d_h^R) (three pages agree; one prints it without the root);
@@ -321,3 +323,74 @@ def cache_elems_per_token(kind: str, layers: int, n_h: int = 0, d_h: int = 0, n_
     if kind == "mla":
         return (d_c + d_r) * layers
     raise ValueError(kind)
+
+
+# ----------------------------------------------------------------------------
+# Quantized latent cache: FP8 E4M3 codes with one fp32 scale per row
+# ----------------------------------------------------------------------------
+# The pages say the served DeepSeek-V2 quantizes its KV cache to about 6 bits per element
+# ([review] section 4, "Inference efficiency"; [report] the 93.3% derivation and the
+# economics section) and name no format.  The first concrete format taken here is the
+# OCP FP8 E4M3 ("fn") encoding of every element of the row [c^KV ; k^R], with one scale
+# per row that maps the row's largest magnitude to the format's largest value, 448.
+#
+# E4M3: bit 7 sign, bits 6..3 exponent e (bias 7), bits 2..0 mantissa m.
+#   e > 0: (-1)^sign * 2^(e-7) * (1 + m/8);   e == 0: (-1)^sign * 2^-6 * m/8;
+#   codes 0x7F and 0xFF are NaN; there is no infinity; the largest finite value is 448.
+#
+# Quantization decides integer codes, so it is written in the precision the kernel uses,
+# float32: amax = max |x| over the row, s = fp32(amax / 448), code = E4M3 nearest to
+# fp32(x / s), ties to even, magnitudes above 448 saturated to 448.  A row of zeros gets
+# s = 0 and all codes 0.  Dequantization: x^ = value(code) * s.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code) -> np.ndarray:
+    """Value of every E4M3 code (uint8 array); NaN for 0x7F and 0xFF."""
+    c = np.asarray(code).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """Nearest E4M3 code of every value of y (exact binary values, e.g. float32), ties to
+    even, magnitudes above 448 saturated; the sign bit follows y's sign bit (so -0.0 and
+    negative values that round to zero give 0x80)."""
+    y = np.asarray(y, np.float64)                 # exact: float32 widens without rounding
+    neg = np.signbit(y)
+    a = np.abs(y)
+    # normal range: a = f * 2^k with 0.5 <= f < 1 (frexp is exact), so a = 2^(k-1) (1 + t)
+    f, k = np.frexp(a)
+    e = k - 1                                    # a in [2^e, 2^(e+1))
+    step = np.exp2(e - 3.0)                      # spacing of E4M3 values in that binade
+    q_norm = np.rint(a / step)                   # exact division by a power of two; rint: ties to even
+    # q_norm in [8, 16]; 16 is the next binade's 8 (code arithmetic carries it over)
+    code_norm = (e + 7) * 8 + (q_norm - 8)
+    # subnormal range a < 2^-6: spacing 2^-9, codes 0..8 (8 is the smallest normal)
+    code_sub = np.rint(a / 2.0 ** -9)
+    mag = np.where(a < 2.0 ** -6, code_sub, code_norm)
+    mag = np.minimum(mag, 0x7E)                  # saturate (also the carry past 448)
+    return (mag.astype(np.int64) | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def quantize_rows(rows):
+    """Per-row E4M3 quantization of rows [R, W] (values exact in float32).  Returns
+    (codes uint8 [R, W], scales float32 [R]); decisions in float32 as stated above."""
+    x = np.asarray(rows, np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    scales = (amax / np.float32(E4M3_MAX)).astype(np.float32)      # float32 division
+    safe = np.where(scales > 0, scales, np.float32(1.0)).astype(np.float32)
+    y = (x / safe[:, None]).astype(np.float32)                     # float32 division
+    codes = e4m3_encode(y)
+    codes[scales == 0] = 0
+    return codes, scales
+
+
+def dequantize_rows(codes, scales) -> np.ndarray:
+    """x^ = value(code) * scale, fp64 [R, W]."""
+    return e4m3_value(codes) * np.asarray(scales, np.float64)[:, None]

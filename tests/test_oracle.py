@@ -594,6 +594,197 @@ def test_prologue_then_decode_depends_only_on_relative_positions():
 
 
 # ----------------------------------------------------------------------------
+# Quantized latent cache: E4M3 codes with one scale per row
+# ----------------------------------------------------------------------------
+
+def test_e4m3_values_match_the_library_decoding():
+    """Every one of the 256 codes against torch's float8_e4m3fn (the OCP E4M3 format)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    ours = O.e4m3_value(codes)
+    assert np.array_equal(np.isnan(lib), np.isnan(ours))
+    assert np.array_equal(lib[~np.isnan(lib)], ours[~np.isnan(ours)])
+    assert np.nanmax(ours) == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+
+
+def test_e4m3_encode_round_trips_every_finite_code():
+    codes = np.arange(256, dtype=np.uint8)
+    v = O.e4m3_value(codes)
+    fin = ~np.isnan(v)
+    assert np.array_equal(O.e4m3_encode(v[fin]), codes[fin])    # 0x80 is -0.0 and comes back
+
+
+def test_e4m3_encode_matches_the_library_rounding_in_range():
+    """Random float32 values up to 464 (torch does not saturate past it) and every midpoint."""
+    import torch
+    rng = np.random.default_rng(51)
+    y = np.concatenate([rng.standard_normal(100000) * 40, rng.standard_normal(20000) * 0.01,
+                        rng.uniform(-464, 464, 20000)]).astype(np.float32)
+    v = np.sort(O.e4m3_value(np.arange(0x7F, dtype=np.uint8)))
+    mids = ((v[1:] + v[:-1]) / 2).astype(np.float32)             # exact in float32
+    y = np.concatenate([y, mids, -mids, np.float32([464.0, -464.0, 0.0, -0.0])])
+    lib = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(y), lib)
+
+
+def test_e4m3_encode_ties_to_even_and_saturates():
+    v = O.e4m3_value(np.arange(0x7F, dtype=np.uint8))          # codes 0..0x7E, increasing
+    mids = (v[1:] + v[:-1]) / 2
+    got = O.e4m3_encode(mids).astype(np.int64)
+    lo = np.arange(0x7E)                                         # the midpoint between code c and c+1
+    assert np.array_equal(got, np.where(lo % 2 == 0, lo, lo + 1))
+    assert list(O.e4m3_encode([448.0, 463.9, 480.0, 1e6, -1e6])) == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE]
+
+
+def _quant_rows(seed=53, n=40, w=576):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, w)) * np.exp(rng.uniform(-6, 6, (n, 1)))
+    x[3] = 0.0                                                   # a row of zeros
+    x[5, :] = 0.0
+    x[5, 17] = -2.5                                              # one element
+    return x.astype(np.float32).astype(np.float64)
+
+
+def test_quantize_rows_scale_maps_the_largest_magnitude_to_448():
+    x = _quant_rows()
+    codes, s = O.quantize_rows(x)
+    assert s.dtype == np.float32 and s[3] == 0 and not codes[3].any()
+    for r in range(len(x)):
+        if s[r] == 0:
+            continue
+        assert s[r] == np.float32(np.float32(np.abs(x[r]).max()) / np.float32(448))
+        j = int(np.argmax(np.abs(x[r])))
+        assert codes[r, j] & 0x7F == 0x7E                        # |x| / s within rounding of 448
+
+
+def test_dequantized_rows_are_within_half_an_e4m3_step():
+    x = _quant_rows()
+    codes, s = O.quantize_rows(x)
+    xh = O.dequantize_rows(codes, s)
+    # half a step: 2^-4 relative in the normal range, 2^-10 * s below 2^-6 * s; the float32
+    # division adds at most one float32 rounding (2^-24 relative)
+    bound = np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * s[:, None].astype(np.float64)) * (1 + 2.0 ** -20)
+    assert np.all(np.abs(xh - x) <= bound)
+    assert np.array_equal(np.signbit(xh[np.abs(x) > 2.0 ** -9 * s[:, None]]),
+                          np.signbit(x[np.abs(x) > 2.0 ** -9 * s[:, None]]))
+
+
+def test_quantize_rows_is_lossless_on_e4m3_grid_rows():
+    """Rows that already are E4M3 values times a power of two, with 448 present, come back
+    exactly, and so does the decode over them."""
+    rng = np.random.default_rng(55)
+    grid = O.e4m3_value(rng.integers(0, 0x7F, (24, 576)).astype(np.uint8) | np.uint8(0))
+    grid *= np.where(rng.random((24, 576)) < 0.5, -1.0, 1.0)
+    grid[:, 7] = 448.0
+    x = grid * np.exp2(rng.integers(-12, 4, (24, 1)).astype(np.float64))
+    codes, s = O.quantize_rows(x)
+    assert np.array_equal(O.dequantize_rows(codes, s), x)
+
+
+def test_decode_over_a_quantized_cache_is_the_decode_over_its_dequantized_rows():
+    """The special case that reduces to the unquantized decode: grid rows quantize exactly."""
+    rng = np.random.default_rng(57)
+    n_h, d_h, d_c, d_r, L = 2, 4, 16, 8, 11
+    codes = rng.integers(0, 0x7F, (L, d_c + d_r)).astype(np.uint8)
+    codes[:, 0] = 0x7E
+    rows = O.e4m3_value(codes) * np.exp2(rng.integers(-8, 0, (L, 1)).astype(np.float64))
+    q_c, q_r = rng.standard_normal((1, n_h, d_h)), rng.standard_normal((1, n_h, d_r))
+    w_uk, w_uv = rng.standard_normal((n_h, d_h, d_c)), rng.standard_normal((n_h, d_h, d_c))
+    off = np.array([0, L])
+    cq, sq = O.quantize_rows(rows)
+    rq = O.dequantize_rows(cq, sq)
+    a = O.absorbed_decode(rq[:, :d_c], rq[:, d_c:], off, q_c, q_r, w_uk, w_uv, 1)
+    b = O.naive_decode(rows[:, :d_c], rows[:, d_c:], off, q_c, q_r, w_uk, w_uv, 1)
+    assert rel(a["o_c"], b["o_c"]) <= 1e-12
+
+
+def _encoder_pins(enc):
+    """The encoder pins above, run on a given encoder (raises AssertionError on a miss)."""
+    import torch
+    rng = np.random.default_rng(51)
+    y = np.concatenate([rng.standard_normal(20000) * 40, rng.standard_normal(20000) * 0.01]).astype(np.float32)
+    v = np.sort(O.e4m3_value(np.arange(0x7F, dtype=np.uint8)))
+    mids = ((v[1:] + v[:-1]) / 2).astype(np.float32)
+    y = np.concatenate([y, mids, -mids])
+    lib = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(enc(y), lib)
+    assert list(enc(np.float32([480.0, 1e6, -1e6]))) == [0x7E, 0x7E, 0xFE]
+
+
+def _quantizer_pins(quant):
+    """The quantizer pins above, run on a given quantizer."""
+    x = _quant_rows()
+    codes, s = quant(x)
+    for r in range(len(x)):
+        if s[r] != 0:
+            assert codes[r, int(np.argmax(np.abs(x[r])))] & 0x7F == 0x7E
+    xh = O.dequantize_rows(codes, s)
+    bound = np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * s[:, None].astype(np.float64)) * (1 + 2.0 ** -20)
+    assert np.all(np.abs(xh - x) <= bound)
+
+
+def _enc_truncate(y):                            # toward zero instead of to nearest
+    v = np.sort(O.e4m3_value(np.arange(0x7F, dtype=np.uint8)))
+    idx = np.searchsorted(v, np.abs(np.asarray(y, np.float64)), side="right") - 1
+    return (np.minimum(idx, 0x7E) | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def _enc_ties_away(y):                           # ties away from zero
+    y = np.asarray(y, np.float64)
+    c = O.e4m3_encode(y).astype(np.int64)
+    v = O.e4m3_value(c.astype(np.uint8))
+    up = O.e4m3_value((np.minimum((c & 0x7F) + 1, 0x7E) | (c & 0x80)).astype(np.uint8))
+    tie = np.abs(np.abs(up) + np.abs(v) - 2 * np.abs(y)) == 0
+    return np.where(tie & ((c & 0x7F) % 2 == 0) & (np.abs(y) > np.abs(v)), np.minimum((c & 0x7F) + 1, 0x7E) | (c & 0x80), c).astype(np.uint8)
+
+
+def _enc_no_subnormals(y):                       # flush below 2^-6 to zero
+    c = O.e4m3_encode(y)
+    return np.where(np.abs(np.asarray(y, np.float64)) < 2.0 ** -6, c & 0x80, c).astype(np.uint8)
+
+
+def _enc_no_saturation(y):                       # let the carry past 448 through
+    c = O.e4m3_encode(y).astype(np.int64)
+    return np.where(np.abs(np.asarray(y, np.float64)) > 464, (c & 0x80) | 0x7F, c).astype(np.uint8)
+
+
+def _quant_with(max_value=448.0, invert=False):
+    def quant(rows):
+        x = np.asarray(rows, np.float32)
+        s = (np.max(np.abs(x), axis=1) / np.float32(max_value)).astype(np.float32)
+        safe = np.where(s > 0, s, np.float32(1)).astype(np.float32)
+        y = (x * safe[:, None] if invert else x / safe[:, None]).astype(np.float32)
+        codes = O.e4m3_encode(y)
+        codes[s == 0] = 0
+        return codes, s
+    return quant
+
+
+def test_the_quantizer_pins_pass_on_the_oracle():
+    _encoder_pins(O.e4m3_encode)
+    _quantizer_pins(O.quantize_rows)
+
+
+@pytest.mark.parametrize("mutant", ["truncate", "ties_away", "no_subnormals", "no_saturation",
+                                    "fnuz_max", "scale_inverted"])
+def test_planted_quantizer_mistakes_are_caught(mutant):
+    with pytest.raises(AssertionError):
+        if mutant == "truncate":
+            _encoder_pins(_enc_truncate)
+        elif mutant == "ties_away":
+            _encoder_pins(_enc_ties_away)
+        elif mutant == "no_subnormals":
+            _encoder_pins(_enc_no_subnormals)
+        elif mutant == "no_saturation":
+            _encoder_pins(_enc_no_saturation)
+        elif mutant == "fnuz_max":               # scale for E4M3-FNUZ's largest value, 240
+            _quantizer_pins(_quant_with(240.0))
+        else:                                    # multiply by the scale instead of dividing
+            _quantizer_pins(_quant_with(invert=True))
+
+
+# ----------------------------------------------------------------------------
 # Cache-size numbers printed on the pages
 # ----------------------------------------------------------------------------
 
