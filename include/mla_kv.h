@@ -25,6 +25,10 @@
  *   mla_kv_append     new cache rows [W^DKV h ; RoPE(W^KR h)] at given rows
  *   mla_absorb_q_rope mla_absorb_q with q^R rotated at the tokens' positions
  *
+ * A quantized cache keeps each row as FP8 E4M3 codes with one fp32 scale:
+ *   mla_quantize_rows_fp8  rows -> codes and scales
+ *   mla_decode_fp8         mla_decode over the dequantized rows value(code) * scale
+ *
  * Together they compute, for query t and head i,
  *   o_{t,i} = sum_j softmax_j(q_{t,i}^T k_{j,i} * scale) v^C_{j,i}
  * with k_{j,i} = [W^UK_i c^KV_j ; k^R_j], v^C_{j,i} = W^UV_i c^KV_j and
@@ -63,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 4
+#define MLA_ABI_VERSION 5
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -169,6 +173,52 @@ mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t n_new, int32_t d_mode
                            const void* w_dkv, const void* w_kr, const int64_t* positions,
                            const int64_t* dst_rows, void* rows, int64_t stride, float rope_theta,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mla_quantize_rows_fp8 - quantize cache rows to FP8 E4M3 codes with one scale per row.
+ * The pages report a KV cache quantized to about 6 bits per element in serving ([review]
+ * section 4, "Inference efficiency"; [report] the 93.3% derivation and the economics
+ * section) and give no format; this is a first concrete one.  For source row i, with
+ * x its first d_c + d_r elements (the row [c^KV ; k^R]) and every step in fp32:
+ *   s     = max_k |x_k| / 448                        (correctly rounded division)
+ *   c_k   = the OCP E4M3 ("fn") code nearest to x_k / s (correctly rounded division),
+ *           ties to even, magnitudes above 448 saturated to 448; sign bit from x_k / s
+ *   a row of zeros gets s = 0 and all codes 0
+ *   codes[dst * code_stride + k] = c_k,   scales[dst] = s,   dst = dst_rows ? dst_rows[i] : i
+ * Dequantized value: value(c_k) * s, with value(c) = (-1)^(c>>7) 2^(e-7) (1 + m/8) for
+ * e = (c>>3)&15 > 0, (-1)^(c>>7) 2^-6 m/8 for e = 0, m = c&7 (0x7F, 0xFF: NaN, never written).
+ *
+ *   rows       [n_rows, row_stride] in dims->dtype (MLA_BF16 or MLA_F32)
+ *   dst_rows   [n_rows] int64 device memory, or NULL; distinct, each below the number
+ *              of code rows (not checked)
+ *   codes      uint8 code rows of code_stride >= d_c + d_r bytes
+ *   scales     fp32, one per code row
+ * Needs d_c + d_r <= 1024 (else MLA_ERR_UNSUPPORTED), row_stride >= d_c + d_r, dst_rows
+ * 8-byte and scales 4-byte aligned; finite inputs.  One wave per row; not on the decode's
+ * hot loop.
+ */
+mla_status_t mla_quantize_rows_fp8(const mla_dims_t* dims, int64_t n_rows, const void* rows,
+                                   int64_t row_stride, const int64_t* dst_rows, uint8_t* codes,
+                                   int64_t code_stride, float* scales, hipStream_t stream);
+
+/*
+ * mla_decode_fp8 - mla_decode over a quantized cache: row j's key is
+ * value(codes_j[0 : d_c + d_r]) * scales[j] and its value value(codes_j[0 : d_c]) * scales[j]
+ * (codes and scales as mla_quantize_rows_fp8 writes them).  Sequences, masks, splits,
+ * outputs and the empty-split rule are those of mla_decode.
+ *
+ *   q_abs       [batch*q_per_seq, n_h, d_c+d_r] bf16 (dims->dtype must be MLA_BF16)
+ *   codes       code rows of code_stride bytes;  scales  fp32, one per code row
+ *   seq_offsets, num_splits, split_rows, partial_dtype, o_part, lse_part  as mla_decode
+ * The codes widen exactly to bf16 MFMA operands; the row scale multiplies the fp32
+ * scores and is folded into each softmax weight before that weight's rounding to bf16.
+ * Needs d_c == 512, d_r == 64, n_h % 32 == 0 (else MLA_ERR_UNSUPPORTED); codes, q_abs and
+ * o_part 16-byte aligned, code_stride a multiple of 16, scales 4-byte aligned.
+ */
+mla_status_t mla_decode_fp8(const mla_dims_t* dims, int32_t batch, int32_t q_per_seq, const void* q_abs,
+                            const uint8_t* codes, int64_t code_stride, const float* scales,
+                            const int64_t* seq_offsets, int32_t num_splits, int32_t split_rows,
+                            int32_t partial_dtype, void* o_part, float* lse_part, hipStream_t stream);
 
 /* Bytes of o_part for (n_q, num_splits, partial_dtype):
  * num_splits * n_q * n_h * d_c * (4 for MLA_F32, 2 for MLA_F16).  lse_part holds

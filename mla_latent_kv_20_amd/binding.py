@@ -50,6 +50,8 @@ SIGNATURES = {
     "mla_absorb_q_rope": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P, ctypes.c_float, _P, _P]),
     "mla_kv_append": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _I64, ctypes.c_float, _P, _SZ, _P]),
     "mla_kv_append_workspace_bytes": (_SZ, [_DIMS_P, _I32]),
+    "mla_quantize_rows_fp8": (_I32, [_DIMS_P, _I64, _P, _I64, _P, _P, _I64, _P, _P]),
+    "mla_decode_fp8": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _P, _P, _P]),
 }
 
 _lib = None
@@ -197,6 +199,43 @@ def decode(d: MlaDims, q_abs, c_kv, k_r, offsets, batch: int, q_per_seq: int = 1
         ctypes.byref(d), batch, q_per_seq, _ptr(q_abs), _ptr(c_kv), int(c_kv.stride(0)), _ptr(k_r),
         int(k_r.stride(0)), _ptr(offsets), num_splits, split_rows, partial_dtype, _ptr(o_part),
         _ptr(lse_part), _stream(stream)))
+    return o_part, lse_part
+
+
+def quantize_rows_fp8(d: MlaDims, rows, dst_rows=None, codes=None, scales=None, stream=None):
+    """E4M3 codes and one fp32 scale per row of ``rows`` [n, >= d_c + d_r] -> (codes, scales).
+
+    Without ``dst_rows`` row i goes to code row i and new [n, d_c + d_r] uint8 / [n] fp32
+    tensors are returned; with it, ``codes`` and ``scales`` must be given.
+    """
+    import torch
+    n = int(rows.shape[0])
+    width = d.d_c + d.d_r
+    if codes is None:
+        codes = torch.empty((n, width), dtype=torch.uint8, device=rows.device)
+    if scales is None:
+        scales = torch.empty((n,), dtype=torch.float32, device=rows.device)
+    _check("mla_quantize_rows_fp8", load().mla_quantize_rows_fp8(
+        ctypes.byref(d), n, _ptr(rows), int(rows.stride(0)), _ptr(dst_rows), _ptr(codes),
+        int(codes.stride(0)), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def decode_fp8(d: MlaDims, q_abs, codes, scales, offsets, batch: int, q_per_seq: int = 1,
+               num_splits: int = 1, split_rows: int = 0, o_part=None, lse_part=None, stream=None,
+               partial_dtype: int = MLA_F32):
+    """mla_decode over a quantized cache (uint8 code rows ``codes``, fp32 ``scales``)."""
+    import torch
+    n_q = batch * q_per_seq
+    if o_part is None:
+        o_part = torch.empty((num_splits, n_q, d.n_h, d.d_c), dtype=_torch_dtype(partial_dtype),
+                             device=q_abs.device)
+    partial_dtype = _dtype_code(o_part)
+    if lse_part is None:
+        lse_part = torch.empty((num_splits, n_q, d.n_h), dtype=torch.float32, device=q_abs.device)
+    _check("mla_decode_fp8", load().mla_decode_fp8(
+        ctypes.byref(d), batch, q_per_seq, _ptr(q_abs), _ptr(codes), int(codes.stride(0)), _ptr(scales),
+        _ptr(offsets), num_splits, split_rows, partial_dtype, _ptr(o_part), _ptr(lse_part), _stream(stream)))
     return o_part, lse_part
 
 

@@ -37,6 +37,15 @@ hipError_t launch_kv_append(bool bf16, const void* h, const void* w_dkv, const v
                             const int64_t* positions, const int64_t* dst_rows, void* rows, int64_t stride,
                             float* workspace, int n_new, int d_model, int d_c, int d_r, double theta,
                             hipStream_t stream);
+// quant_fp8.hip, decode_fp8.hip
+bool quantize_rows_supported(int width);
+hipError_t launch_quantize_rows(bool bf16, const void* src, int64_t src_stride, int64_t n,
+                                const int64_t* dst_rows, uint8_t* codes, int64_t code_stride, float* scales,
+                                int width, hipStream_t stream);
+hipError_t launch_decode_fp8(const bf16_bits* q_abs, const uint8_t* codes, int64_t stride, const float* scales,
+                             const int64_t* offsets, void* o_part, bool f16_partials, float* lse_part, int batch,
+                             int q_per_seq, int n_h, int num_splits, int split_rows, float scale,
+                             hipStream_t stream);
 size_t decode_f32_smem_bytes(int d_c, int d_r);
 hipError_t launch_decode_f32(const float* q_abs, const float* c_kv, int64_t c_stride, const float* k_r,
                              int64_t r_stride, const int64_t* offsets, float* o_part, float* lse_part,
@@ -226,6 +235,48 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, int32_t q_per_seq
                                           seq_offsets, o_part, partial_dtype == MLA_F16, lse_part,
                                           batch, q_per_seq, dims->n_h, num_splits, split_rows, scale,
                                           stream));
+}
+
+mla_status_t mla_quantize_rows_fp8(const mla_dims_t* dims, int64_t n_rows, const void* rows,
+                                   int64_t row_stride, const int64_t* dst_rows, uint8_t* codes,
+                                   int64_t code_stride, float* scales, hipStream_t stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  const int64_t width = (int64_t)dims->d_c + dims->d_r;
+  if (n_rows < 0 || row_stride < width || code_stride < width) return MLA_ERR_SHAPE;
+  if (!mla::quantize_rows_supported((int)width)) return MLA_ERR_UNSUPPORTED;
+  if (n_rows == 0) return MLA_OK;
+  if (!rows || !codes || !scales) return MLA_ERR_NULL;
+  if (n_rows >= ((int64_t)1 << 33) || (n_rows - 1) * row_stride >= ((int64_t)1 << 40)) return MLA_ERR_SHAPE;
+  if (!aligned(rows, esize(dims)) || !aligned(scales, 4) || (dst_rows && !aligned(dst_rows, 8))) return MLA_ERR_ALIGN;
+  return launched(mla::launch_quantize_rows(dims->dtype == MLA_BF16, rows, row_stride, n_rows, dst_rows, codes,
+                                            code_stride, scales, (int)width, stream));
+}
+
+mla_status_t mla_decode_fp8(const mla_dims_t* dims, int32_t batch, int32_t q_per_seq, const void* q_abs,
+                            const uint8_t* codes, int64_t code_stride, const float* scales,
+                            const int64_t* seq_offsets, int32_t num_splits, int32_t split_rows,
+                            int32_t partial_dtype, void* o_part, float* lse_part, hipStream_t stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (partial_dtype != MLA_F32 && partial_dtype != MLA_F16) return MLA_ERR_DTYPE;
+  if (batch < 0 || q_per_seq < 1 || num_splits < 1) return MLA_ERR_SHAPE;
+  if (num_splits > 1 && split_rows < 1) return MLA_ERR_SHAPE;
+  if (code_stride < (int64_t)dims->d_c + dims->d_r) return MLA_ERR_SHAPE;
+  if (dims->dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (dims->d_c != kDecodeDc || dims->d_r != kDecodeDr || dims->n_h % 32) return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (!q_abs || !codes || !scales || !seq_offsets || !o_part || !lse_part) return MLA_ERR_NULL;
+  const int64_t n_q = (int64_t)batch * q_per_seq;
+  if (n_q >= kMaxElems / dims->n_h || (int64_t)num_splits * n_q * dims->n_h * dims->d_c >= ((int64_t)1 << 40))
+    return MLA_ERR_SHAPE;
+  if ((int64_t)num_splits * n_q * dims->n_h >= kMaxElems) return MLA_ERR_SHAPE;
+  if (code_stride * 32 >= ((int64_t)1 << 31)) return MLA_ERR_SHAPE;
+  if (!aligned(seq_offsets, 8) || !aligned(lse_part, 4) || !aligned(scales, 4)) return MLA_ERR_ALIGN;
+  if (!aligned(q_abs, 16) || !aligned(codes, 16) || code_stride % 16 || !aligned(o_part, 16)) return MLA_ERR_ALIGN;
+  return launched(mla::launch_decode_fp8((const uint16_t*)q_abs, codes, code_stride, scales, seq_offsets, o_part,
+                                         partial_dtype == MLA_F16, lse_part, batch, q_per_seq, dims->n_h,
+                                         num_splits, split_rows, scale_of(dims), stream));
 }
 
 mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t n_q, int32_t num_splits,

@@ -37,7 +37,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert set(names) == set(B.SIGNATURES), names
     for n in names:
         assert hasattr(lib, n)
-    assert lib.mla_abi_version() == 4
+    assert lib.mla_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -165,6 +165,43 @@ def test_prologue_argument_checks(lib):
     assert rope(d, qr=FAKE + 1) == B.MLA_ERR_ALIGN
     assert rope(dims(d_r=1024)) == B.MLA_ERR_UNSUPPORTED           # bf16: d_r <= 512
     assert rope(dims(dtype=7)) == B.MLA_ERR_DTYPE
+
+
+def test_quantized_cache_argument_checks(lib):
+    """mla_quantize_rows_fp8 and mla_decode_fp8 reject bad arguments before any launch."""
+    d = dims()
+    q = lambda d, n=4, rows=FAKE, rs=576, dst=None, codes=FAKE, cs=576, sc=FAKE: \
+        lib.mla_quantize_rows_fp8(ctypes.byref(d), n, rows, rs, dst, codes, cs, sc, None)
+    assert q(d, n=0, rows=None, codes=None, sc=None) == B.MLA_OK
+    assert q(d, n=-1) == B.MLA_ERR_SHAPE
+    assert q(d, rs=575) == B.MLA_ERR_SHAPE                         # a row holds d_c + d_r
+    assert q(d, cs=575) == B.MLA_ERR_SHAPE
+    for k in ("rows", "codes", "sc"):
+        assert q(d, **{k: None}) == B.MLA_ERR_NULL
+    assert q(d, rows=FAKE + 1) == B.MLA_ERR_ALIGN                  # bf16 elements
+    assert q(d, sc=FAKE + 2) == B.MLA_ERR_ALIGN
+    assert q(d, dst=FAKE + 4) == B.MLA_ERR_ALIGN
+    assert q(dims(d_c=1000, d_r=64), rs=2048, cs=2048) == B.MLA_ERR_UNSUPPORTED   # width <= 1024
+    assert q(dims(dtype=B.MLA_F16)) == B.MLA_ERR_DTYPE
+    dec = lambda d, batch=2, qps=1, qa=FAKE, codes=FAKE, cs=576, sc=FAKE, off=FAKE, S=1, R=0, \
+        part=B.MLA_F32, op=FAKE, lp=FAKE: \
+        lib.mla_decode_fp8(ctypes.byref(d), batch, qps, qa, codes, cs, sc, off, S, R, part, op, lp, None)
+    assert dec(d, batch=0) == B.MLA_OK
+    assert dec(d, batch=-1) == B.MLA_ERR_SHAPE
+    assert dec(d, qps=0) == B.MLA_ERR_SHAPE
+    assert dec(d, S=3, R=0) == B.MLA_ERR_SHAPE
+    assert dec(d, cs=575) == B.MLA_ERR_SHAPE
+    assert dec(d, part=B.MLA_BF16) == B.MLA_ERR_DTYPE
+    for k in ("qa", "codes", "sc", "off", "op", "lp"):
+        assert dec(d, **{k: None}) == B.MLA_ERR_NULL
+    assert dec(dims(dtype=B.MLA_F32)) == B.MLA_ERR_UNSUPPORTED      # queries are bf16
+    assert dec(dims(d_c=256)) == B.MLA_ERR_UNSUPPORTED
+    assert dec(dims(n_h=48)) == B.MLA_ERR_UNSUPPORTED
+    assert dec(d, codes=FAKE + 8) == B.MLA_ERR_ALIGN
+    assert dec(d, cs=584) == B.MLA_ERR_ALIGN                       # code rows: 16-byte multiples
+    assert dec(d, sc=FAKE + 2) == B.MLA_ERR_ALIGN
+    assert dec(d, qa=FAKE + 8) == B.MLA_ERR_ALIGN
+    assert dec(d, off=FAKE + 4) == B.MLA_ERR_ALIGN
 
 
 def test_partial_bytes(lib):
