@@ -281,6 +281,29 @@ def main():
                                                               pos_new, dst_new, new_rows, workspace=ws_new))
         calls["absorb_q_rope"] = (wcopies, lambda j: B.absorb_q_rope(d, base["q_c"], base["q_r"], w_uk_set[j],
                                                                       pos_new, bufs["q_abs"]))
+    # Quantized cache (E4M3 codes, one scale per row): each layer copy's cache quantized into
+    # code buffers of its own, enough of them to exceed twice the MALL; the decode alone and
+    # the step absorb_q, decode_fp8, merge_out_proj.
+    fp8 = d.dtype == B.MLA_BF16 and w.d_c == 512 and w.d_r == 64 and w.n_h % 32 == 0
+    if fp8:
+        code_bytes = w.rows * (w.d_c + w.d_r + 4)
+        fcopies = max(copies, math.ceil(2 * MALL_BYTES / code_bytes))
+        fp8_sets = [B.quantize_rows_fp8(d, layers[j % copies]["cache"]) for j in range(fcopies)]
+        torch.cuda.synchronize()
+
+        def fp8_decode(j):
+            return B.decode_fp8(d, bufs["q_abs"], fp8_sets[j][0], fp8_sets[j][1], base["offsets"], w.batch,
+                                w.q_per_seq, S, R, bufs["o_part"], bufs["lse_part"])
+
+        def fp8_step(j):
+            L = layers[j % copies]
+            qa = B.absorb_q(d, L["q_c"], L["q_r"], L["w_uk"], bufs["q_abs"])
+            op, lp = B.decode_fp8(d, qa, fp8_sets[j][0], fp8_sets[j][1], L["offsets"], w.batch, w.q_per_seq,
+                                  S, R, bufs["o_part"], bufs["lse_part"])
+            B.merge_out_proj(d, op, lp, L["w_uv"], bufs["o_c"], bufs["lse"], None)
+
+        calls["decode_fp8"] = (fcopies, fp8_decode)
+        calls["step_fp8"] = (fcopies, fp8_step)
     per = {}
     for name, item in calls.items():
         if item is None:
@@ -348,6 +371,7 @@ def main():
                                                        + n_q * (w.d_c + w.d_r) * esz + 16 * n_q)
                                                       / (per["kv_append"] * 1e-3) / 1e9, 1)},
                       "absorb_q_rope_ms": round(per["absorb_q_rope"], 5)} if prologue else None),
+        "fp8_cache": (fp8_summary(w, per, flops, cached, fcopies) if fp8 else None),
         "decode_merge_tokens_per_s": round(cached / ((dec_ms + per.get("merge", 0.0)) * 1e-3), 1),
         "timing": "hip graph replay (one graph per pass over the layer copies)" if not args.no_graph else "eager launches",
         "step_calls": "absorb_q, decode, merge_out_proj" if fused else "absorb_q, decode, merge_splits, out_proj",
@@ -357,6 +381,21 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def fp8_summary(w, per, flops, cached, fcopies):
+    """The quantized-cache decode: E4M3 codes (576 B) and a 4-byte scale per row."""
+    ms = per["decode_fp8"]
+    nbytes = w.rows * (w.d_c + w.d_r + 4) + w.n_q * w.n_h * (w.d_c + w.d_r) * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfs = flops / (ms * 1e-3) / 1e12
+    return {"format": "e4m3 codes + fp32 scale per row", "code_copies": fcopies,
+            "decode_ms": round(ms, 5), "step_ms": round(per["step_fp8"], 5),
+            "step_tokens_per_s": round(cached / (per["step_fp8"] * 1e-3), 1),
+            "algorithmic_bytes_per_launch": nbytes, "GB_per_s": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "TFLOP_per_s": round(tfs, 1),
+            "mfma_frac": round(tfs / PEAK_BF16_TFLOPS, 4),
+            "bound": "mfma" if flops / nbytes > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"}
 
 
 if __name__ == "__main__":
