@@ -210,7 +210,11 @@ mla_status_t mla_quantize_rows_fp8(const mla_dims_t* dims, int64_t n_rows, const
  *   q_abs       [batch*q_per_seq, n_h, d_c+d_r] bf16 (dims->dtype must be MLA_BF16)
  *   codes       code rows of code_stride bytes;  scales  fp32, one per code row
  *   seq_offsets, num_splits, split_rows, partial_dtype, o_part, lse_part  as mla_decode
- * The codes widen exactly to bf16 MFMA operands; the row scale multiplies the fp32
+ * Scores: the codes are E4M3 MFMA operands as stored; each head's bf16 query is scaled by a
+ * power of two and split into two E4M3 parts whose sum is exact for every component above
+ * 2^-10 of the head's largest.  The E4M3 MFMA adds its products with about 13 bits below
+ * the largest of each group of 8 (logit error a few 1e-5 at DeepSeek-V2 scale).  Weighted
+ * sum: the codes widen exactly to bf16 MFMA operands.  The row scale multiplies the fp32
  * scores and is folded into each softmax weight before that weight's rounding to bf16.
  * Needs d_c == 512, d_r == 64, n_h % 32 == 0 (else MLA_ERR_UNSUPPORTED); codes, q_abs and
  * o_part 16-byte aligned, code_stride a multiple of 16, scales 4-byte aligned.

@@ -5,8 +5,10 @@ Quantization decides integer codes, so codes and scales must equal the oracle's 
 decode's bounds against the oracle's decode over the dequantized rows (m = max|ref|):
   o     max|o - o_ref| <= 1e-2 * m + 1e-3
   lse   |d lse| <= 1e-3 for one call on given queries; the o bound end to end
-The codes widen exactly to bf16, so the only roundings beyond the bf16 decode's are the
-fp32 products by the row scales.
+Beyond the bf16 decode's roundings: the scores come from the E4M3 MFMA on the codes and
+an exact-to-2^-10 two-part E4M3 split of each head's query, whose products the MFMA adds
+with about 13 bits below the largest of each group of 8 (a few 1e-5 in the logits here);
+the weighted sum widens the codes exactly to bf16; the row scales multiply in fp32.
 
 Every GPU step first prints the case it runs.
 """
