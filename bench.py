@@ -31,6 +31,9 @@ if ROOT not in sys.path:
 
 METRIC = "MLA decode cached-latent-tokens/s on 1 GPU; % of HBM BW and bf16 MFMA peak"
 UNIT = "cached-latent-tokens/s"
+# prefill workloads (no cached rows: T_q = T_k, causal) count the prompt tokens instead
+PREFILL_METRIC = "MLA prefill tokens/s on 1 GPU (absorbed form, causal); % of bf16 MFMA peak"
+PREFILL_UNIT = "prefill-tokens/s"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 ROW_BYTES = 1152               # one cached latent row [c_KV 512 ; k_R 64] in bf16
@@ -92,14 +95,15 @@ def cpu_baseline(w, budget_s: float):
             heads += 1
             if time.perf_counter() - t0 > budget_s:
                 break
-        covered += (hi - lo - appended) * heads / w.n_h
+        covered += (hi - lo - appended if w.cached_rows() else w.q_per_seq) * heads / w.n_h
         seqs, heads_last = b + 1, heads
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": covered / dt, "unit": UNIT, "cores": int(threads), "kind": "oracle",
+    return {"value": covered / dt, "unit": UNIT if w.cached_rows() else PREFILL_UNIT, "cores": int(threads), "kind": "oracle",
             "sample": f"sequences 0..{seqs - 1} of {w.batch} in order ({heads_last} of {w.n_h} heads of "
-                      f"the last), naive fp64 form (materialized k^C, v^C), {covered:.0f} cached rows "
+                      f"the last), naive fp64 form (materialized k^C, v^C), {covered:.0f} "
+                      f"{'cached rows' if w.cached_rows() else 'prompt tokens'} "
                       f"in {dt:.1f} s; tokens/s over that sample"}
 
 
@@ -240,7 +244,9 @@ def main():
         graph_ms = g0.elapsed_time(g1) / K
     ms_per_step = graph_ms
     cached = w.cached_rows()
-    value = cached / (ms_per_step * 1e-3)
+    prefill = cached == 0
+    tokens = w.n_q if prefill else cached          # the unit of every rate below
+    value = tokens / (ms_per_step * 1e-3)
 
     # Each kernel alone: launches over the layer copies captured as one HIP graph and replayed,
     # so the mean is GPU time per launch (dispatch gaps included, no host launch cost).  The
@@ -354,7 +360,8 @@ def main():
     roof["algorithmic_flop_per_launch"] = flops
 
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1, "steps": K,
+        "metric": PREFILL_METRIC if prefill else METRIC, "value": round(value, 1),
+        "unit": PREFILL_UNIT if prefill else UNIT, "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == W.BF16 else "f32",
         "data": "synthetic (seeded Gaussian latent cache, DeepSeek-V2 attention dims, random weights)",
@@ -371,8 +378,8 @@ def main():
                                                        + n_q * (w.d_c + w.d_r) * esz + 16 * n_q)
                                                       / (per["kv_append"] * 1e-3) / 1e9, 1)},
                       "absorb_q_rope_ms": round(per["absorb_q_rope"], 5)} if prologue else None),
-        "fp8_cache": (fp8_summary(w, per, flops, cached, fcopies) if fp8 else None),
-        "decode_merge_tokens_per_s": round(cached / ((dec_ms + per.get("merge", 0.0)) * 1e-3), 1),
+        "fp8_cache": (fp8_summary(w, per, flops, tokens, fcopies) if fp8 else None),
+        "decode_merge_tokens_per_s": round(tokens / ((dec_ms + per.get("merge", 0.0)) * 1e-3), 1),
         "timing": "hip graph replay (one graph per pass over the layer copies)" if not args.no_graph else "eager launches",
         "step_calls": "absorb_q, decode, merge_out_proj" if fused else "absorb_q, decode, merge_splits, out_proj",
         "mfma_frac_decode": round(flops / (dec_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

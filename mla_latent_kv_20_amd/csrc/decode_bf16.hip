@@ -164,7 +164,10 @@ mla_decode_bf16_kernel(DecodeParams P) {
   // XCD L % 8), and the members of a stream (query tokens, head groups: same rows) run
   // side by side on one XCD, as do the splits of one sequence (one L2 fetch of its
   // queries).
-  //  - Few sequences: XCD x takes the contiguous stream range [x * streams_per_xcd, ...).
+  //  - Fewer than 8 streams (a long prefill, a few sequences): (stream, member) items are
+  //    dealt round-robin over the XCDs, so that all eight work.
+  //  - Otherwise, with fewer than 16 sequences: XCD x takes the contiguous stream range
+  //    [x * streams_per_xcd, ...).
   //  - seqs_per_xcd > 0 (16 or more sequences): every workgroup ranks the sequences by
   //    length (longest first, ties by index) and XCD x takes ranks x, 15-x, 16+x, 31-x, ...
   //    (snake order), longest first.  Every XCD then gets the same number of sequences
@@ -175,12 +178,20 @@ mla_decode_bf16_kernel(DecodeParams P) {
   const int L = blockIdx.x;
   const int xcd = L & 7;
   const int k = L >> 3;
-  const int member = k % P.group_size;
+  int member = k % P.group_size;
   const int j = k / P.group_size;
-  if (j >= P.streams_per_xcd) return;
+  if (P.streams >= 8 && j >= P.streams_per_xcd) return;
   int b, s;
   int used_splits = P.num_splits;                  // splits of sequence b that hold rows
-  if (P.seqs_per_xcd > 0) {
+  if (P.streams < 8) {
+    // fewer streams than XCDs (one long prefill, a few sequences): (stream, member) items
+    // dealt round-robin over the XCDs, so that every XCD works
+    const int stream = L / P.group_size;
+    if (stream >= P.streams) return;
+    member = L - stream * P.group_size;
+    b = stream / P.num_splits;
+    s = stream - b * P.num_splits;
+  } else if (P.seqs_per_xcd > 0) {
     // lengths in LDS (free until the first loads), padded to a multiple of 4 with -1,
     // which ranks below every length
     const int bpad = (P.batch + 3) & ~3;
@@ -229,7 +240,9 @@ mla_decode_bf16_kernel(DecodeParams P) {
     s = stream - b * P.num_splits;
   }
   const int hg = member % P.head_groups;
-  const int r = member / P.head_groups;
+  // a stream's queries latest first: under a causal mask they see the most rows, so the
+  // longest items start first
+  const int r = P.q_per_seq - 1 - member / P.head_groups;
   const int n = b * P.q_per_seq + r;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -540,7 +553,8 @@ hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* rows, int
     P.seqs_per_xcd = 0;
     P.streams_per_xcd = (P.streams + 7) / 8;
   }
-  const long long grid = (long long)P.streams_per_xcd * 8 * P.group_size;
+  const long long grid = P.streams < 8 ? (long long)P.streams * P.group_size
+                                        : (long long)P.streams_per_xcd * 8 * P.group_size;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // Dynamic LDS above 64 KiB must be allowed once per kernel (thread-safe static init).
   static const hipError_t attr32 = hipFuncSetAttribute(

@@ -222,17 +222,26 @@ __global__ void __launch_bounds__(kThreads, 1)
 mla_decode_fp8_kernel(DecodeParams P) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-  // ---- work item: as the bf16 decode (round-robin XCDs; streams of one sequence on one
-  // XCD; with 16 or more sequences, length-ranked snake order and only non-empty splits).
+  // ---- work item: as the bf16 decode (round-robin XCDs; fewer than 8 streams: items dealt
+  // round-robin; else streams of one sequence on one XCD; with 16 or more sequences,
+  // length-ranked snake order and only non-empty splits).
   const int L = blockIdx.x;
   const int xcd = L & 7;
   const int k = L >> 3;
-  const int member = k % P.group_size;
+  int member = k % P.group_size;
   const int j = k / P.group_size;
-  if (j >= P.streams_per_xcd) return;
+  if (P.streams >= 8 && j >= P.streams_per_xcd) return;
   int b, s;
   int used_splits = P.num_splits;
-  if (P.seqs_per_xcd > 0) {
+  if (P.streams < 8) {
+    // fewer streams than XCDs (one long prefill, a few sequences): (stream, member) items
+    // dealt round-robin over the XCDs, so that every XCD works
+    const int stream = L / P.group_size;
+    if (stream >= P.streams) return;
+    member = L - stream * P.group_size;
+    b = stream / P.num_splits;
+    s = stream - b * P.num_splits;
+  } else if (P.seqs_per_xcd > 0) {
     const int bpad = (P.batch + 3) & ~3;
     int* lens = (int*)smem;
     int* by_rank = lens + bpad;
@@ -278,7 +287,9 @@ mla_decode_fp8_kernel(DecodeParams P) {
     s = stream - b * P.num_splits;
   }
   const int hg = member % P.head_groups;
-  const int r = member / P.head_groups;
+  // a stream's queries latest first: under a causal mask they see the most rows, so the
+  // longest items start first
+  const int r = P.q_per_seq - 1 - member / P.head_groups;
   const int n = b * P.q_per_seq + r;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -583,7 +594,8 @@ hipError_t launch_decode_fp8(const bf16_bits* q_abs, const uint8_t* codes, int64
     P.seqs_per_xcd = 0;
     P.streams_per_xcd = (P.streams + 7) / 8;
   }
-  const long long grid = (long long)P.streams_per_xcd * 8 * P.group_size;
+  const long long grid = P.streams < 8 ? (long long)P.streams * P.group_size
+                                        : (long long)P.streams_per_xcd * 8 * P.group_size;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   static const hipError_t attr32 = hipFuncSetAttribute(
       (const void*)mla_decode_fp8_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);

@@ -306,6 +306,16 @@ CONFIGS: Dict[str, tuple] = {
         "DeepSeek-V2 dims, B=64, T=8192 cached + 4 new rows, 4 queries/seq, causal among new, bf16",
         dict(**DSV2, dtype=BF16, lengths=[8192] * 64, q_per_seq=4, appended_rows=True,
              num_splits=1, split_rows=0)),
+    # prefill (T_q = T_k, causal): every row is a new token's own row and query r sees rows
+    # 0..r, the generalized mask with no cached rows
+    "dsv2_prefill_b1_t4096": (
+        "DeepSeek-V2 dims, prefill of one 4096-token sequence (causal), bf16",
+        dict(**DSV2, dtype=BF16, lengths=[0], q_per_seq=4096, appended_rows=True,
+             num_splits=1, split_rows=0)),
+    "dsv2_prefill_small": (
+        "DeepSeek-V2 dims, prefill of two 83-token sequences (causal), bf16",
+        dict(**DSV2, dtype=BF16, lengths=[0, 0], q_per_seq=83, appended_rows=True,
+             num_splits=2, split_rows=48)),
     # extra shapes (not measured): the toy module dims of "MLA(Multi-head Latent Attention):
     # DeepSeek-V2 논문정리" section "MLA 코드 구현", and small DeepSeek-V2-shaped caches
     "toy_p3": (

@@ -82,3 +82,15 @@ def test_logit_std_matches_the_workload_description(q_mult, lo, hi):
 def test_tiny_config_logit_std_near_one():
     s = _logits(W.make_config("tiny_f32"))
     assert 0.7 <= s.std() <= 1.3
+
+
+def test_prefill_layout():
+    """Prefill: no cached rows, T new rows per sequence at positions 0..T-1, query r at
+    position r, so the generalized mask gives query r rows 0..r."""
+    import oracle as O
+    w = W.make_config("dsv2_prefill_small")
+    assert w.batch == 2 and w.q_per_seq == 83 and w.cached_rows() == 0
+    assert list(w.offsets) == [0, 83, 166] and w.n_q == 166
+    for b in range(2):
+        for r in (0, 1, 47, 82):
+            assert O.visible_rows(int(w.lengths[b]), w.q_per_seq, r) == r + 1
