@@ -190,6 +190,9 @@ def main():
         qa = B.absorb_q(d, L["q_c"], L["q_r"], L["w_uk"], bufs["q_abs"])
         op, lp = B.decode(d, qa, L["cache"][:, :w.d_c], L["cache"][:, w.d_c:], L["offsets"], w.batch,
                           w.q_per_seq, S, R, bufs["o_part"], bufs["lse_part"])
+        if S == 1 and part == B.MLA_F32:        # one fp32 split: the decode's output is final
+            B.out_proj(d, op[0], L["w_uv"], bufs["o_c"])
+            return
         if fused:
             B.merge_out_proj(d, op, lp, L["w_uv"], bufs["o_c"], bufs["lse"], None)
             return
@@ -306,7 +309,10 @@ def main():
             qa = B.absorb_q(d, L["q_c"], L["q_r"], L["w_uk"], bufs["q_abs"])
             op, lp = B.decode_fp8(d, qa, fp8_sets[j][0], fp8_sets[j][1], L["offsets"], w.batch, w.q_per_seq,
                                   S, R, bufs["o_part"], bufs["lse_part"])
-            B.merge_out_proj(d, op, lp, L["w_uv"], bufs["o_c"], bufs["lse"], None)
+            if S == 1 and part == B.MLA_F32:
+                B.out_proj(d, op[0], L["w_uv"], bufs["o_c"])
+            else:
+                B.merge_out_proj(d, op, lp, L["w_uv"], bufs["o_c"], bufs["lse"], None)
 
         calls["decode_fp8"] = (fcopies, fp8_decode)
         calls["step_fp8"] = (fcopies, fp8_step)
@@ -381,7 +387,8 @@ def main():
         "fp8_cache": (fp8_summary(w, per, flops, tokens, fcopies) if fp8 else None),
         "decode_merge_tokens_per_s": round(tokens / ((dec_ms + per.get("merge", 0.0)) * 1e-3), 1),
         "timing": "hip graph replay (one graph per pass over the layer copies)" if not args.no_graph else "eager launches",
-        "step_calls": "absorb_q, decode, merge_out_proj" if fused else "absorb_q, decode, merge_splits, out_proj",
+        "step_calls": ("absorb_q, decode, out_proj (one fp32 split: no merge)" if S == 1 and part == B.MLA_F32
+                       else "absorb_q, decode, merge_out_proj" if fused else "absorb_q, decode, merge_splits, out_proj"),
         "mfma_frac_decode": round(flops / (dec_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
     }
