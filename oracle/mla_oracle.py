@@ -254,8 +254,36 @@ def absorbed_decode(c_kv, k_r, offsets, q_c, q_r, w_uk, w_uv, q_per_seq: int,
 # Helpers for the pages' side claims
 # ----------------------------------------------------------------------------
 
-def rope_pairs(x, positions, theta: float = 10000.0) -> np.ndarray:
-    """RoPE as a complex rotation of the pairs (x_k, x_{k+d/2}) by angle pos * theta^(-2k/d).
+def rope_frequencies(d: int, theta: float = 10000.0, yarn: Optional[dict] = None) -> np.ndarray:
+    """Per-position angle of each rotate-half pair k < d/2: theta^(-2k/d) ([notes] "MLA 코드
+    구현"), or with yarn = dict(factor=s, original_len=L, alpha=a, beta=b) YaRN's NTK-by-parts
+    ([report] training and infrastructure section: each frequency pair is scaled by the number
+    of turns it makes over the training length; DeepSeek-V2: s = 40, a = 1, b = 32).  Reading
+    taken where the page is brief: a pair making r = L f / (2 pi) turns over L keeps f when
+    r >= b, is interpolated to f / s when r <= a, and between the two the frequency is the
+    linear blend of f / s and f with weight (r - a) / (b - a) on f."""
+    k = np.arange(d // 2, dtype=np.float64)
+    f = np.power(float(theta), -2.0 * k / d)
+    if yarn is None or yarn["factor"] <= 1.0:
+        return f
+    turns = yarn["original_len"] * f / (2.0 * math.pi)
+    g = np.clip((turns - yarn["alpha"]) / (yarn["beta"] - yarn["alpha"]), 0.0, 1.0)
+    return (1.0 - g) * f / yarn["factor"] + g * f
+
+
+def yarn_softmax_scale(d_h: int, d_r: int, yarn: Optional[dict] = None) -> float:
+    """1/sqrt(d_h + d_h^R) times YaRN's length factor t, sqrt(t) = mscale * ln s + 1 ([report]
+    training and infrastructure section: DeepSeek-V2 takes mscale = 0.0707).  Reading: t
+    multiplies every logit."""
+    base = default_scale(d_h, d_r)
+    if yarn is None or yarn["factor"] <= 1.0:
+        return base
+    return base * (yarn["mscale"] * math.log(yarn["factor"]) + 1.0) ** 2
+
+
+def rope_pairs(x, positions, theta: float = 10000.0, yarn: Optional[dict] = None) -> np.ndarray:
+    """RoPE as a complex rotation of the pairs (x_k, x_{k+d/2}) by angle pos * f_k
+    (rope_frequencies).
 
     Same rotate-half convention as the helpers in [notes] "MLA 코드 구현", written as complex
     multiplication so that it shares no arithmetic with any other implementation.
@@ -264,8 +292,7 @@ def rope_pairs(x, positions, theta: float = 10000.0) -> np.ndarray:
     d = x.shape[-1]
     h = d // 2
     z = x[..., :h] + 1j * x[..., h:]
-    k = np.arange(h, dtype=np.float64)
-    ang = np.asarray(positions, np.float64)[..., None] * np.power(theta, -2.0 * k / d)
+    ang = np.asarray(positions, np.float64)[..., None] * rope_frequencies(d, theta, yarn)
     z = z * np.exp(1j * ang)
     return np.concatenate([z.real, z.imag], axis=-1)
 
@@ -274,7 +301,7 @@ def rope_pairs(x, positions, theta: float = 10000.0) -> np.ndarray:
 # Decode prologue: the new tokens' latent rows and the rotated query part
 # ----------------------------------------------------------------------------
 
-def kv_prologue(h, w_dkv, w_kr, positions, theta: float = 10000.0):
+def kv_prologue(h, w_dkv, w_kr, positions, theta: float = 10000.0, yarn: Optional[dict] = None):
     """Latent row of each new token: c^KV = W^DKV h ([notes] eq. 9) and the decoupled RoPE
     key k^R = RoPE(W^KR h) at the token's position ([notes] "Decoupled Rotary Position
     Embedding", items 2-3; "MLA 코드 구현": the down-projections and the rotation apply to the
@@ -285,7 +312,7 @@ def kv_prologue(h, w_dkv, w_kr, positions, theta: float = 10000.0):
     """
     h = np.asarray(h, np.float64)
     c_kv = h @ np.asarray(w_dkv, np.float64).T
-    k_r = rope_pairs(h @ np.asarray(w_kr, np.float64).T, np.asarray(positions), theta)
+    k_r = rope_pairs(h @ np.asarray(w_kr, np.float64).T, np.asarray(positions), theta, yarn)
     return c_kv, k_r
 
 
@@ -303,11 +330,12 @@ def append_rows(rows, dst_rows, c_kv, k_r) -> np.ndarray:
     return out
 
 
-def absorb_q_rope(q_c, q_r_raw, w_uk, positions, theta: float = 10000.0) -> np.ndarray:
+def absorb_q_rope(q_c, q_r_raw, w_uk, positions, theta: float = 10000.0,
+                  yarn: Optional[dict] = None) -> np.ndarray:
     """absorb_q with every head's RoPE part rotated at its token's position first ([notes]
     "MLA 코드 구현": q^R is rotated head by head at the new tokens' positions; "Decoupled
     Rotary Position Embedding", item 1).  positions [n_q]."""
-    q_r = rope_pairs(np.asarray(q_r_raw, np.float64), np.asarray(positions)[:, None], theta)
+    q_r = rope_pairs(np.asarray(q_r_raw, np.float64), np.asarray(positions)[:, None], theta, yarn)
     return absorb_q(q_c, q_r, w_uk)
 
 

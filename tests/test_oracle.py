@@ -594,6 +594,86 @@ def test_prologue_then_decode_depends_only_on_relative_positions():
 
 
 # ----------------------------------------------------------------------------
+# YaRN (long-context RoPE on the decoupled key and query)
+# ----------------------------------------------------------------------------
+
+YARN_DSV2 = dict(factor=40.0, original_len=4096, alpha=1.0, beta=32.0, mscale=0.0707)
+
+
+def _yarn_regime_pins(freq_fn):
+    """The three regimes at DeepSeek-V2's parameters, from each pair's turns over the 4096
+    training positions written out in closed form: >= 32 turns keep the frequency, <= 1 turn
+    divides it by 40, in between it lies strictly between and grows with the turns."""
+    d = 64
+    base = [10000.0 ** (-2.0 * k / d) for k in range(d // 2)]
+    turns = [4096 * b / (2 * math.pi) for b in base]
+    got = freq_fn(d)
+    mid = []
+    for k in range(d // 2):
+        if turns[k] >= 32:
+            assert abs(got[k] - base[k]) <= 1e-15 * base[k], k
+        elif turns[k] <= 1:
+            assert abs(got[k] - base[k] / 40) <= 1e-15 * base[k], k
+        else:
+            assert base[k] / 40 < got[k] < base[k], k
+            mid.append(got[k] / base[k])
+    assert len(mid) >= 3 and all(a > b for a, b in zip(mid, mid[1:]))   # ratio falls with the turns
+
+
+def test_yarn_frequency_regimes():
+    _yarn_regime_pins(lambda d: O.rope_frequencies(d, 10000.0, YARN_DSV2))
+
+
+def test_yarn_off_is_plain_rope():
+    x = np.random.default_rng(61).standard_normal((5, 64))
+    pos = np.array([0, 3, 4096, 70000, 131071])
+    for off in (None, dict(YARN_DSV2, factor=1.0)):
+        assert np.array_equal(O.rope_pairs(x, pos[:, None], yarn=off), O.rope_pairs(x, pos[:, None]))
+    assert O.yarn_softmax_scale(128, 64, None) == O.default_scale(128, 64)
+
+
+def test_yarn_rope_stays_relative_and_norm_preserving():
+    rng = np.random.default_rng(63)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    y = YARN_DSV2
+    a = O.rope_pairs(q, 150000, yarn=y) @ O.rope_pairs(k, 149000, yarn=y)
+    b = O.rope_pairs(q, 1000, yarn=y) @ O.rope_pairs(k, 0, yarn=y)
+    assert abs(a - b) <= 1e-9 * (np.linalg.norm(q) * np.linalg.norm(k))
+    assert abs(np.linalg.norm(O.rope_pairs(q, 123457, yarn=y)) - np.linalg.norm(q)) <= 1e-12 * np.linalg.norm(q)
+
+
+def test_yarn_length_factor_as_printed():
+    """sqrt(t) = 0.0707 ln s + 1 ([report] training and infrastructure section), t on the logits."""
+    base = O.default_scale(128, 64)
+    s_two = math.exp(1.0 / 0.0707)                                   # sqrt(t) = 2, t = 4
+    assert abs(O.yarn_softmax_scale(128, 64, dict(YARN_DSV2, factor=s_two)) - 4.0 * base) <= 1e-12 * base
+    t40 = O.yarn_softmax_scale(128, 64, YARN_DSV2) / base
+    assert 1.58 < t40 < 1.60                                         # (0.0707 ln 40 + 1)^2 = 1.5896
+
+
+@pytest.mark.parametrize("mutant", ["ramp_inverted", "all_interpolated", "turns_without_two_pi",
+                                    "alpha_beta_swapped"])
+def test_planted_yarn_mistakes_are_caught(mutant):
+    def freq(d):
+        k = np.arange(d // 2, dtype=np.float64)
+        f = np.power(10000.0, -2.0 * k / d)
+        turns = 4096 * f / (2 * math.pi)
+        a, b = 1.0, 32.0
+        if mutant == "turns_without_two_pi":
+            turns = 4096 * f
+        if mutant == "alpha_beta_swapped":
+            a, b = b, a
+        g = np.clip((turns - a) / (b - a), 0.0, 1.0)
+        if mutant == "ramp_inverted":
+            g = 1.0 - g
+        if mutant == "all_interpolated":
+            g = np.zeros_like(g)
+        return (1.0 - g) * f / 40.0 + g * f
+    with pytest.raises(AssertionError):
+        _yarn_regime_pins(freq)
+
+
+# ----------------------------------------------------------------------------
 # Quantized latent cache: E4M3 codes with one scale per row
 # ----------------------------------------------------------------------------
 
