@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 5
+#define MLA_ABI_VERSION 6
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -94,6 +94,28 @@ typedef struct mla_dims {
   int32_t dtype;            /* mla_dtype_t of every non-fp32 tensor below */
   float softmax_scale;      /* > 0: used as given; <= 0: 1/sqrt(d_h + d_r) */
 } mla_dims_t;
+
+/* RoPE of the decoupled key and query (mla_kv_append, mla_absorb_q_rope).  Pair k of a
+ * d_r-wide vector turns by f_k = theta^(-2k/d_r) per position ([notes] "MLA 코드 구현").
+ * With yarn_factor s > 1 the frequencies follow YaRN's NTK-by-parts, which DeepSeek-V2 applies
+ * to the decoupled key only ([report] training and infrastructure section: s = 40, alpha = 1,
+ * beta = 32; [review] section 4): a pair that makes r = L f_k / (2 pi) turns over the
+ * training length L keeps f_k when r >= beta, turns at f_k / s when r <= alpha, and at
+ * (1 - g) f_k / s + g f_k, g = (r - alpha) / (beta - alpha), in between.  The logits' length
+ * factor t, sqrt(t) = yarn_mscale * ln s + 1 (DeepSeek-V2: 0.0707), multiplies the softmax
+ * scale: mla_rope_softmax_scale gives the value for mla_dims_t.softmax_scale. */
+typedef struct mla_rope {
+  float theta;              /* > 0: the base; <= 0: 10000 */
+  float yarn_factor;        /* s; <= 1: plain RoPE (the other YaRN fields are ignored) */
+  int32_t yarn_original_len;/* L, the training length (DeepSeek-V2: 4096); > 0 with s > 1 */
+  float yarn_alpha;         /* alpha (1) */
+  float yarn_beta;          /* beta (32); > alpha with s > 1 */
+  float yarn_mscale;        /* coefficient of ln s in sqrt(t) (0.0707) */
+} mla_rope_t;
+
+/* Softmax scale with YaRN's length factor: (dims->softmax_scale > 0 ? it : 1/sqrt(d_h + d_r))
+ * * t, t = (yarn_mscale * ln s + 1)^2 for s > 1, else 1.  NULL dims: 0; NULL rope: no factor. */
+float mla_rope_softmax_scale(const mla_dims_t* dims, const mla_rope_t* rope);
 
 /* Library ABI version (MLA_ABI_VERSION of the build). */
 int32_t mla_abi_version(void);
@@ -127,14 +149,14 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t n_q,
  *
  *   q_r_raw    [n_q, n_h, d_r]   dtype   per-head RoPE query before rotation
  *   positions  [n_q] int64, device memory: each query token's position
- *   rope_theta > 0: the RoPE base; <= 0: 10000
+ *   rope       RoPE parameters (mla_rope_t), or NULL: theta = 10000, no YaRN
  * Other arguments and errors as mla_absorb_q; positions must be 8-byte aligned
  * and non-NULL (MLA_ERR_NULL); bf16 needs d_r <= 512.  The angle is fp64, reduced
  * to [-pi, pi] in fp64; its sine and cosine are fp32 (relative error ~1e-7).
  */
 mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t n_q, const void* q_c,
                                const void* q_r_raw, const void* w_uk, const int64_t* positions,
-                               float rope_theta, void* q_abs, hipStream_t stream);
+                               const mla_rope_t* rope, void* q_abs, hipStream_t stream);
 
 /*
  * mla_kv_append - the new tokens' latent rows, written into the cache ([notes]
@@ -145,7 +167,7 @@ mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t n_q, const void* 
  *   rows[dst_rows[t] * stride + 0 : d_c]         = c^KV_t
  *   rows[dst_rows[t] * stride + d_c : d_c + d_r] = k^R_t
  * RoPE rotates the pairs (v_k, v_{k+d_r/2}), k < d_r/2, by the angle
- * positions[t] * theta^(-2k/d_r): (v_k cos - v_{k+d_r/2} sin, v_{k+d_r/2} cos + v_k sin),
+ * positions[t] * f_k (mla_rope_t): (v_k cos - v_{k+d_r/2} sin, v_{k+d_r/2} cos + v_k sin),
  * the rotate-half form of the listing in "MLA 코드 구현"; the angle is fp64, reduced
  * to [-pi, pi] in fp64, with fp32 sine and cosine and an fp64 rotation (relative error
  * ~1e-7).  No other cache element is touched.
@@ -157,7 +179,7 @@ mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t n_q, const void* 
  *   dst_rows   [n_new] int64, device memory: each token's cache row; distinct rows,
  *              each below the number of rows behind `rows` (not checked)
  *   rows       cache rows [*, stride] in dtype, packed [c^KV | k^R] (stride >= d_c + d_r)
- *   rope_theta > 0: the RoPE base; <= 0: 10000
+ *   rope       RoPE parameters (mla_rope_t), or NULL: theta = 10000, no YaRN
  *   workspace  device scratch of at least mla_kv_append_workspace_bytes(dims, n_new)
  *              bytes (bf16: fp32 partial sums over slices of d_model; fp32 needs none and
  *              may pass NULL, 0); its contents on entry do not matter, on return they are
@@ -166,12 +188,14 @@ mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t n_q, const void* 
  * rounded once to bf16 (the k^R outputs after the rotation of the fp32 sums);
  * needs d_model % 512 == 0, d_model <= 8192, (d_c + d_r) % 32 == 0 (else
  * MLA_ERR_UNSUPPORTED) and 16-byte aligned h, w_dkv and w_kr.  fp32: any shape.
- * positions and dst_rows 8-byte aligned, workspace 4-byte aligned.
+ * positions and dst_rows 8-byte aligned, workspace 4-byte aligned.  A rope with s > 1 needs
+ * yarn_original_len > 0 and yarn_beta > yarn_alpha, all finite (else MLA_ERR_SHAPE); the same
+ * holds for mla_absorb_q_rope.
  */
 size_t mla_kv_append_workspace_bytes(const mla_dims_t* dims, int32_t n_new);
 mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t n_new, int32_t d_model, const void* h,
                            const void* w_dkv, const void* w_kr, const int64_t* positions,
-                           const int64_t* dst_rows, void* rows, int64_t stride, float rope_theta,
+                           const int64_t* dst_rows, void* rows, int64_t stride, const mla_rope_t* rope,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*

@@ -36,7 +36,19 @@ class MlaDims(ctypes.Structure):
                 ("softmax_scale", _F32)]
 
 
+class MlaRope(ctypes.Structure):
+    _fields_ = [("theta", _F32), ("yarn_factor", _F32), ("yarn_original_len", _I32), ("yarn_alpha", _F32),
+                ("yarn_beta", _F32), ("yarn_mscale", _F32)]
+
+
+def rope(theta: float = 10000.0, yarn_factor: float = 0.0, yarn_original_len: int = 4096,
+         yarn_alpha: float = 1.0, yarn_beta: float = 32.0, yarn_mscale: float = 0.0707) -> MlaRope:
+    """RoPE parameters; the YaRN defaults are DeepSeek-V2's (yarn_factor 40 turns them on)."""
+    return MlaRope(theta, yarn_factor, yarn_original_len, yarn_alpha, yarn_beta, yarn_mscale)
+
+
 _DIMS_P = ctypes.POINTER(MlaDims)
+_ROPE_P = ctypes.POINTER(MlaRope)
 SIGNATURES = {
     "mla_abi_version": (_I32, []),
     "mla_status_string": (ctypes.c_char_p, [_I32]),
@@ -47,8 +59,9 @@ SIGNATURES = {
     "mla_merge_splits": (_I32, [_DIMS_P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "mla_out_proj": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P]),
     "mla_merge_out_proj": (_I32, [_DIMS_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]),
-    "mla_absorb_q_rope": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P, ctypes.c_float, _P, _P]),
-    "mla_kv_append": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _I64, ctypes.c_float, _P, _SZ, _P]),
+    "mla_absorb_q_rope": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P, _ROPE_P, _P, _P]),
+    "mla_kv_append": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _I64, _ROPE_P, _P, _SZ, _P]),
+    "mla_rope_softmax_scale": (_F32, [_DIMS_P, _ROPE_P]),
     "mla_kv_append_workspace_bytes": (_SZ, [_DIMS_P, _I32]),
     "mla_quantize_rows_fp8": (_I32, [_DIMS_P, _I64, _P, _I64, _P, _P, _I64, _P, _P]),
     "mla_decode_fp8": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _P, _P, _P]),
@@ -141,15 +154,17 @@ def absorb_q(d: MlaDims, q_c, q_r, w_uk, q_abs=None, stream=None):
     return q_abs
 
 
-def absorb_q_rope(d: MlaDims, q_c, q_r_raw, w_uk, positions, q_abs=None, rope_theta: float = 10000.0,
+def absorb_q_rope(d: MlaDims, q_c, q_r_raw, w_uk, positions, q_abs=None, rope: Optional[MlaRope] = None,
                   stream=None):
-    """q_abs[n, i] = [W^UK_i^T q_c[n, i] ; RoPE(q_r_raw[n, i], positions[n])]."""
+    """q_abs[n, i] = [W^UK_i^T q_c[n, i] ; RoPE(q_r_raw[n, i], positions[n])] (rope: MlaRope or
+    None for theta 10000 without YaRN)."""
     import torch
     n_q = q_c.shape[0]
     if q_abs is None:
         q_abs = torch.empty((n_q, d.n_h, d.d_c + d.d_r), dtype=q_c.dtype, device=q_c.device)
     _check("mla_absorb_q_rope", load().mla_absorb_q_rope(ctypes.byref(d), n_q, _ptr(q_c), _ptr(q_r_raw),
-                                                          _ptr(w_uk), _ptr(positions), float(rope_theta),
+                                                          _ptr(w_uk), _ptr(positions),
+                                                          ctypes.byref(rope) if rope is not None else None,
                                                           _ptr(q_abs), _stream(stream)))
     return q_abs
 
@@ -158,7 +173,7 @@ def kv_append_workspace_bytes(d: MlaDims, n_new: int) -> int:
     return int(load().mla_kv_append_workspace_bytes(ctypes.byref(d), n_new))
 
 
-def kv_append(d: MlaDims, h, w_dkv, w_kr, positions, dst_rows, rows, rope_theta: float = 10000.0,
+def kv_append(d: MlaDims, h, w_dkv, w_kr, positions, dst_rows, rows, rope: Optional[MlaRope] = None,
               workspace=None, stream=None):
     """Write [W^DKV h_t ; RoPE(W^KR h_t, positions[t])] into cache row dst_rows[t] of `rows`
     ([*, stride] tensor, stride = rows.stride(0)); returns rows.  The workspace (bytes from
@@ -171,7 +186,7 @@ def kv_append(d: MlaDims, h, w_dkv, w_kr, positions, dst_rows, rows, rope_theta:
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("mla_kv_append", load().mla_kv_append(ctypes.byref(d), n_new, d_model, _ptr(h), _ptr(w_dkv),
                                                   _ptr(w_kr), _ptr(positions), _ptr(dst_rows), _ptr(rows),
-                                                  rows.stride(0), float(rope_theta),
+                                                  rows.stride(0), ctypes.byref(rope) if rope is not None else None,
                                                   _ptr(workspace) if workspace is not None else None,
                                                   ws_bytes, _stream(stream)))
     return rows
@@ -322,6 +337,11 @@ def decode_step(d: MlaDims, q_c, q_r, w_uk, w_uv, cache, offsets, batch: int, q_
         o_lat, lse = merge_splits(d, o_part, lse_part, b.get("o_lat"), b.get("lse"), stream)
     o_c = out_proj(d, o_lat, w_uv, b.get("o_c"), stream=stream)
     return dict(q_abs=q_abs, o_part=o_part, lse_part=lse_part, o_lat=o_lat, lse=lse, o_c=o_c)
+
+
+def rope_softmax_scale(d: MlaDims, rope: Optional[MlaRope] = None) -> float:
+    """The softmax scale with YaRN's length factor (mla_rope_softmax_scale)."""
+    return float(load().mla_rope_softmax_scale(ctypes.byref(d), ctypes.byref(rope) if rope is not None else None))
 
 
 def default_scale(d_h: int, d_r: int) -> float:

@@ -37,7 +37,7 @@ struct AbsorbParams {
   bf16_bits* q_abs;       // [n_q, n_h, d_c + d_r]
   int n_q, n_h, d_h, d_c, d_r;
   const int64_t* pos;     // [n_q] token positions: rotate q_r there first; null: copy q_r as is
-  double log_theta;       // ln(RoPE theta)
+  RopeSpec rope;
 };
 
 __global__ void __launch_bounds__(kThreads)
@@ -178,7 +178,7 @@ absorb_q_bf16_kernel(AbsorbParams P) {
     const int slots = kThreads / half;            // query slots per pair index (d_r <= 512)
     if (tid < half * slots) {
       const int k = tid % half;
-      const double inv = rope_inv_freq(k, P.d_r, P.log_theta);
+      const double inv = rope_inv_freq(k, P.d_r, P.rope);
       for (int n = tid / half; n < P.n_q; n += slots) {
         const bf16_bits* src = P.q_r + ((size_t)n * P.n_h + i) * P.d_r;
         double x = bf16_to_f32(src[k]);
@@ -282,8 +282,8 @@ bool out_proj_bf16_supported(int d_h, int d_c) {
 
 hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, const bf16_bits* w_uk,
                                 bf16_bits* q_abs, int n_q, int n_h, int d_h, int d_c, int d_r,
-                                const int64_t* positions, double theta, hipStream_t stream) {
-  AbsorbParams P{q_c, q_r, w_uk, q_abs, n_q, n_h, d_h, d_c, d_r, positions, positions ? log(theta) : 0.0};
+                                const int64_t* positions, const RopeSpec& rope, hipStream_t stream) {
+  AbsorbParams P{q_c, q_r, w_uk, q_abs, n_q, n_h, d_h, d_c, d_r, positions, rope};
   const size_t smem = (size_t)d_h * kAbsPitch + 32 * kAbsOutPitch;
   const int grid = 8 * ((n_h + 7) / 8) * (d_c / kAbsCols);
   hipLaunchKernelGGL(absorb_q_bf16_kernel, dim3(grid), dim3(kThreads), smem, stream, P);

@@ -7,6 +7,8 @@
 #include <cmath>
 #include <cstdint>
 
+#include "rope_spec.h"
+
 namespace mla {
 typedef uint16_t bf16_bits;
 // kernels (decode_bf16.hip, absorb_bf16.hip, merge_f32.hip)
@@ -16,7 +18,7 @@ hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* rows, int
                               int split_rows, float scale, hipStream_t stream);
 hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, const bf16_bits* w_uk,
                                 bf16_bits* q_abs, int n_q, int n_h, int d_h, int d_c, int d_r,
-                                const int64_t* positions, double theta, hipStream_t stream);
+                                const int64_t* positions, const RopeSpec& rope, hipStream_t stream);
 hipError_t launch_out_proj_bf16(const float* o_lat, const bf16_bits* w_uv, bf16_bits* o_c, int n_q,
                                 int n_h, int d_h, int d_c, hipStream_t stream);
 bool absorb_bf16_supported(int d_h, int d_c);
@@ -29,13 +31,13 @@ hipError_t launch_merge(const void* o_part, bool f16_partials, const float* lse_
                         float* lse, int n_q, int n_h, int d_c, int num_splits, hipStream_t stream);
 hipError_t launch_absorb_q_f32(const float* q_c, const float* q_r, const float* w_uk, float* q_abs,
                                int n_q, int n_h, int d_h, int d_c, int d_r, const int64_t* positions,
-                               double theta, hipStream_t stream);
+                               const RopeSpec& rope, hipStream_t stream);
 // prologue.hip
 bool kv_append_bf16_supported(int d_model, int d_c, int d_r);
 size_t kv_append_workspace_bytes(bool bf16, int n_new, int d_c, int d_r);
 hipError_t launch_kv_append(bool bf16, const void* h, const void* w_dkv, const void* w_kr,
                             const int64_t* positions, const int64_t* dst_rows, void* rows, int64_t stride,
-                            float* workspace, int n_new, int d_model, int d_c, int d_r, double theta,
+                            float* workspace, int n_new, int d_model, int d_c, int d_r, const RopeSpec& rope,
                             hipStream_t stream);
 // quant_fp8.hip, decode_fp8.hip
 bool quantize_rows_supported(int width);
@@ -83,11 +85,40 @@ size_t esize(const mla_dims_t* d) { return d->dtype == MLA_BF16 ? 2 : 4; }
 
 mla_status_t launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
 
+bool finite(float x) { return x == x && !std::isinf(x); }
+
+// mla_rope_t -> the kernels' RopeSpec; NULL: theta 10000, no YaRN.
+mla_status_t rope_spec(const mla_rope_t* r, mla::RopeSpec* out) {
+  const double theta = r && r->theta > 0.f ? (double)r->theta : 10000.0;
+  *out = mla::RopeSpec{std::log(theta), 1.0, 1.0, 0.0, 1.0};
+  if (!r) return MLA_OK;
+  if (!finite(r->theta) || !finite(r->yarn_factor)) return MLA_ERR_SHAPE;
+  if (r->yarn_factor > 1.f) {
+    if (r->yarn_original_len <= 0 || !finite(r->yarn_alpha) || !finite(r->yarn_beta) ||
+        !(r->yarn_beta > r->yarn_alpha))
+      return MLA_ERR_SHAPE;
+    out->yarn_s = r->yarn_factor;
+    out->yarn_len = r->yarn_original_len;
+    out->yarn_alpha = r->yarn_alpha;
+    out->yarn_beta = r->yarn_beta;
+  }
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+float mla_rope_softmax_scale(const mla_dims_t* dims, const mla_rope_t* rope) {
+  if (!dims || dims->d_h + dims->d_r <= 0) return 0.f;
+  const double base = dims->softmax_scale > 0.f ? (double)dims->softmax_scale
+                                                : 1.0 / std::sqrt((double)(dims->d_h + dims->d_r));
+  if (!rope || !(rope->yarn_factor > 1.f)) return (float)base;
+  const double sqrt_t = (double)rope->yarn_mscale * std::log((double)rope->yarn_factor) + 1.0;
+  return (float)(base * sqrt_t * sqrt_t);
+}
 
 const char* mla_status_string(mla_status_t s) {
   switch (s) {
@@ -124,9 +155,12 @@ mla_status_t mla_check_offsets(const int64_t* host_offsets, int32_t batch, int32
 namespace {
 // Shared by mla_absorb_q and mla_absorb_q_rope: positions == nullptr copies q_r as is.
 mla_status_t absorb_common(const mla_dims_t* dims, int32_t n_q, const void* q_c, const void* q_r,
-                           const void* w_uk, const int64_t* positions, float rope_theta, void* q_abs,
+                           const void* w_uk, const int64_t* positions, const mla_rope_t* rope, void* q_abs,
                            hipStream_t stream) {
   mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  mla::RopeSpec spec;
+  st = rope_spec(rope, &spec);
   if (st != MLA_OK) return st;
   if (n_q < 0) return MLA_ERR_SHAPE;
   if (n_q == 0) return MLA_OK;
@@ -135,33 +169,32 @@ mla_status_t absorb_common(const mla_dims_t* dims, int32_t n_q, const void* q_c,
   if ((int64_t)n_q * dims->n_h * d_qk >= kMaxElems ||
       (int64_t)dims->n_h * dims->d_h * dims->d_c >= kMaxElems)
     return MLA_ERR_SHAPE;
-  const double theta = rope_theta > 0.f ? (double)rope_theta : 10000.0;
   if (positions && !aligned(positions, 8)) return MLA_ERR_ALIGN;
   const uintptr_t a = esize(dims);
   if (!aligned(q_c, a) || !aligned(q_r, a) || !aligned(w_uk, a) || !aligned(q_abs, a)) return MLA_ERR_ALIGN;
   if (dims->dtype == MLA_F32)
     return launched(mla::launch_absorb_q_f32((const float*)q_c, (const float*)q_r, (const float*)w_uk,
                                              (float*)q_abs, n_q, dims->n_h, dims->d_h, dims->d_c,
-                                             dims->d_r, positions, theta, stream));
+                                             dims->d_r, positions, spec, stream));
   if (!mla::absorb_bf16_supported(dims->d_h, dims->d_c) || dims->d_r % 8) return MLA_ERR_UNSUPPORTED;
   if (positions && dims->d_r > 512) return MLA_ERR_UNSUPPORTED;  // a pair index per thread of 256
   if (!aligned(q_c, 16) || !aligned(w_uk, 16)) return MLA_ERR_ALIGN;
   return launched(mla::launch_absorb_q_bf16((const uint16_t*)q_c, (const uint16_t*)q_r,
                                             (const uint16_t*)w_uk, (uint16_t*)q_abs, n_q, dims->n_h,
-                                            dims->d_h, dims->d_c, dims->d_r, positions, theta, stream));
+                                            dims->d_h, dims->d_c, dims->d_r, positions, spec, stream));
 }
 }  // namespace
 
 mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t n_q, const void* q_c, const void* q_r,
                           const void* w_uk, void* q_abs, hipStream_t stream) {
-  return absorb_common(dims, n_q, q_c, q_r, w_uk, nullptr, 0.f, q_abs, stream);
+  return absorb_common(dims, n_q, q_c, q_r, w_uk, nullptr, nullptr, q_abs, stream);
 }
 
 mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t n_q, const void* q_c, const void* q_r_raw,
-                               const void* w_uk, const int64_t* positions, float rope_theta, void* q_abs,
+                               const void* w_uk, const int64_t* positions, const mla_rope_t* rope, void* q_abs,
                                hipStream_t stream) {
   if (n_q > 0 && !positions) return MLA_ERR_NULL;
-  return absorb_common(dims, n_q, q_c, q_r_raw, w_uk, positions, rope_theta, q_abs, stream);
+  return absorb_common(dims, n_q, q_c, q_r_raw, w_uk, positions, rope, q_abs, stream);
 }
 
 size_t mla_kv_append_workspace_bytes(const mla_dims_t* dims, int32_t n_new) {
@@ -171,9 +204,12 @@ size_t mla_kv_append_workspace_bytes(const mla_dims_t* dims, int32_t n_new) {
 
 mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t n_new, int32_t d_model, const void* h,
                            const void* w_dkv, const void* w_kr, const int64_t* positions,
-                           const int64_t* dst_rows, void* rows, int64_t stride, float rope_theta,
+                           const int64_t* dst_rows, void* rows, int64_t stride, const mla_rope_t* rope,
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  mla::RopeSpec spec;
+  st = rope_spec(rope, &spec);
   if (st != MLA_OK) return st;
   if (n_new < 0 || d_model < 1) return MLA_ERR_SHAPE;
   if (n_new == 0) return MLA_OK;
@@ -183,7 +219,6 @@ mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t n_new, int32_t d_mode
   if (!aligned(positions, 8) || !aligned(dst_rows, 8)) return MLA_ERR_ALIGN;
   const uintptr_t a = esize(dims);
   if (!aligned(h, a) || !aligned(w_dkv, a) || !aligned(w_kr, a) || !aligned(rows, a)) return MLA_ERR_ALIGN;
-  const double theta = rope_theta > 0.f ? (double)rope_theta : 10000.0;
   const bool bf16 = dims->dtype == MLA_BF16;
   if (bf16) {
     if (!mla::kv_append_bf16_supported(d_model, dims->d_c, dims->d_r)) return MLA_ERR_UNSUPPORTED;
@@ -193,7 +228,7 @@ mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t n_new, int32_t d_mode
     if (!aligned(workspace, 4)) return MLA_ERR_ALIGN;
   }
   return launched(mla::launch_kv_append(bf16, h, w_dkv, w_kr, positions, dst_rows, rows, stride,
-                                        (float*)workspace, n_new, d_model, dims->d_c, dims->d_r, theta, stream));
+                                        (float*)workspace, n_new, d_model, dims->d_c, dims->d_r, spec, stream));
 }
 
 mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, int32_t q_per_seq, const void* q_abs,

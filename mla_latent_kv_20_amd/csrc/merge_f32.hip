@@ -186,7 +186,7 @@ merge_splits_kernel(const PartT* __restrict__ o_part, const float* __restrict__ 
 __global__ void absorb_q_f32_kernel(const float* __restrict__ q_c, const float* __restrict__ q_r,
                                     const float* __restrict__ w_uk, float* __restrict__ q_abs,
                                     int n_q, int n_h, int d_h, int d_c, int d_r,
-                                    const int64_t* __restrict__ pos, double log_theta) {
+                                    const int64_t* __restrict__ pos, RopeSpec rope) {
   const int d_qk = d_c + d_r;
   const size_t total = (size_t)n_q * n_h * d_qk;
   for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total;
@@ -207,7 +207,7 @@ __global__ void absorb_q_f32_kernel(const float* __restrict__ q_c, const float* 
       const int k = c - d_c;
       const int k0 = k < half ? k : k - half;
       double x = q_r[ni * d_r + k0], y = q_r[ni * d_r + k0 + half];
-      rope_pair(x, y, pos[ni / n_h], k0, d_r, log_theta);
+      rope_pair(x, y, pos[ni / n_h], k0, d_r, rope);
       q_abs[e] = (float)(k < half ? x : y);
     }
   }
@@ -349,10 +349,10 @@ hipError_t launch_merge(const void* o_part, bool f16_partials, const float* lse_
 
 hipError_t launch_absorb_q_f32(const float* q_c, const float* q_r, const float* w_uk, float* q_abs,
                                int n_q, int n_h, int d_h, int d_c, int d_r, const int64_t* positions,
-                               double theta, hipStream_t stream) {
+                               const RopeSpec& rope, hipStream_t stream) {
   const size_t total = (size_t)n_q * n_h * (d_c + d_r);
   hipLaunchKernelGGL(absorb_q_f32_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream, q_c, q_r,
-                     w_uk, q_abs, n_q, n_h, d_h, d_c, d_r, positions, positions ? log(theta) : 0.0);
+                     w_uk, q_abs, n_q, n_h, d_h, d_c, d_r, positions, rope);
   return hipGetLastError();
 }
 

@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "rope_spec.h"
 #include <stdint.h>
 
 namespace mla {
@@ -26,13 +28,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_bits b) {
 }
 
 // RoPE of one rotate-half pair (x, y) = (v_k, v_{k+d/2}) at `pos`: rotation by the angle
-// pos * theta^(-2k/d) ([notes] "MLA(Multi-head Latent Attention): DeepSeek-V2 논문정리",
-// "MLA 코드 구현").  The inverse frequency and the angle are fp64 (angles reach 1e5 rad at
-// long context); the angle is reduced to [-pi, pi] in fp64 (error ~1e-11 rad), its sine and
-// cosine taken in fp32 and the rotation done in fp64: ~1e-7 relative, far below the bf16 and
-// fp32 outputs' rounding.
-__device__ __forceinline__ double rope_inv_freq(int k, int d, double log_theta) {
-  return exp(-(2.0 * k / d) * log_theta);
+// pos * f_k, f_k the pair's frequency (rope_spec.h).  The frequency and the angle are fp64
+// (angles reach 1e5 rad at long context); the angle is reduced to [-pi, pi] in fp64 (error
+// ~1e-11 rad), its sine and cosine taken in fp32 and the rotation done in fp64: ~1e-7
+// relative, far below the bf16 and fp32 outputs' rounding.
+__device__ __forceinline__ double rope_inv_freq(int k, int d, const RopeSpec& r) {
+  const double f = exp(-(2.0 * k / d) * r.log_theta);
+  if (!(r.yarn_s > 1.0)) return f;
+  const double turns = r.yarn_len * f * 0.15915494309189535;   // turns over the training length
+  double g = (turns - r.yarn_alpha) / (r.yarn_beta - r.yarn_alpha);
+  g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+  return (1.0 - g) * f / r.yarn_s + g * f;
 }
 __device__ __forceinline__ void rope_rotate(double& x, double& y, int64_t pos, double inv_freq) {
   const double ang = (double)pos * inv_freq;
@@ -45,8 +51,8 @@ __device__ __forceinline__ void rope_rotate(double& x, double& y, int64_t pos, d
   y = ny;
 }
 __device__ __forceinline__ void rope_pair(double& x, double& y, int64_t pos, int k, int d,
-                                          double log_theta) {
-  rope_rotate(x, y, pos, rope_inv_freq(k, d, log_theta));
+                                          const RopeSpec& r) {
+  rope_rotate(x, y, pos, rope_inv_freq(k, d, r));
 }
 __device__ __forceinline__ bf16_bits f32_to_bf16(float f) {
   return __builtin_bit_cast(bf16_bits, (__bf16)f);

@@ -36,7 +36,7 @@ struct AppendParams {
   float* ws;               // bf16: [kSplitK][n_new][d_c + d_r] partial sums
   int64_t stride;
   int n_new, d_model, d_c, d_r;
-  double log_theta;        // ln(theta)
+  RopeSpec rope;
 };
 
 // Kernel 1: partial products of one (column block, token block, K slice).
@@ -114,7 +114,7 @@ __global__ void kv_append_finish_kernel(AppendParams P) {
         y += src[s * slice + P.d_c + k + half];
       }
       double dx = x, dy = y;
-      rope_pair(dx, dy, P.pos[t], k, P.d_r, P.log_theta);
+      rope_pair(dx, dy, P.pos[t], k, P.d_r, P.rope);
       dst[P.d_c + k] = f32_to_bf16((float)dx);
       dst[P.d_c + k + half] = f32_to_bf16((float)dy);
     }
@@ -147,7 +147,7 @@ __global__ void kv_append_f32_kernel(AppendParams P) {
         ay = fmaf(wy[m], h[m], ay);
       }
       double dx = ax, dy = ay;
-      rope_pair(dx, dy, P.pos[t], k0, P.d_r, P.log_theta);
+      rope_pair(dx, dy, P.pos[t], k0, P.d_r, P.rope);
       dst[c] = (float)(k < half ? dx : dy);
     }
   }
@@ -169,10 +169,9 @@ size_t kv_append_workspace_bytes(bool bf16, int n_new, int d_c, int d_r) {
 
 hipError_t launch_kv_append(bool bf16, const void* h, const void* w_dkv, const void* w_kr,
                             const int64_t* positions, const int64_t* dst_rows, void* rows, int64_t stride,
-                            float* workspace, int n_new, int d_model, int d_c, int d_r, double theta,
+                            float* workspace, int n_new, int d_model, int d_c, int d_r, const RopeSpec& rope,
                             hipStream_t stream) {
-  AppendParams P{h, w_dkv, w_kr, positions, dst_rows, rows, workspace, stride, n_new, d_model, d_c, d_r,
-                 log(theta)};
+  AppendParams P{h, w_dkv, w_kr, positions, dst_rows, rows, workspace, stride, n_new, d_model, d_c, d_r, rope};
   if (bf16) {
     hipLaunchKernelGGL(kv_append_partial_kernel, dim3((d_c + d_r) / 32, (n_new + 31) / 32, kSplitK),
                        dim3(kAppThreads), 0, stream, P);

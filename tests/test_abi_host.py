@@ -37,7 +37,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert set(names) == set(B.SIGNATURES), names
     for n in names:
         assert hasattr(lib, n)
-    assert lib.mla_abi_version() == 5
+    assert lib.mla_abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -133,9 +133,9 @@ def test_prologue_argument_checks(lib):
     """mla_kv_append and mla_absorb_q_rope reject bad arguments before any launch."""
     d = dims()
     app = lambda d, n=4, dm=5120, h=FAKE, wd=FAKE, wr=FAKE, pos=FAKE, dst=FAKE, rows=FAKE, stride=576, \
-        ws=FAKE, wsb=1 << 30: \
-        lib.mla_kv_append(ctypes.byref(d), n, dm, h, wd, wr, pos, dst, rows, stride, ctypes.c_float(0.0),
-                          ws, wsb, None)
+        ws=FAKE, wsb=1 << 30, rope=None: \
+        lib.mla_kv_append(ctypes.byref(d), n, dm, h, wd, wr, pos, dst, rows, stride,
+                          ctypes.byref(rope) if rope is not None else None, ws, wsb, None)
     assert app(d, n=0, h=None, wd=None, wr=None, pos=None, dst=None, rows=None, ws=None, wsb=0) == B.MLA_OK
     assert app(d, n=-1) == B.MLA_ERR_SHAPE
     assert app(d, dm=0) == B.MLA_ERR_SHAPE
@@ -155,8 +155,9 @@ def test_prologue_argument_checks(lib):
     assert app(dims(d_r=63)) == B.MLA_ERR_SHAPE                    # RoPE pairs need an even d_r
     f32 = dims(dtype=B.MLA_F32)
     assert lib.mla_kv_append_workspace_bytes(ctypes.byref(f32), 4) == 0
-    rope = lambda d, n=4, qc=FAKE, qr=FAKE, w=FAKE, pos=FAKE, out=FAKE: \
-        lib.mla_absorb_q_rope(ctypes.byref(d), n, qc, qr, w, pos, ctypes.c_float(0.0), out, None)
+    rope = lambda d, n=4, qc=FAKE, qr=FAKE, w=FAKE, pos=FAKE, out=FAKE, rp=None: \
+        lib.mla_absorb_q_rope(ctypes.byref(d), n, qc, qr, w, pos, ctypes.byref(rp) if rp is not None else None,
+                              out, None)
     assert rope(d, n=0, qc=None, qr=None, w=None, pos=None, out=None) == B.MLA_OK
     assert rope(d, n=-2) == B.MLA_ERR_SHAPE
     assert rope(d, pos=None) == B.MLA_ERR_NULL
@@ -165,6 +166,25 @@ def test_prologue_argument_checks(lib):
     assert rope(d, qr=FAKE + 1) == B.MLA_ERR_ALIGN
     assert rope(dims(d_r=1024)) == B.MLA_ERR_UNSUPPORTED           # bf16: d_r <= 512
     assert rope(dims(dtype=7)) == B.MLA_ERR_DTYPE
+    # YaRN parameters: checked only when the factor turns YaRN on
+    for bad in (B.rope(yarn_factor=40.0, yarn_original_len=0), B.rope(yarn_factor=40.0, yarn_beta=1.0),
+                B.rope(theta=float("nan")), B.rope(yarn_factor=float("inf"))):
+        assert rope(d, rp=bad) == B.MLA_ERR_SHAPE
+        assert app(d, rope=bad) == B.MLA_ERR_SHAPE
+    assert rope(d, rp=B.rope(yarn_factor=1.0, yarn_original_len=0), pos=FAKE + 4) == B.MLA_ERR_ALIGN   # s <= 1: plain
+
+
+def test_rope_softmax_scale(lib):
+    d = dims()
+    base = 1.0 / np.sqrt(192.0)
+    assert np.isclose(lib.mla_rope_softmax_scale(ctypes.byref(d), None), base, rtol=1e-6)
+    assert np.isclose(lib.mla_rope_softmax_scale(ctypes.byref(d), ctypes.byref(B.rope())), base, rtol=1e-6)
+    y = B.rope(yarn_factor=40.0)
+    t = (0.0707 * np.log(40.0) + 1.0) ** 2                          # sqrt(t) = 0.0707 ln s + 1
+    assert np.isclose(lib.mla_rope_softmax_scale(ctypes.byref(d), ctypes.byref(y)), base * t, rtol=1e-6)
+    assert np.isclose(lib.mla_rope_softmax_scale(ctypes.byref(dims(softmax_scale=0.5)), ctypes.byref(y)),
+                      0.5 * t, rtol=1e-6)
+    assert lib.mla_rope_softmax_scale(None, None) == 0.0
 
 
 def test_quantized_cache_argument_checks(lib):

@@ -170,3 +170,91 @@ def test_prologue_then_decode_step(torch, name):
     err = float(np.max(np.abs(got - ref["o_c"])))
     say(f"    o_c: max|d| = {err:.3e} (bound {tol:.3e})")
     assert err <= tol
+
+
+# YaRN (DeepSeek-V2's long-context RoPE: s = 40, L = 4096, alpha = 1, beta = 32)
+YARN = dict(factor=40.0, original_len=4096, alpha=1.0, beta=32.0, mscale=0.0707)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "dsv2_small"])
+def test_kv_append_yarn(torch, name):
+    w = W.make_config(name)
+    n = w.n_q
+    pos = new_token_positions(w)
+    pos[0], pos[-1] = 131071, 40000                      # angles where the ramp matters
+    rows0 = D.packed_rows(w)
+    total = rows0.shape[0]
+    dst = total + np.arange(n)
+    p = W.draw_prologue(w, D_MODEL[name], pos, dst)
+    say(f"[kv_append yarn] {name} n_new={n}")
+    buf = D._tensor(np.concatenate([rows0, np.zeros((n, w.d_c + w.d_r))], axis=0).astype(rows0.dtype),
+                    w.dtype, "cuda")
+    B.kv_append(dims_of(w), D._tensor(p.h, w.dtype, "cuda"), D._tensor(p.w_dkv, w.dtype, "cuda"),
+                D._tensor(p.w_kr, w.dtype, "cuda"), torch.from_numpy(p.positions).cuda(),
+                torch.from_numpy(p.dst_rows).cuda(), buf, rope=B.rope(yarn_factor=40.0))
+    torch.cuda.synchronize()
+    c, k = O.kv_prologue(W.to_f64(p.h, w.dtype), W.to_f64(p.w_dkv, w.dtype), W.to_f64(p.w_kr, w.dtype), pos,
+                         yarn=YARN)
+    got = D.to_numpy_f64(buf)
+    check("c_kv rows", got[dst, :w.d_c], c, w.dtype)
+    check("k_r rows (yarn)", got[dst, w.d_c:], k, w.dtype)
+    plain = O.kv_prologue(W.to_f64(p.h, w.dtype), W.to_f64(p.w_dkv, w.dtype), W.to_f64(p.w_kr, w.dtype), pos)[1]
+    assert float(np.max(np.abs(plain - k))) > 0.1                  # YaRN changed the rotations
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "dsv2_small"])
+def test_absorb_q_rope_yarn(torch, name):
+    w = W.make_config(name)
+    pos = new_token_positions(w)
+    pos[0] = 131071
+    p = W.draw_prologue(w, D_MODEL[name], pos, np.zeros(w.n_q, np.int64))
+    say(f"[absorb_q_rope yarn] {name}")
+    t = D.to_device(w)
+    qa = B.absorb_q_rope(dims_of(w), t["q_c"], D._tensor(p.q_r_raw, w.dtype, "cuda"), t["w_uk"],
+                         torch.from_numpy(p.positions).cuda(), rope=B.rope(yarn_factor=40.0))
+    torch.cuda.synchronize()
+    ref = O.absorb_q_rope(w.f64("q_c"), W.to_f64(p.q_r_raw, w.dtype), w.f64("w_uk"), pos, yarn=YARN)
+    got = D.to_numpy_f64(qa)
+    check("q_abs rope (yarn)", got[..., w.d_c:], ref[..., w.d_c:], w.dtype)
+
+
+def test_prologue_then_decode_step_yarn(torch):
+    """The serving step at a long position with YaRN: rotations and the softmax scale's
+    length factor, through the ABI, against the oracle."""
+    w = W.make_config("dsv2_small")
+    lens = np.diff(w.offsets).astype(np.int64)
+    off = w.offsets.astype(np.int64)
+    new_off = off + np.arange(w.batch + 1)
+    rows0 = D.packed_rows(w)
+    layout = np.zeros((rows0.shape[0] + w.batch, w.d_c + w.d_r), rows0.dtype)
+    for b in range(w.batch):
+        layout[new_off[b]:new_off[b] + lens[b]] = rows0[off[b]:off[b + 1]]
+    pos = lens + 100000                                  # deep into the extended context
+    dst = new_off[1:] - 1
+    p = W.draw_prologue(w, D_MODEL["dsv2_small"], pos, dst)
+    y = B.rope(yarn_factor=40.0)
+    d = dims_of(w)
+    d.softmax_scale = B.rope_softmax_scale(d, y)
+    say(f"[prologue step yarn] softmax scale {d.softmax_scale:.6f}")
+    buf = D._tensor(layout, w.dtype, "cuda")
+    B.kv_append(d, D._tensor(p.h, w.dtype, "cuda"), D._tensor(p.w_dkv, w.dtype, "cuda"),
+                D._tensor(p.w_kr, w.dtype, "cuda"), torch.from_numpy(pos).cuda(), torch.from_numpy(dst).cuda(),
+                buf, rope=y)
+    t = D.to_device(w)
+    qa = B.absorb_q_rope(d, t["q_c"], D._tensor(p.q_r_raw, w.dtype, "cuda"), t["w_uk"], torch.from_numpy(pos).cuda(),
+                         rope=y)
+    op, lp = B.decode(d, qa, buf[:, :w.d_c], buf[:, w.d_c:], torch.from_numpy(new_off).cuda(), w.batch, 1, 3, 96)
+    o_lat, lse = B.merge_splits(d, op, lp)
+    o_c = B.out_proj(d, o_lat, t["w_uv"])
+    torch.cuda.synchronize()
+    c_new, k_new = O.kv_prologue(W.to_f64(p.h, w.dtype), W.to_f64(p.w_dkv, w.dtype), W.to_f64(p.w_kr, w.dtype),
+                                 pos, yarn=YARN)
+    rows = O.append_rows(W.to_f64(layout, w.dtype), dst, c_new, k_new)
+    q_r = O.rope_pairs(W.to_f64(p.q_r_raw, w.dtype), pos[:, None], yarn=YARN)
+    ref = O.absorbed_decode(rows[:, :w.d_c], rows[:, w.d_c:], new_off, w.f64("q_c"), q_r, w.f64("w_uk"),
+                            w.f64("w_uv"), 1, scale=O.yarn_softmax_scale(w.d_h, w.d_r, YARN))
+    got = D.to_numpy_f64(o_c)
+    m = float(np.max(np.abs(ref["o_c"])))
+    err = float(np.max(np.abs(got - ref["o_c"])))
+    say(f"    o_c: max|d| = {err:.3e} (bound {1e-2 * m + 1e-3:.3e})")
+    assert err <= 1e-2 * m + 1e-3
