@@ -35,7 +35,9 @@ out_proj) that the C-ABI entry points are compared against one by one.  The deco
 prologue (kv_prologue, append_rows, absorb_q_rope) gives the new tokens' cache rows and
 the rotated queries from the hidden states.  A quantized cache (e4m3_value, e4m3_encode,
 quantize_rows, dequantize_rows) stores each row as FP8 E4M3 codes with one scale per row;
-its decode is the decode above over the dequantized rows.
+its decode is the decode above over the dequantized rows.  Offline weight folding (q_up,
+fold_q, absorb_q_folded, o_proj, fold_o, out_folded) gives the path from the compressed
+query c^Q to the attention block's output u in the unfolded and the folded forms.
 
 Readings where the pages are silent or garbled (each is listed in the design notes):
   * scale 1/sqrt(d_h + d_h^R) (three pages agree; one prints it without the root);
@@ -422,3 +424,53 @@ def quantize_rows(rows):
 def dequantize_rows(codes, scales) -> np.ndarray:
     """x^ = value(code) * scale, fp64 [R, W]."""
     return e4m3_value(codes) * np.asarray(scales, np.float64)[:, None]
+
+
+# ----------------------------------------------------------------------------
+# Offline weight folding: from c^Q to the block output u
+# ----------------------------------------------------------------------------
+# q^C = W^UQ c^Q ([notes] eq. 13).  The score's content term is
+# (W^UQ c^Q)^T (W^UK c^KV) = (c^Q)^T ((W^UQ)^T W^UK) c^KV ([notes] "Decoupled Rotary Position
+# Embedding", the expansion of the score; [report] "Идея 1"), so the token-independent product
+# can be formed once: per head, G_i = (W^UK_i)^T W^UQ_i [d_c x d_cq] maps c^Q straight to the
+# absorbed query.  On the output side u = W^O [o^C_1; ...; o^C_nh] with o^C_i = W^UV_i o_lat_i
+# ([notes] "Value에 대한 수식 전개": W'^O = W^O W^UV), so W'^O_i = W^O_i W^UV_i [d_model x d_c]
+# and u = sum_i W'^O_i o_lat_i.
+# Layouts: c^Q [n, d_cq]; W^UQ [n_h, d_h, d_cq] (head i's rows of W^UQ); W^O [d_model, n_h d_h]
+# (columns i d_h .. i d_h + d_h - 1 act on head i); G [n_h, d_c, d_cq]; W'^O [d_model, n_h d_c].
+
+def q_up(c_q, w_uq) -> np.ndarray:
+    """q^C[n, i] = W^UQ_i c^Q[n] ([notes] eq. 13) -> [n, n_h, d_h]."""
+    return np.einsum("idk,nk->nid", np.asarray(w_uq, np.float64), np.asarray(c_q, np.float64))
+
+
+def fold_q(w_uq, w_uk) -> np.ndarray:
+    """G_i = (W^UK_i)^T W^UQ_i -> [n_h, d_c, d_cq]."""
+    return np.einsum("idc,idk->ick", np.asarray(w_uk, np.float64), np.asarray(w_uq, np.float64))
+
+
+def absorb_q_folded(c_q, g, q_r) -> np.ndarray:
+    """q_abs[n, i] = [G_i c^Q[n] ; q_r[n, i]] -> [n, n_h, d_c + d_r]."""
+    lat = np.einsum("ick,nk->nic", np.asarray(g, np.float64), np.asarray(c_q, np.float64))
+    return np.concatenate([lat, np.asarray(q_r, np.float64)], axis=2)
+
+
+def o_proj(o_c, w_o) -> np.ndarray:
+    """u[n] = W^O [o^C[n, 0]; ...; o^C[n, n_h-1]] -> [n, d_model]."""
+    o_c = np.asarray(o_c, np.float64)
+    return o_c.reshape(o_c.shape[0], -1) @ np.asarray(w_o, np.float64).T
+
+
+def fold_o(w_o, w_uv) -> np.ndarray:
+    """W'^O_i = W^O_i W^UV_i, side by side -> [d_model, n_h d_c]."""
+    w_o = np.asarray(w_o, np.float64)
+    w_uv = np.asarray(w_uv, np.float64)
+    n_h, d_h, d_c = w_uv.shape
+    blocks = [w_o[:, i * d_h:(i + 1) * d_h] @ w_uv[i] for i in range(n_h)]
+    return np.concatenate(blocks, axis=1)
+
+
+def out_folded(o_lat, w_fold) -> np.ndarray:
+    """u[n] = W'^O [o_lat[n, 0]; ...; o_lat[n, n_h-1]] -> [n, d_model]."""
+    o_lat = np.asarray(o_lat, np.float64)
+    return o_lat.reshape(o_lat.shape[0], -1) @ np.asarray(w_fold, np.float64).T

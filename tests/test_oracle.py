@@ -594,6 +594,93 @@ def test_prologue_then_decode_depends_only_on_relative_positions():
 
 
 # ----------------------------------------------------------------------------
+# Offline weight folding
+# ----------------------------------------------------------------------------
+
+def _fold_inputs(seed=71, n=3, n_h=2, d_h=4, d_c=6, d_r=2, d_cq=5, d_model=7, L=9):
+    rng = np.random.default_rng(seed)
+    return dict(c_q=rng.standard_normal((n, d_cq)), w_uq=rng.standard_normal((n_h, d_h, d_cq)),
+                w_uk=rng.standard_normal((n_h, d_h, d_c)), w_uv=rng.standard_normal((n_h, d_h, d_c)),
+                w_o=rng.standard_normal((d_model, n_h * d_h)), q_r=rng.standard_normal((n, n_h, d_r)),
+                c_kv=rng.standard_normal((L, d_c)), o_lat=rng.standard_normal((n, n_h, d_c)))
+
+
+def test_folded_score_equals_unfolded_score():
+    """The NumPy check the [report] exercises ask for: (W^UQ c^Q)^T (W^UK c^KV) equals
+    (c^Q)^T ((W^UQ)^T W^UK) c^KV up to rounding, per head, written out with scalar loops."""
+    a = _fold_inputs()
+    g = O.fold_q(a["w_uq"], a["w_uk"])
+    n_h, d_h, d_cq = a["w_uq"].shape
+    d_c = a["w_uk"].shape[2]
+    for n in range(3):
+        for i in range(n_h):
+            for j in range(a["c_kv"].shape[0]):
+                q = [sum(a["w_uq"][i][d][k] * a["c_q"][n][k] for k in range(d_cq)) for d in range(d_h)]
+                kk = [sum(a["w_uk"][i][d][c] * a["c_kv"][j][c] for c in range(d_c)) for d in range(d_h)]
+                lhs = sum(q[d] * kk[d] for d in range(d_h))
+                rhs = sum(a["c_q"][n][k] * g[i][c][k] * a["c_kv"][j][c] for k in range(d_cq) for c in range(d_c))
+                assert abs(lhs - rhs) <= 1e-12 * (1 + abs(lhs))
+
+
+def test_folded_query_equals_up_projection_then_absorption():
+    a = _fold_inputs()
+    folded = O.absorb_q_folded(a["c_q"], O.fold_q(a["w_uq"], a["w_uk"]), a["q_r"])
+    unfolded = O.absorb_q(O.q_up(a["c_q"], a["w_uq"]), a["q_r"], a["w_uk"])
+    assert rel(folded, unfolded) <= 1e-13
+
+
+def test_fold_q_with_an_identity_up_projection_is_w_uk_transposed():
+    a = _fold_inputs(d_cq=6)
+    eye = np.zeros((2, 4, 6))
+    eye[:, :, :4] = np.eye(4)                                    # c^Q's first d_h components are q^C
+    g = O.fold_q(eye, a["w_uk"])
+    assert np.array_equal(g[:, :, :4], np.transpose(a["w_uk"], (0, 2, 1))) and not g[:, :, 4:].any()
+
+
+def test_folded_output_equals_value_projection_then_w_o():
+    """[notes] "Value에 대한 수식 전개": W^O (W^UV o) = (W^O W^UV) o, over all heads."""
+    a = _fold_inputs()
+    folded = O.out_folded(a["o_lat"], O.fold_o(a["w_o"], a["w_uv"]))
+    unfolded = O.o_proj(O.out_proj(a["o_lat"], a["w_uv"]), a["w_o"])
+    assert rel(folded, unfolded) <= 1e-13
+    # scalar loops for one output
+    n_h, d_h, d_c = a["w_uv"].shape
+    u0 = sum(a["w_o"][2][i * d_h + d] * sum(a["w_uv"][i][d][c] * a["o_lat"][1][i][c] for c in range(d_c))
+             for i in range(n_h) for d in range(d_h))
+    assert abs(folded[1][2] - u0) <= 1e-12 * (1 + abs(u0))
+
+
+def test_decode_from_c_q_is_the_same_folded_or_not():
+    a = _fold_inputs(L=11)
+    rng = np.random.default_rng(73)
+    k_r = rng.standard_normal((11, 2))
+    q_c = O.q_up(a["c_q"], a["w_uq"])
+    ref = O.absorbed_decode(a["c_kv"], k_r, np.array([0, 4, 11]), q_c[:2], a["q_r"][:2], a["w_uk"], a["w_uv"], 1)
+    qa = O.absorb_q_folded(a["c_q"][:2], O.fold_q(a["w_uq"], a["w_uk"]), a["q_r"][:2])
+    o, lse = O.attend_latent(qa, a["c_kv"], k_r, np.array([0, 4, 11]), 1, O.default_scale(4, 2))
+    assert rel(O.out_proj(o, a["w_uv"]), ref["o_c"]) <= 1e-12
+
+
+@pytest.mark.parametrize("mutant", ["q_transposed", "o_heads_shifted", "o_uv_transposed"])
+def test_planted_folding_mistakes_are_caught(mutant):
+    a = _fold_inputs(d_h=4, d_c=4, d_cq=4)                       # square blocks: wrong products still run
+    if mutant == "q_transposed":
+        g = np.einsum("idc,idk->ikc", a["w_uk"], a["w_uq"])    # G_i^T in G_i's place
+        with pytest.raises(AssertionError):
+            assert rel(O.absorb_q_folded(a["c_q"], g, a["q_r"]),
+                       O.absorb_q(O.q_up(a["c_q"], a["w_uq"]), a["q_r"], a["w_uk"])) <= 1e-13
+        return
+    n_h, d_h, d_c = a["w_uv"].shape
+    if mutant == "o_heads_shifted":
+        blocks = [a["w_o"][:, ((i + 1) % n_h) * d_h:((i + 1) % n_h + 1) * d_h] @ a["w_uv"][i] for i in range(n_h)]
+    else:
+        blocks = [a["w_o"][:, i * d_h:(i + 1) * d_h] @ a["w_uv"][i].T for i in range(n_h)]
+    wf = np.concatenate(blocks, axis=1)
+    with pytest.raises(AssertionError):
+        assert rel(O.out_folded(a["o_lat"], wf), O.o_proj(O.out_proj(a["o_lat"], a["w_uv"]), a["w_o"])) <= 1e-13
+
+
+# ----------------------------------------------------------------------------
 # YaRN (long-context RoPE on the decoupled key and query)
 # ----------------------------------------------------------------------------
 
