@@ -25,6 +25,11 @@
  *   mla_kv_append     new cache rows [W^DKV h ; RoPE(W^KR h)] at given rows
  *   mla_absorb_q_rope mla_absorb_q with q^R rotated at the tokens' positions
  *
+ * From the compressed query c^Q to the block output u, unfolded and with folded weights:
+ *   mla_q_up, mla_o_proj                 q^C = W^UQ c^Q;  u = W^O [o^C_1; ...; o^C_nh]
+ *   mla_fold_q, mla_absorb_q_folded      G_i = (W^UK_i)^T W^UQ_i;  q_abs = [G_i c^Q ; q^R]
+ *   mla_fold_o, mla_out_folded           W'^O = W^O W^UV;  u = W'^O [o_lat_1; ...]
+ *
  * A quantized cache keeps each row as FP8 E4M3 codes with one fp32 scale:
  *   mla_quantize_rows_fp8  rows -> codes and scales
  *   mla_decode_fp8         mla_decode over the dequantized rows value(code) * scale
@@ -67,7 +72,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 6
+#define MLA_ABI_VERSION 7
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -247,6 +252,43 @@ mla_status_t mla_decode_fp8(const mla_dims_t* dims, int32_t batch, int32_t q_per
                             const uint8_t* codes, int64_t code_stride, const float* scales,
                             const int64_t* seq_offsets, int32_t num_splits, int32_t split_rows,
                             int32_t partial_dtype, void* o_part, float* lse_part, hipStream_t stream);
+
+/*
+ * Weight folding ([notes] eq. 13 and "Decoupled Rotary Position Embedding": the score's content
+ * term (c^Q)^T (W^UQ)^T W^UK c^KV has a token-independent middle product; "Value에 대한 수식
+ * 전개": W'^O = W^O W^UV; [report] "Идея 1").  bf16 only (dims->dtype MLA_BF16); fp32
+ * accumulation, every output rounded once to bf16.  Layouts (row-major):
+ *   c_q    [n_q, d_cq]                      compressed query c^Q
+ *   w_uq   [n_h, d_h, d_cq]                 head i's rows of W^UQ (q^C_i = W^UQ_i c^Q)
+ *   q_c    [n_q, n_h, d_h]                  q^C, the input of mla_absorb_q
+ *   g      [n_h, d_c, d_cq]                 G_i = (W^UK_i)^T W^UQ_i: c^Q -> absorbed query
+ *   o_c    [n_q, n_h, d_h]                  per-head outputs (mla_out_proj)
+ *   w_o    [d_model, n_h * d_h]             W^O; columns i d_h .. i d_h + d_h - 1 act on head i
+ *   w_fold [d_model, n_h * d_c]             W'^O_i = W^O_i W^UV_i, side by side
+ *   u      [n_q, d_model]                   the block output
+ * Decode-time products (mla_q_up, mla_absorb_q_folded, mla_o_proj, mla_out_folded) stream
+ * their weight once; long reductions are split over workgroups with fp32 partial sums in the
+ * caller's workspace (mla_proj_workspace_bytes; contents undefined on return; calls sharing
+ * it must not overlap).  They need d_cq, d_c, d_model, n_h * d_h and n_h * d_c multiples of
+ * 128 (DeepSeek-V2: 1536, 512, 5120, 16384, 65536), else MLA_ERR_UNSUPPORTED, and 16-byte
+ * aligned tensors.  The folds (mla_fold_q, mla_fold_o) are offline: plain fp32 kernels, any
+ * shape.  mla_absorb_q_folded copies q_r (already rotated) into the RoPE part as mla_absorb_q.
+ */
+size_t mla_proj_workspace_bytes(const mla_dims_t* dims, int32_t n_q, int32_t d_model, int32_t d_cq);
+mla_status_t mla_q_up(const mla_dims_t* dims, int32_t n_q, int32_t d_cq, const void* c_q, const void* w_uq,
+                      void* q_c, void* workspace, size_t workspace_bytes, hipStream_t stream);
+mla_status_t mla_fold_q(const mla_dims_t* dims, int32_t d_cq, const void* w_uq, const void* w_uk, void* g,
+                        hipStream_t stream);
+mla_status_t mla_absorb_q_folded(const mla_dims_t* dims, int32_t n_q, int32_t d_cq, const void* c_q,
+                                 const void* g, const void* q_r, void* q_abs, hipStream_t stream);
+mla_status_t mla_o_proj(const mla_dims_t* dims, int32_t n_q, int32_t d_model, const void* o_c, const void* w_o,
+                        void* u, void* workspace, size_t workspace_bytes, hipStream_t stream);
+mla_status_t mla_fold_o(const mla_dims_t* dims, int32_t d_model, const void* w_o, const void* w_uv, void* w_fold,
+                        hipStream_t stream);
+/* o_lat [n_q, n_h, d_c] fp32 (rounded to bf16 as the MFMA operand, as mla_out_proj). */
+mla_status_t mla_out_folded(const mla_dims_t* dims, int32_t n_q, int32_t d_model, const float* o_lat,
+                            const void* w_fold, void* u, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /* Bytes of o_part for (n_q, num_splits, partial_dtype):
  * num_splits * n_q * n_h * d_c * (4 for MLA_F32, 2 for MLA_F16).  lse_part holds

@@ -62,6 +62,13 @@ SIGNATURES = {
     "mla_absorb_q_rope": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P, _ROPE_P, _P, _P]),
     "mla_kv_append": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _I64, _ROPE_P, _P, _SZ, _P]),
     "mla_rope_softmax_scale": (_F32, [_DIMS_P, _ROPE_P]),
+    "mla_proj_workspace_bytes": (_SZ, [_DIMS_P, _I32, _I32, _I32]),
+    "mla_q_up": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "mla_fold_q": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P]),
+    "mla_absorb_q_folded": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _P]),
+    "mla_o_proj": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "mla_fold_o": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P]),
+    "mla_out_folded": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
     "mla_kv_append_workspace_bytes": (_SZ, [_DIMS_P, _I32]),
     "mla_quantize_rows_fp8": (_I32, [_DIMS_P, _I64, _P, _I64, _P, _P, _I64, _P, _P]),
     "mla_decode_fp8": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _P, _P, _P]),
@@ -337,6 +344,88 @@ def decode_step(d: MlaDims, q_c, q_r, w_uk, w_uv, cache, offsets, batch: int, q_
         o_lat, lse = merge_splits(d, o_part, lse_part, b.get("o_lat"), b.get("lse"), stream)
     o_c = out_proj(d, o_lat, w_uv, b.get("o_c"), stream=stream)
     return dict(q_abs=q_abs, o_part=o_part, lse_part=lse_part, o_lat=o_lat, lse=lse, o_c=o_c)
+
+
+def proj_workspace_bytes(d: MlaDims, n_q: int, d_model: int, d_cq: int) -> int:
+    return int(load().mla_proj_workspace_bytes(ctypes.byref(d), n_q, d_model, d_cq))
+
+
+def _ws(workspace, need, device):
+    import torch
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return workspace, nbytes
+
+
+def q_up(d: MlaDims, c_q, w_uq, q_c=None, workspace=None, stream=None):
+    """q^C = W^UQ c^Q: c_q [n_q, d_cq], w_uq [n_h, d_h, d_cq] -> [n_q, n_h, d_h] bf16."""
+    import torch
+    n_q, d_cq = c_q.shape
+    if q_c is None:
+        q_c = torch.empty((n_q, d.n_h, d.d_h), dtype=torch.bfloat16, device=c_q.device)
+    ws, nb = _ws(workspace, proj_workspace_bytes(d, n_q, d.d_c, d_cq), c_q.device)
+    _check("mla_q_up", load().mla_q_up(ctypes.byref(d), n_q, d_cq, _ptr(c_q), _ptr(w_uq), _ptr(q_c), _ptr(ws), nb,
+                                       _stream(stream)))
+    return q_c
+
+
+def fold_q(d: MlaDims, w_uq, w_uk, g=None, stream=None):
+    """G_i = (W^UK_i)^T W^UQ_i -> [n_h, d_c, d_cq] bf16."""
+    import torch
+    d_cq = w_uq.shape[2]
+    if g is None:
+        g = torch.empty((d.n_h, d.d_c, d_cq), dtype=torch.bfloat16, device=w_uq.device)
+    _check("mla_fold_q", load().mla_fold_q(ctypes.byref(d), d_cq, _ptr(w_uq), _ptr(w_uk), _ptr(g), _stream(stream)))
+    return g
+
+
+def absorb_q_folded(d: MlaDims, c_q, g, q_r, q_abs=None, stream=None):
+    """q_abs[n, i] = [G_i c^Q[n] ; q_r[n, i]] -> [n_q, n_h, d_c + d_r] bf16."""
+    import torch
+    n_q, d_cq = c_q.shape
+    if q_abs is None:
+        q_abs = torch.empty((n_q, d.n_h, d.d_c + d.d_r), dtype=torch.bfloat16, device=c_q.device)
+    _check("mla_absorb_q_folded", load().mla_absorb_q_folded(ctypes.byref(d), n_q, d_cq, _ptr(c_q), _ptr(g),
+                                                              _ptr(q_r), _ptr(q_abs), _stream(stream)))
+    return q_abs
+
+
+def o_proj(d: MlaDims, o_c, w_o, u=None, workspace=None, stream=None):
+    """u = W^O [o^C_1; ...; o^C_nh]: o_c [n_q, n_h, d_h], w_o [d_model, n_h d_h] -> [n_q, d_model]."""
+    import torch
+    n_q = o_c.shape[0]
+    d_model = w_o.shape[0]
+    if u is None:
+        u = torch.empty((n_q, d_model), dtype=torch.bfloat16, device=o_c.device)
+    ws, nb = _ws(workspace, proj_workspace_bytes(d, n_q, d_model, 128), o_c.device)
+    _check("mla_o_proj", load().mla_o_proj(ctypes.byref(d), n_q, d_model, _ptr(o_c), _ptr(w_o), _ptr(u), _ptr(ws),
+                                           nb, _stream(stream)))
+    return u
+
+
+def fold_o(d: MlaDims, w_o, w_uv, w_fold=None, stream=None):
+    """W'^O_i = W^O_i W^UV_i side by side -> [d_model, n_h d_c] bf16."""
+    import torch
+    d_model = w_o.shape[0]
+    if w_fold is None:
+        w_fold = torch.empty((d_model, d.n_h * d.d_c), dtype=torch.bfloat16, device=w_o.device)
+    _check("mla_fold_o", load().mla_fold_o(ctypes.byref(d), d_model, _ptr(w_o), _ptr(w_uv), _ptr(w_fold),
+                                           _stream(stream)))
+    return w_fold
+
+
+def out_folded(d: MlaDims, o_lat, w_fold, u=None, workspace=None, stream=None):
+    """u = W'^O [o_lat_1; ...]: o_lat [n_q, n_h, d_c] fp32 -> [n_q, d_model] bf16."""
+    import torch
+    n_q = o_lat.shape[0]
+    d_model = w_fold.shape[0]
+    if u is None:
+        u = torch.empty((n_q, d_model), dtype=torch.bfloat16, device=o_lat.device)
+    ws, nb = _ws(workspace, proj_workspace_bytes(d, n_q, d_model, 128), o_lat.device)
+    _check("mla_out_folded", load().mla_out_folded(ctypes.byref(d), n_q, d_model, _ptr(o_lat), _ptr(w_fold), _ptr(u),
+                                                   _ptr(ws), nb, _stream(stream)))
+    return u
 
 
 def rope_softmax_scale(d: MlaDims, rope: Optional[MlaRope] = None) -> float:

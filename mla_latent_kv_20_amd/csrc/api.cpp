@@ -48,6 +48,18 @@ hipError_t launch_decode_fp8(const bf16_bits* q_abs, const uint8_t* codes, int64
                              const int64_t* offsets, void* o_part, bool f16_partials, float* lse_part, int batch,
                              int q_per_seq, int n_h, int num_splits, int split_rows, float scale,
                              hipStream_t stream);
+// fold.hip
+bool gemm_xwt_supported(int N, int K);
+size_t gemm_xwt_workspace_bytes(int M, int N, int K, int batch);
+hipError_t launch_gemm_xwt(bool x_f32, const void* x, int64_t ldx, int64_t bsx, const bf16_bits* w, int64_t ldw,
+                           int64_t bsw, bf16_bits* out, int64_t ldo, int64_t bso, float* ws, int M, int N, int K,
+                           int batch, bool allow_split, hipStream_t stream);
+hipError_t launch_copy_rope(const bf16_bits* q_r, bf16_bits* q_abs, int n_q, int n_h, int d_c, int d_r,
+                            hipStream_t stream);
+hipError_t launch_fold_q(const bf16_bits* w_uq, const bf16_bits* w_uk, bf16_bits* g, int n_h, int d_h, int d_c,
+                         int d_cq, hipStream_t stream);
+hipError_t launch_fold_o(const bf16_bits* w_o, const bf16_bits* w_uv, bf16_bits* wf, int n_h, int d_h, int d_c,
+                         int d_model, hipStream_t stream);
 size_t decode_f32_smem_bytes(int d_c, int d_r);
 hipError_t launch_decode_f32(const float* q_abs, const float* c_kv, int64_t c_stride, const float* k_r,
                              int64_t r_stride, const int64_t* offsets, float* o_part, float* lse_part,
@@ -312,6 +324,131 @@ mla_status_t mla_decode_fp8(const mla_dims_t* dims, int32_t batch, int32_t q_per
   return launched(mla::launch_decode_fp8((const uint16_t*)q_abs, codes, code_stride, scales, seq_offsets, o_part,
                                          partial_dtype == MLA_F16, lse_part, batch, q_per_seq, dims->n_h,
                                          num_splits, split_rows, scale_of(dims), stream));
+}
+
+namespace {
+// Shared checks of the folding calls: bf16 dims, sizes in range.
+mla_status_t fold_dims(const mla_dims_t* dims) {
+  const mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  return dims->dtype == MLA_BF16 ? MLA_OK : MLA_ERR_UNSUPPORTED;
+}
+bool big(int64_t a, int64_t b) { return a * b >= kMaxElems; }
+}  // namespace
+
+size_t mla_proj_workspace_bytes(const mla_dims_t* dims, int32_t n_q, int32_t d_model, int32_t d_cq) {
+  if (fold_dims(dims) != MLA_OK || n_q <= 0 || d_model <= 0 || d_cq <= 0) return 0;
+  const int hd = dims->n_h * dims->d_h, hc = dims->n_h * dims->d_c;
+  size_t need = 0;
+  if (mla::gemm_xwt_supported(hd, d_cq)) need = mla::gemm_xwt_workspace_bytes(n_q, hd, d_cq, 1);
+  if (mla::gemm_xwt_supported(d_model, hd)) {
+    const size_t b = mla::gemm_xwt_workspace_bytes(n_q, d_model, hd, 1);
+    need = b > need ? b : need;
+  }
+  if (mla::gemm_xwt_supported(d_model, hc)) {
+    const size_t b = mla::gemm_xwt_workspace_bytes(n_q, d_model, hc, 1);
+    need = b > need ? b : need;
+  }
+  return need;
+}
+
+mla_status_t mla_q_up(const mla_dims_t* dims, int32_t n_q, int32_t d_cq, const void* c_q, const void* w_uq,
+                      void* q_c, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  mla_status_t st = fold_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_q < 0 || d_cq < 1) return MLA_ERR_SHAPE;
+  const int hd = dims->n_h * dims->d_h;
+  if (!mla::gemm_xwt_supported(hd, d_cq)) return MLA_ERR_UNSUPPORTED;
+  if (n_q == 0) return MLA_OK;
+  if (!c_q || !w_uq || !q_c) return MLA_ERR_NULL;
+  if (big(n_q, d_cq) || big(hd, d_cq) || big(n_q, hd)) return MLA_ERR_SHAPE;
+  if (!aligned(c_q, 16) || !aligned(w_uq, 16) || !aligned(q_c, 2)) return MLA_ERR_ALIGN;
+  const size_t need = mla::gemm_xwt_workspace_bytes(n_q, hd, d_cq, 1);
+  if (need && (!workspace || workspace_bytes < need)) return workspace ? MLA_ERR_SHAPE : MLA_ERR_NULL;
+  if (need && !aligned(workspace, 4)) return MLA_ERR_ALIGN;
+  return launched(mla::launch_gemm_xwt(false, c_q, d_cq, 0, (const uint16_t*)w_uq, d_cq, 0, (uint16_t*)q_c, hd, 0,
+                                       (float*)workspace, n_q, hd, d_cq, 1, true, stream));
+}
+
+mla_status_t mla_fold_q(const mla_dims_t* dims, int32_t d_cq, const void* w_uq, const void* w_uk, void* g,
+                        hipStream_t stream) {
+  mla_status_t st = fold_dims(dims);
+  if (st != MLA_OK) return st;
+  if (d_cq < 1) return MLA_ERR_SHAPE;
+  if (!w_uq || !w_uk || !g) return MLA_ERR_NULL;
+  if (big((int64_t)dims->n_h * dims->d_c, d_cq) || big((int64_t)dims->n_h * dims->d_h, d_cq)) return MLA_ERR_SHAPE;
+  if (!aligned(w_uq, 2) || !aligned(w_uk, 2) || !aligned(g, 2)) return MLA_ERR_ALIGN;
+  return launched(mla::launch_fold_q((const uint16_t*)w_uq, (const uint16_t*)w_uk, (uint16_t*)g, dims->n_h,
+                                     dims->d_h, dims->d_c, d_cq, stream));
+}
+
+mla_status_t mla_absorb_q_folded(const mla_dims_t* dims, int32_t n_q, int32_t d_cq, const void* c_q,
+                                 const void* g, const void* q_r, void* q_abs, hipStream_t stream) {
+  mla_status_t st = fold_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_q < 0 || d_cq < 1) return MLA_ERR_SHAPE;
+  if (!mla::gemm_xwt_supported(dims->d_c, d_cq)) return MLA_ERR_UNSUPPORTED;
+  if (n_q == 0) return MLA_OK;
+  if (!c_q || !g || !q_r || !q_abs) return MLA_ERR_NULL;
+  const int64_t d_qk = (int64_t)dims->d_c + dims->d_r;
+  if (big(n_q, d_cq) || big((int64_t)dims->n_h * dims->d_c, d_cq) || big((int64_t)n_q * dims->n_h, d_qk))
+    return MLA_ERR_SHAPE;
+  if (!aligned(c_q, 16) || !aligned(g, 16) || !aligned(q_r, 2) || !aligned(q_abs, 2)) return MLA_ERR_ALIGN;
+  st = launched(mla::launch_gemm_xwt(false, c_q, d_cq, 0, (const uint16_t*)g, d_cq, (int64_t)dims->d_c * d_cq,
+                                     (uint16_t*)q_abs, dims->n_h * d_qk, d_qk, nullptr, n_q, dims->d_c, d_cq,
+                                     dims->n_h, false, stream));
+  if (st != MLA_OK) return st;
+  return launched(mla::launch_copy_rope((const uint16_t*)q_r, (uint16_t*)q_abs, n_q, dims->n_h, dims->d_c,
+                                        dims->d_r, stream));
+}
+
+mla_status_t mla_o_proj(const mla_dims_t* dims, int32_t n_q, int32_t d_model, const void* o_c, const void* w_o,
+                        void* u, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  mla_status_t st = fold_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_q < 0 || d_model < 1) return MLA_ERR_SHAPE;
+  const int hd = dims->n_h * dims->d_h;
+  if (!mla::gemm_xwt_supported(d_model, hd)) return MLA_ERR_UNSUPPORTED;
+  if (n_q == 0) return MLA_OK;
+  if (!o_c || !w_o || !u) return MLA_ERR_NULL;
+  if (big(n_q, hd) || big(d_model, hd) || big(n_q, d_model)) return MLA_ERR_SHAPE;
+  if (!aligned(o_c, 16) || !aligned(w_o, 16) || !aligned(u, 2)) return MLA_ERR_ALIGN;
+  const size_t need = mla::gemm_xwt_workspace_bytes(n_q, d_model, hd, 1);
+  if (need && (!workspace || workspace_bytes < need)) return workspace ? MLA_ERR_SHAPE : MLA_ERR_NULL;
+  if (need && !aligned(workspace, 4)) return MLA_ERR_ALIGN;
+  return launched(mla::launch_gemm_xwt(false, o_c, hd, 0, (const uint16_t*)w_o, hd, 0, (uint16_t*)u, d_model, 0,
+                                       (float*)workspace, n_q, d_model, hd, 1, true, stream));
+}
+
+mla_status_t mla_fold_o(const mla_dims_t* dims, int32_t d_model, const void* w_o, const void* w_uv, void* w_fold,
+                        hipStream_t stream) {
+  mla_status_t st = fold_dims(dims);
+  if (st != MLA_OK) return st;
+  if (d_model < 1) return MLA_ERR_SHAPE;
+  if (!w_o || !w_uv || !w_fold) return MLA_ERR_NULL;
+  if (big(d_model, (int64_t)dims->n_h * dims->d_c) || big(d_model, (int64_t)dims->n_h * dims->d_h)) return MLA_ERR_SHAPE;
+  if (!aligned(w_o, 2) || !aligned(w_uv, 2) || !aligned(w_fold, 2)) return MLA_ERR_ALIGN;
+  return launched(mla::launch_fold_o((const uint16_t*)w_o, (const uint16_t*)w_uv, (uint16_t*)w_fold, dims->n_h,
+                                     dims->d_h, dims->d_c, d_model, stream));
+}
+
+mla_status_t mla_out_folded(const mla_dims_t* dims, int32_t n_q, int32_t d_model, const float* o_lat,
+                            const void* w_fold, void* u, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  mla_status_t st = fold_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_q < 0 || d_model < 1) return MLA_ERR_SHAPE;
+  const int hc = dims->n_h * dims->d_c;
+  if (!mla::gemm_xwt_supported(d_model, hc)) return MLA_ERR_UNSUPPORTED;
+  if (n_q == 0) return MLA_OK;
+  if (!o_lat || !w_fold || !u) return MLA_ERR_NULL;
+  if (big(n_q, hc) || big(d_model, hc) || big(n_q, d_model)) return MLA_ERR_SHAPE;
+  if (!aligned(o_lat, 16) || !aligned(w_fold, 16) || !aligned(u, 2)) return MLA_ERR_ALIGN;
+  const size_t need = mla::gemm_xwt_workspace_bytes(n_q, d_model, hc, 1);
+  if (need && (!workspace || workspace_bytes < need)) return workspace ? MLA_ERR_SHAPE : MLA_ERR_NULL;
+  if (need && !aligned(workspace, 4)) return MLA_ERR_ALIGN;
+  return launched(mla::launch_gemm_xwt(true, o_lat, hc, 0, (const uint16_t*)w_fold, hc, 0, (uint16_t*)u, d_model, 0,
+                                       (float*)workspace, n_q, d_model, hc, 1, true, stream));
 }
 
 mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t n_q, int32_t num_splits,

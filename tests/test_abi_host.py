@@ -37,7 +37,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert set(names) == set(B.SIGNATURES), names
     for n in names:
         assert hasattr(lib, n)
-    assert lib.mla_abi_version() == 6
+    assert lib.mla_abi_version() == 7
 
 
 def test_status_strings(lib):
@@ -222,6 +222,41 @@ def test_quantized_cache_argument_checks(lib):
     assert dec(d, sc=FAKE + 2) == B.MLA_ERR_ALIGN
     assert dec(d, qa=FAKE + 8) == B.MLA_ERR_ALIGN
     assert dec(d, off=FAKE + 4) == B.MLA_ERR_ALIGN
+
+
+def test_folding_argument_checks(lib):
+    d = dims()
+    by = ctypes.byref
+    ws = lib.mla_proj_workspace_bytes(by(d), 32, 5120, 1536)
+    assert ws > 0 and ws % 4 == 0
+    assert lib.mla_proj_workspace_bytes(by(dims(dtype=B.MLA_F32)), 32, 5120, 1536) == 0
+    qup = lambda d, n=32, dcq=1536, cq=FAKE, w=FAKE, out=FAKE, w_s=FAKE, nb=1 << 30: \
+        lib.mla_q_up(by(d), n, dcq, cq, w, out, w_s, nb, None)
+    assert qup(d, n=0, cq=None, w=None, out=None, w_s=None, nb=0) == B.MLA_OK
+    assert qup(d, n=-1) == B.MLA_ERR_SHAPE
+    assert qup(d, dcq=1500) == B.MLA_ERR_UNSUPPORTED                 # multiples of 128
+    assert qup(dims(dtype=B.MLA_F32)) == B.MLA_ERR_UNSUPPORTED
+    assert qup(d, cq=None) == B.MLA_ERR_NULL
+    assert qup(d, w_s=None, nb=0) == B.MLA_ERR_NULL                 # the split needs a workspace
+    assert qup(d, nb=8) == B.MLA_ERR_SHAPE
+    assert qup(d, cq=FAKE + 8) == B.MLA_ERR_ALIGN
+    fq = lambda d, dcq=1536, a=FAKE, b=FAKE, g=FAKE: lib.mla_fold_q(by(d), dcq, a, b, g, None)
+    assert fq(d, dcq=0) == B.MLA_ERR_SHAPE and fq(d, g=None) == B.MLA_ERR_NULL and fq(d, a=FAKE + 1) == B.MLA_ERR_ALIGN
+    aqf = lambda d, n=32, dcq=1536, cq=FAKE, g=FAKE, qr=FAKE, out=FAKE: \
+        lib.mla_absorb_q_folded(by(d), n, dcq, cq, g, qr, out, None)
+    assert aqf(d, n=0, cq=None, g=None, qr=None, out=None) == B.MLA_OK
+    assert aqf(d, qr=None) == B.MLA_ERR_NULL and aqf(d, g=FAKE + 4) == B.MLA_ERR_ALIGN
+    assert aqf(dims(d_c=200)) == B.MLA_ERR_UNSUPPORTED
+    op = lambda d, n=32, dm=5120, oc=FAKE, w=FAKE, u=FAKE, w_s=FAKE, nb=1 << 30: \
+        lib.mla_o_proj(by(d), n, dm, oc, w, u, w_s, nb, None)
+    assert op(d, dm=5000) == B.MLA_ERR_UNSUPPORTED and op(d, u=None) == B.MLA_ERR_NULL
+    assert op(d, oc=FAKE + 2) == B.MLA_ERR_ALIGN and op(d, dm=0) == B.MLA_ERR_SHAPE
+    fo = lambda d, dm=5120, a=FAKE, b=FAKE, wf=FAKE: lib.mla_fold_o(by(d), dm, a, b, wf, None)
+    assert fo(d, dm=0) == B.MLA_ERR_SHAPE and fo(d, wf=None) == B.MLA_ERR_NULL
+    of = lambda d, n=32, dm=5120, ol=FAKE, wf=FAKE, u=FAKE, w_s=FAKE, nb=1 << 30: \
+        lib.mla_out_folded(by(d), n, dm, ol, wf, u, w_s, nb, None)
+    assert of(d, ol=FAKE + 4) == B.MLA_ERR_ALIGN and of(d, wf=None) == B.MLA_ERR_NULL
+    assert of(d, w_s=FAKE + 2) == B.MLA_ERR_ALIGN and of(dims(dtype=B.MLA_F32)) == B.MLA_ERR_UNSUPPORTED
 
 
 def test_partial_bytes(lib):
