@@ -40,6 +40,7 @@ ROW_BYTES = 1152               # one cached latent row [c_KV 512 ; k_R 64] in bf
 FLOP_PER_ROW_HEAD = 2 * 576 + 2 * 512   # score + weighted sum, per (row, query head)
 MALL_BYTES = 256 << 20
 D_MODEL = 5120                 # DeepSeek-V2 hidden width: input of the decode prologue
+D_CQ = 1536                    # DeepSeek-V2 compressed query width (W^UQ's input)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "mla_latent_kv_20_amd", "csrc", f)
                   for f in ("decode_bf16.hip", "mla_common.h")]
@@ -316,6 +317,37 @@ def main():
 
         calls["decode_fp8"] = (fcopies, fp8_decode)
         calls["step_fp8"] = (fcopies, fp8_step)
+    # Weight folding (c^Q -> absorbed query, o_lat -> block output), unfolded against folded,
+    # at DeepSeek-V2's d_cq and d_model; each weight cycles over enough copies to exceed twice
+    # the MALL.
+    fold = d.dtype == B.MLA_BF16 and w.d_c % 128 == 0 and (w.n_h * w.d_h) % 128 == 0
+    if fold:
+        gen = torch.Generator(device=dev).manual_seed(11)
+        bf16 = base["q_c"].dtype
+
+        def randw(shape, fan):
+            return (torch.randn(shape, generator=gen, device=dev) / math.sqrt(fan)).to(bf16)
+
+        def copies_for(nbytes):
+            return max(1, math.ceil(2 * MALL_BYTES / nbytes))
+
+        c_q = torch.randn((n_q, D_CQ), generator=gen, device=dev).to(bf16)
+        ucop = copies_for(w.n_h * w.d_h * D_CQ * esz)
+        w_uq_set = [randw((w.n_h, w.d_h, D_CQ), D_CQ) for _ in range(ucop)]
+        gcop = copies_for(w.n_h * w.d_c * D_CQ * esz)
+        g_set = [B.fold_q(d, w_uq_set[j % ucop], base["w_uk"]) for j in range(gcop)]
+        ocop = copies_for(D_MODEL * w.n_h * w.d_h * esz)
+        w_o_set = [randw((D_MODEL, w.n_h * w.d_h), w.n_h * w.d_h) for _ in range(ocop)]
+        fcop = copies_for(D_MODEL * w.n_h * w.d_c * esz)
+        wf_set = [B.fold_o(d, w_o_set[j % ocop], base["w_uv"]) for j in range(fcop)]
+        torch.cuda.synchronize()
+        q_c_buf = torch.empty((n_q, w.n_h, w.d_h), dtype=bf16, device=dev)
+        u_buf = torch.empty((n_q, D_MODEL), dtype=bf16, device=dev)
+        pws = torch.empty(max(1, B.proj_workspace_bytes(d, n_q, D_MODEL, D_CQ)), dtype=torch.uint8, device=dev)
+        calls["q_up"] = (ucop, lambda j: B.q_up(d, c_q, w_uq_set[j], q_c_buf, pws))
+        calls["absorb_q_folded"] = (gcop, lambda j: B.absorb_q_folded(d, c_q, g_set[j], base["q_r"], bufs["q_abs"]))
+        calls["o_proj"] = (ocop, lambda j: B.o_proj(d, bufs["o_c"], w_o_set[j], u_buf, pws))
+        calls["out_folded"] = (fcop, lambda j: B.out_folded(d, bufs["o_lat"], wf_set[j], u_buf, pws))
     per = {}
     for name, item in calls.items():
         if item is None:
@@ -385,6 +417,7 @@ def main():
                                                       / (per["kv_append"] * 1e-3) / 1e9, 1)},
                       "absorb_q_rope_ms": round(per["absorb_q_rope"], 5)} if prologue else None),
         "fp8_cache": (fp8_summary(w, per, flops, tokens, fcopies) if fp8 else None),
+        "folding": (fold_summary(w, per, esz) if fold else None),
         "decode_merge_tokens_per_s": round(tokens / ((dec_ms + per.get("merge", 0.0)) * 1e-3), 1),
         "timing": "hip graph replay (one graph per pass over the layer copies)" if not args.no_graph else "eager launches",
         "step_calls": ("absorb_q, decode, out_proj (one fp32 split: no merge)" if S == 1 and part == B.MLA_F32
@@ -395,6 +428,26 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def fold_summary(w, per, esz):
+    """Unfolded against folded weights, per step, from c^Q and from o_lat."""
+    uq = w.n_h * w.d_h * D_CQ * esz
+    uk = w.n_h * w.d_h * w.d_c * esz
+    g = w.n_h * w.d_c * D_CQ * esz
+    wo = D_MODEL * w.n_h * w.d_h * esz
+    wf = D_MODEL * w.n_h * w.d_c * esz
+    q_unf = per["q_up"] + per["absorb_q"]
+    o_unf = per["out_proj"] + per["o_proj"]
+    return {"d_cq": D_CQ, "d_model": D_MODEL,
+            "query": {"unfolded_ms": round(q_unf, 5), "q_up_ms": round(per["q_up"], 5),
+                      "absorb_q_ms": round(per["absorb_q"], 5), "folded_ms": round(per["absorb_q_folded"], 5),
+                      "unfolded_weight_bytes": uq + uk, "folded_weight_bytes": g,
+                      "folded_GB_per_s": round(g / (per["absorb_q_folded"] * 1e-3) / 1e9, 1)},
+            "output": {"unfolded_ms": round(o_unf, 5), "out_proj_ms": round(per["out_proj"], 5),
+                       "o_proj_ms": round(per["o_proj"], 5), "folded_ms": round(per["out_folded"], 5),
+                       "unfolded_weight_bytes": uk + wo, "folded_weight_bytes": wf,
+                       "folded_GB_per_s": round(wf / (per["out_folded"] * 1e-3) / 1e9, 1)}}
 
 
 def fp8_summary(w, per, flops, cached, fcopies):

@@ -9,7 +9,7 @@
 // Decode-time products are skinny GEMMs, C[n][m] = sum_k X[n][k] W[m][k] with few rows n (the
 // batch's queries) and a weight W read once: gemm_xwt_kernel streams W rows as MFMA B
 // operands (a row's k values contiguous), X rows as A operands, 32 rows x 32 columns per
-// wave, eight k-steps of loads in flight before their MFMAs.  Long K is split over
+// wave, two batches of eight k-steps of loads alternating with their MFMAs.  Long K is split over
 // workgroups; fp32 partial sums go to a caller workspace and gemm_finish_kernel adds them in
 // slice order.  The folds themselves are offline: plain fp32 kernels.
 #include "mla_common.h"
@@ -65,14 +65,25 @@ gemm_xwt_kernel(GemmParams P) {
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  for (int k = k_begin; k < k_end; k += kGK) {
-    bf16x8 a[kGU], bw[kGU];
+  // two batches of loads: the next batch is in flight while the current one's MFMAs run
+  bf16x8 a[2][kGU], bw[2][kGU];
+  auto fetch = [&](int h, int k) {
 #pragma unroll
-    for (int u = 0; u < kGU; ++u) bw[u] = *(const bf16x8*)(wrow + k + 16 * u);
+    for (int u = 0; u < kGU; ++u) bw[h][u] = *(const bf16x8*)(wrow + k + 16 * u);
 #pragma unroll
-    for (int u = 0; u < kGU; ++u) a[u] = load_x8<kXf32>(P.x, xoff + k + 16 * u);
+    for (int u = 0; u < kGU; ++u) a[h][u] = load_x8<kXf32>(P.x, xoff + k + 16 * u);
+  };
+  auto consume = [&](int h) {
 #pragma unroll
-    for (int u = 0; u < kGU; ++u) acc = mfma32x32x16(a[u], bw[u], acc);
+    for (int u = 0; u < kGU; ++u) acc = mfma32x32x16(a[h][u], bw[h][u], acc);
+  };
+  if (k_begin < k_end) fetch(0, k_begin);
+  for (int k = k_begin; k < k_end; k += 2 * kGK) {
+    const bool more = k + kGK < k_end;
+    if (more) fetch(1, k + kGK);
+    consume(0);
+    if (k + 2 * kGK < k_end) fetch(0, k + 2 * kGK);
+    if (more) consume(1);
   }
   // D[n][m]: lane l, reg r -> row n0 + 8(r/4) + 4(l/32) + r%4, column m0 + l%32
   const int m = m0 + (lane & 31);
