@@ -11,11 +11,11 @@
 //
 // One workgroup = one (query token, split of rows, group of 128 heads); 4 waves,
 // wave w owns heads [32w, 32w+32) of the group, one wave per SIMD.  Per 32-row tile:
-//   * the tile streams HBM -> LDS as 16-byte direct-to-LDS loads, double buffered: the
-//     nine loads of tile t+1 leave together right after the barrier that opens tile t.
-//     (A direct-to-LDS load stalls the issuing wave while the memory pipeline is backed
-//     up, so the loads go out in one burst with the previous tile's already landed, and
-//     only one tile is in flight.)
+//   * the tile streams HBM -> LDS as 16-byte direct-to-LDS loads into a ring of three
+//     stages: the nine loads of tile t+1 leave together right after the barrier that
+//     opens tile t.  (A direct-to-LDS load stalls the issuing wave while the memory
+//     pipeline is backed up, so the loads go out in one burst with the previous tile's
+//     already landed, and only one tile is in flight.)
 //   * S^T[32 rows x 32 heads] = K_tile[32 x 576] . Q^T (36 MFMA 32x32x16), with the
 //     wave's queries resident in VGPRs as MFMA B operands and the scores accumulated in
 //     VGPRs;
@@ -23,6 +23,8 @@
 //     l^32 owns the other 16), max exchanged across the pair;
 //   * O^T[512 dv x 32 heads] += V_tile^T . P^T (32 MFMA), V^T operands read from the
 //     row-major tile with the LDS transpose read, accumulators in AGPRs.
+// The weighted sum of tile t-1 is interleaved with the scores of tile t (one MFMA of
+// each in turn), so two tiles are read while the third stage fills.
 // The softmax works in the log2 domain (scale folded with log2 e) and rescales the
 // accumulators only when a head's running maximum grows by more than 8.
 #include "mla_common.h"
@@ -41,7 +43,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kHeadsPerWg = kWaves * 32;
 constexpr int kLoads = kTile * kChunks / kThreads;            // 9 loads of 1 KiB per wave per tile
-constexpr int kStages = 2;
+constexpr int kStages = 3;              // tile ring: scores of t, weighted sum of t-1, loads of t+1
 constexpr int kKSteps = kDqk / 16;       // 36 MFMA k-steps for the scores
 constexpr int kKReg = kDc / 16;          // 32 k-steps of the latent part (then 4 of the RoPE part)
 constexpr int kQStageWave = 32 * 512;    // query staging per wave: 32 heads x 256 columns bf16
@@ -56,6 +58,20 @@ constexpr int kWaitVmcnt0 = 0x0F70;      // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt
 static_assert(kTile * kChunks == kLoads * kThreads, "tile must split evenly into 1 KiB loads");
 static_assert(kKSteps == 4 * kLoads, "one tile load per 4 score steps");
 static_assert(kKSteps - kKReg == 4, "RoPE part: 4 k-steps of 16");
+static_assert(kTileBytes + kWaves * kQStageWave <= kStages * kTileBytes, "query staging fits in stages 1-2");
+
+// Issue order of the score k-steps when they are interleaved with the weighted sum: the
+// latent steps 0..31 in order (one accumulator chain), the 4 RoPE steps (a second chain)
+// placed between the last latent ones, so that no two dependent MFMAs are adjacent.
+__host__ __device__ constexpr int s_order(int p) {
+  return p <= 28 ? p : (((p - 29) & 1) ? 29 + (p - 30) / 2 : 32 + (p - 29) / 2);
+}
+
+// First MFMA of a score chain: the accumulator source is the constant 0, so no zeroed
+// registers are needed (the destination must not overlap the operands).
+__device__ __forceinline__ void mfma_first_vgpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
 
 struct DecodeParams {
   const bf16_bits* q_abs;       // [n_q, n_h, 576]
@@ -293,10 +309,11 @@ mla_decode_bf16_kernel(DecodeParams P) {
   // issued together: half 0 through an LDS staging area with direct-to-LDS loads, each
   // instruction reading two contiguous 512-byte half-rows, and half 1 with the 64 RoPE
   // columns straight into registers in the MFMA layout (32 rows per instruction; the
-  // staging area has room for one half only).  In the staging area, wave w owns heads
+  // staging area has room for one half only).  The staging area lies in tile stages 1-2,
+  // which take no loads before the barrier that opens tile 0.  In it, wave w owns heads
   // 32w .. 32w+31 at 512 bytes each, chunk c of head h stored at chunk c ^ (h & 15).
   bf16x8 qb[kKSteps];
-  char* qstage = smem + kStages * kTileBytes + wave * kQStageWave;
+  char* qstage = smem + kTileBytes + wave * kQStageWave;
   const char* qbase = (const char*)(P.q_abs + ((size_t)n * P.n_h + hg * kHeadsPerWg) * kDqk);
   uint32_t qoff[kQStageLoads / 2];               // per-lane source offsets of half 0
 #pragma unroll
@@ -371,65 +388,54 @@ mla_decode_bf16_kernel(DecodeParams P) {
     }
   const int row_base = 4 * (lane >> 5);        // S^T rows held: 8(i/4) + row_base + i%4
 
-  for (int t = 0; t < ntiles; ++t) {
-    // tile t resident in LDS for every wave; the stage of tile t-1 is free
-    if (t + 1 < ntiles) wait_tile<kStages - 2>();
-    else wait_tile<0>();
-    lds_barrier();
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  bf16x8 pb0, pb1;                     // P^T operands of the tile whose weighted sum is next
+  // A growing maximum rescales acc just before the next weighted-sum MFMAs rather than in
+  // the softmax: rescaling at the end of an iteration makes the compiler copy the whole
+  // accumulator around the loop.
+  float r_alpha = 1.f;
+  bool r_pending = false;              // wave-uniform
+  auto apply_rescale = [&]() {
+    if (r_pending) {
+      asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");   // MFMA results in acc settled
+#pragma unroll
+      for (int tt = 0; tt < kDvTiles; ++tt) scale_acc_agpr(acc[tt], r_alpha);
+      r_pending = false;
+    }
+  };
 
+  // Top of tile t: every wave's loads of tile t have landed; stage (t+1) % 3 held tile t-2,
+  // read for the last time before this barrier, and takes tile t+1's loads now.
+  auto open_tile = [&](int t) {
+    wait_tile<0>();
+    lds_barrier();
     // Hide the load-offset inputs from loop-invariant hoisting: recomputing an offset
     // costs two VALU ops, keeping nine of them live would cost nine VGPRs we do not have.
     uint32_t dd0 = d0, dd1 = d1, ln16 = lane16;
     int lane_v = lane;
     asm volatile("" : "+v"(dd0), "+v"(dd1), "+v"(ln16), "+v"(lane_v));
-
-    const char* tile = smem + (t % kStages) * kTileBytes;
-    const int tn = t + kStages - 1;              // tile whose loads go out now
+    const int tn = t + 1;
     if (tn < ntiles) {
       const char* next_src = first_row + (int64_t)tn * kTile * stride_bytes;
       char* next_stage = smem + (tn % kStages) * kTileBytes;
       if (contiguous && (tn < ntiles - 1 || last_full)) {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) load_fast(next_src, next_stage, wave, i, dd0, dd1, ln16);
-      } else {                                   // any stride or a partial tile
+      } else {                                 // any stride or a partial tile
         const int rmax = last_rel - tn * kTile < kTile - 1 ? last_rel - tn * kTile : kTile - 1;
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) load_clamped(next_src, stride_bytes, rmax, next_stage, wave, i, lane_v);
       }
     }
+  };
 
-    // ---- scores S^T = K . Q^T; K operands kKAhead steps ahead;
-    // two accumulation chains (even / odd k-steps): a dependent MFMA chain issues at about
-    // 60 cycles per step, two interleaved chains at the MFMA rate (about 37).  The score
-    // accumulators stay in VGPRs (inline-assembly MFMAs) so that the AGPRs hold all of acc.
-    f32x16 st, st1;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      st[i] = 0.f;
-      st1[i] = 0.f;
-    }
-    bf16x8 ka[kKSteps];
-#pragma unroll
-    for (int ks = 0; ks < kKAhead; ++ks)
-      ka[ks] = *(const bf16x8*)(tile + kb[ks & 3] + 128 * (ks >> 2));
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      if (ks + kKAhead < kKSteps) {
-        const int kn = ks + kKAhead;
-        ka[kn] = *(const bf16x8*)(tile + kb[kn & 3] + 128 * (kn >> 2));
-      }
-      const bf16x8 qop = qb[ks];
-      if (ks & 1) mfma_acc_vgpr(st1, ka[ks], qop);
-      else mfma_acc_vgpr(st, ka[ks], qop);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    mfma_vgpr_drain2(st, st1);
-    st += st1;
-
-    // ---- online softmax (log2 domain)
-    const int rem = last_rel - t * kTile;        // rows of this tile with index <= rem count
-    if (rem < kTile - 1) {                       // partial tile: drop the rows past the end
+  // ---- online softmax of tile t (log2 domain): scores -> pb0, pb1
+  auto softmax = [&](int t, f32x16 st) {
+    // No contraction: exp2(s - m) must be exactly 1 where s is the maximum, so the scaled
+    // score and the maximum must be the same rounded product.
+#pragma clang fp contract(off)
+    const int rem = last_rel - t * kTile;      // rows of this tile with index <= rem count
+    if (rem < kTile - 1) {                     // partial tile: drop the rows past the end
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 8 * (i >> 2) + row_base + (i & 3);
@@ -439,7 +445,7 @@ mla_decode_bf16_kernel(DecodeParams P) {
     float mt = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      st[i] *= P.scale_log2;                     // -inf stays -inf (the scale is positive)
+      st[i] *= P.scale_log2;                   // -inf stays -inf (the scale is positive)
       mt = fmaxf(mt, st[i]);
     }
     mt = pair_max(mt);
@@ -448,10 +454,9 @@ mla_decode_bf16_kernel(DecodeParams P) {
       m_ref = mt;                      // accumulators and l_run are still zero: nothing to rescale
     } else if (__any(grow)) {
       const float m_new = grow ? mt : m_ref;
-      const float alpha = fast_exp2(m_ref - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int tt = 0; tt < kDvTiles; ++tt) scale_acc_agpr(acc[tt], alpha);
+      r_alpha = fast_exp2(m_ref - m_new);
+      l_run *= r_alpha;
+      r_pending = true;
       m_ref = m_new;
     }
     uint32_t pw[8];
@@ -462,17 +467,92 @@ mla_decode_bf16_kernel(DecodeParams P) {
       l_run += p0 + p1;
       pw[i >> 1] = pack_bf16x2(p0, p1);
     }
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const bf16x8 pb0 = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-    const bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+    pb0 = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+    pb1 = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+  };
 
-    // ---- O^T += V^T . P^T: 2 row k-steps x 16 dv tiles, V^T operands read kVAhead ahead
+  // ---- tile 0: scores alone, K operands kKAhead steps ahead, two accumulation chains
+  // (even / odd k-steps): a dependent MFMA chain issues at about 60 cycles per step, two
+  // interleaved chains at the MFMA rate.  The score accumulators stay in VGPRs
+  // (inline-assembly MFMAs) so that the AGPRs hold all of acc.
+  open_tile(0);
+  {
+    f32x16 st, st1;
+    bf16x8 ka[kKSteps];
+#pragma unroll
+    for (int ks = 0; ks < kKAhead; ++ks) ka[ks] = *(const bf16x8*)(smem + kb[ks & 3] + 128 * (ks >> 2));
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      if (ks + kKAhead < kKSteps) {
+        const int kn = ks + kKAhead;
+        ka[kn] = *(const bf16x8*)(smem + kb[kn & 3] + 128 * (kn >> 2));
+      }
+      if (ks == 0) mfma_first_vgpr(st, ka[ks], qb[ks]);
+      else if (ks == 1) mfma_first_vgpr(st1, ka[ks], qb[ks]);
+      else if (ks & 1) mfma_acc_vgpr(st1, ka[ks], qb[ks]);
+      else mfma_acc_vgpr(st, ka[ks], qb[ks]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_vgpr_drain2(st, st1);
+    softmax(0, st + st1);
+  }
+
+  // ---- tiles 1..ntiles-1: scores of tile t interleaved with the weighted sum of tile t-1,
+  // O^T += V^T . P^T over 2 row k-steps x 16 dv tiles: S step, O step, S step, ...
+  for (int t = 1; t < ntiles; ++t) {
+    open_tile(t);
+    const char* tile = smem + (t % kStages) * kTileBytes;
+    const char* otile = smem + ((t + kStages - 1) % kStages) * kTileBytes;
+    // Fresh copies of the lane's operand addresses every tile: otherwise the compiler
+    // hoists each (address + step offset) out of the loop, one register each.
+    int kbl[4], vbl[2][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kbl[j] = kb[j];
+    vbl[0][0] = vb[0][0];
+    vbl[0][1] = vb[0][1];
+    vbl[1][0] = vb[1][0];
+    vbl[1][1] = vb[1][1];
+    asm volatile("" : "+v"(kbl[0]), "+v"(kbl[1]), "+v"(kbl[2]), "+v"(kbl[3]), "+v"(vbl[0][0]), "+v"(vbl[0][1]),
+                 "+v"(vbl[1][0]), "+v"(vbl[1][1]));
+    auto kread = [&](int ks) -> bf16x8 { return *(const bf16x8*)(tile + kbl[ks & 3] + 128 * (ks >> 2)); };
+    apply_rescale();
+    f32x16 st, st1;
+    bf16x8 ka[kKSteps];
     bf16x8 va[2 * kDvTiles];
 #pragma unroll
-    for (int u = 0; u < kVAhead; ++u) va[u] = load_vt(tile, vb, u);
+    for (int p = 0; p < kKAhead; ++p) ka[s_order(p)] = kread(s_order(p));
+#pragma unroll
+    for (int u = 0; u < kVAhead; ++u) va[u] = load_vt(otile, vbl, u);
+#pragma unroll
+    for (int p = 0; p < kKSteps; ++p) {
+      if (p + kKAhead < kKSteps) ka[s_order(p + kKAhead)] = kread(s_order(p + kKAhead));
+      const int ks = s_order(p);
+      if (ks == 0) mfma_first_vgpr(st, ka[ks], qb[ks]);
+      else if (ks == kKReg) mfma_first_vgpr(st1, ka[ks], qb[ks]);
+      else if (ks < kKReg) mfma_acc_vgpr(st, ka[ks], qb[ks]);
+      else mfma_acc_vgpr(st1, ka[ks], qb[ks]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks < kKReg) {                        // O step u = ks
+        const int u = ks;
+        if (u + kVAhead < 2 * kDvTiles) va[u + kVAhead] = load_vt(otile, vbl, u + kVAhead);
+        acc[u % kDvTiles] = mfma32x32x16(va[u], u < kDvTiles ? pb0 : pb1, acc[u % kDvTiles]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    mfma_vgpr_drain2(st, st1);
+    softmax(t, st + st1);
+  }
+
+  // ---- the last tile's weighted sum
+  {
+    apply_rescale();
+    const char* otile = smem + ((ntiles - 1) % kStages) * kTileBytes;
+    bf16x8 va[2 * kDvTiles];
+#pragma unroll
+    for (int u = 0; u < kVAhead; ++u) va[u] = load_vt(otile, vb, u);
 #pragma unroll
     for (int u = 0; u < 2 * kDvTiles; ++u) {
-      if (u + kVAhead < 2 * kDvTiles) va[u + kVAhead] = load_vt(tile, vb, u + kVAhead);
+      if (u + kVAhead < 2 * kDvTiles) va[u + kVAhead] = load_vt(otile, vb, u + kVAhead);
       acc[u % kDvTiles] = mfma32x32x16(va[u], u < kDvTiles ? pb0 : pb1, acc[u % kDvTiles]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -546,7 +626,7 @@ hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* rows, int
   P.seqs_per_xcd = batch >= 16 ? (batch + 7) / 8 : 0;
   P.streams_per_xcd = P.seqs_per_xcd > 0 ? P.seqs_per_xcd * num_splits : (P.streams + 7) / 8;
   P.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  size_t smem = (size_t)kStages * kTileBytes + (size_t)kWaves * kQStageWave;
+  size_t smem = (size_t)kStages * kTileBytes;   // the query staging area lies inside the ring
   const size_t out_stage = (size_t)kWaves * 32 * (f16_partials ? out_row_bytes<_Float16>() : out_row_bytes<float>());
   smem = smem > out_stage ? smem : out_stage;
   if (P.seqs_per_xcd > 0 && (size_t)(2 * (batch + 3)) * sizeof(int) > smem) {   // lengths and ranks do not fit in LDS
