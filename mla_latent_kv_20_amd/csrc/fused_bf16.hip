@@ -23,6 +23,7 @@ constexpr int kFDc = 512;                    // latent width handled (one 512-wi
 constexpr int kFPitch = kFDc * 2 + 16;       // bf16 o_lat row in LDS, padded against conflicts
 constexpr int kFSteps = kFDc / 64;           // k-steps of 16 per wave: a quarter of d_c
 constexpr int kFFast = 8;                    // splits whose loads all go out at once
+constexpr int kFWRowBytes = kFDc * 2;        // one W^UV row (bf16)
 
 struct FusedParams {
   const void* o_part;      // [S, n_q, n_h, 512] fp16 or fp32
@@ -217,8 +218,10 @@ __device__ __forceinline__ void merge_rows_fast(const PartT* o_part, const float
 
 // Workgroup = (head i, block of 16 query rows); workgroups are dealt round-robin over the
 // 8 XCDs and all query blocks of head i run on XCD i % 8, so W^UV_i is fetched into one L2.
-// Each of the 8 waves merges 2 of the block's rows (every load in flight at once) into
-// LDS as bf16.  The projection then runs as in mla_out_proj: for each 32-column block of
+// W^UV_i (128 KiB) first streams into LDS with direct-to-LDS loads of one whole 1 KiB row
+// each; read straight into the MFMA operand layout, every load instruction would touch 32
+// rows at 32 bytes each (16.5 against 15.3 us at 32 queries).  Each of the 8 waves then
+// merges 2 of the block's rows (every load in flight at once) into LDS as bf16.  The projection then runs as in mla_out_proj: for each 32-column block of
 // d_h, four k quarters of 8 MFMA steps summed in quarter order; wave w computes column
 // block (w & 3) for quarters (w >> 2) and (w >> 2) + 2.  The MFMA M dimension is 32, so
 // rows 16-31 of each product repeat rows 0-15 and are not stored.
@@ -228,8 +231,12 @@ constexpr int kFColBlocks = 4;               // 32-column blocks of d_h = 128
 template <typename PartT>
 __global__ void __launch_bounds__(kFThreads)
 merge_out_proj_kernel(FusedParams P) {
-  __shared__ __attribute__((aligned(16))) char o_lds[kFRows * kFPitch];
-  __shared__ f32x16 red[4][kFColBlocks][64];     // [k quarter][column block][lane]
+  // LDS: W^UV_i (d_h rows of 1 KiB, chunk c of row r at c ^ (r & 15)), reused for the
+  // k-quarter partial products once the MFMAs have read it; then o_lat rows (bf16)
+  extern __shared__ __attribute__((aligned(1024))) char smem_f[];
+  char* w_lds = smem_f;
+  char* o_lds = smem_f + 32 * kFColBlocks * kFWRowBytes;
+  f32x16 (*red)[kFColBlocks][64] = (f32x16 (*)[kFColBlocks][64])smem_f;   // [k quarter][column block][lane]
   const int qblocks = (P.n_q + kFRows - 1) / kFRows;
   const int xcd = blockIdx.x & 7;
   const int kq = blockIdx.x >> 3;
@@ -247,13 +254,16 @@ merge_out_proj_kernel(FusedParams P) {
   // wave's two quarters q
   const int cbk = wave & 3;
   const int q0 = wave >> 2;
-  bf16x8 wb[2][kFSteps];
+  // W^UV_i streams into LDS first: each instruction one whole 1 KiB row (wave w: rows
+  // 16w .. 16w+15), lane L filling physical chunk L with logical chunk L ^ (r & 15)
   {
-    const bf16_bits* w = P.w_uv + ((size_t)i * P.d_h + 32 * cbk + (lane & 31)) * kFDc + 8 * (lane >> 5);
+    const char* wsrc = (const char*)(P.w_uv + (size_t)i * P.d_h * kFDc);
+    const uint32_t wl = __builtin_amdgcn_readfirstlane(lds_addr(w_lds));
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int s = 0; s < kFSteps; ++s) wb[h][s] = *(const bf16x8*)(w + 16 * (kFSteps * (q0 + 2 * h) + s));
+    for (int j = 0; j < 16; ++j) {
+      const int r = 16 * wave + j;
+      global_to_lds16_sv(wsrc, (uint32_t)(r * kFWRowBytes + ((lane ^ (r & 15)) * 16)), wl + r * kFWRowBytes);
+    }
   }
 
   // ---- merge rows wave and wave + 8 of the block into LDS as bf16
@@ -292,22 +302,30 @@ merge_out_proj_kernel(FusedParams P) {
       if (P.lse && lane == 0) P.lse[qh[j]] = M[j] == -INFINITY ? -INFINITY : M[j] + logf(z[j]);
     }
   }
-  __syncthreads();
+  wait_vmcnt<0>();                                // this wave's W^UV rows have landed
+  lds_barrier();
 
   // ---- o_c block = o_lat block (bf16) . W^UV_i^T
   {
     const char* a = o_lds + (lane & 15) * kFPitch + 16 * (lane >> 5);
+    const int wr = 32 * cbk + (lane & 31);       // W^UV row of this lane's B operands
+    const char* wrow = w_lds + wr * kFWRowBytes;
+    f32x16 accq[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int q = q0 + 2 * h;
-      f32x16 acc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      for (int r = 0; r < 16; ++r) accq[h][r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < kFSteps; ++s)
-        acc = mfma32x32x16(*(const bf16x8*)(a + 32 * (kFSteps * q + s)), wb[h][s], acc);
-      red[q][cbk][lane] = acc;
+      for (int s = 0; s < kFSteps; ++s) {
+        const int c = 2 * (kFSteps * q + s) + (lane >> 5);
+        const bf16x8 wb = *(const bf16x8*)(wrow + ((c ^ (wr & 15)) * 16));
+        accq[h] = mfma32x32x16(*(const bf16x8*)(a + 32 * (kFSteps * q + s)), wb, accq[h]);
+      }
     }
+    __syncthreads();                               // every wave has read W^UV: red reuses it
+#pragma unroll
+    for (int h = 0; h < 2; ++h) red[q0 + 2 * h][cbk][lane] = accq[h];
   }
   __syncthreads();
   // wave w finishes column block (w & 3), registers 8 (w >> 2) .. +7: rows 16 (w >> 2)
@@ -334,10 +352,17 @@ hipError_t launch_merge_out_proj_bf16(const void* o_part, bool f16_partials, con
                                       int n_q, int n_h, int d_h, int num_splits, hipStream_t stream) {
   FusedParams P{o_part, lse_part, w_uv, o_c, lse, o_lat, n_q, n_h, d_h, num_splits};
   const int grid = 8 * ((n_h + 7) / 8) * ((n_q + kFRows - 1) / kFRows);
+  const size_t smem = (size_t)32 * kFColBlocks * kFWRowBytes + (size_t)kFRows * kFPitch;
+  static const hipError_t a16 = hipFuncSetAttribute((const void*)merge_out_proj_kernel<_Float16>,
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  static const hipError_t a32 = hipFuncSetAttribute((const void*)merge_out_proj_kernel<float>,
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (a16 != hipSuccess) return a16;
+  if (a32 != hipSuccess) return a32;
   if (f16_partials)
-    hipLaunchKernelGGL(merge_out_proj_kernel<_Float16>, dim3(grid), dim3(kFThreads), 0, stream, P);
+    hipLaunchKernelGGL(merge_out_proj_kernel<_Float16>, dim3(grid), dim3(kFThreads), smem, stream, P);
   else
-    hipLaunchKernelGGL(merge_out_proj_kernel<float>, dim3(grid), dim3(kFThreads), 0, stream, P);
+    hipLaunchKernelGGL(merge_out_proj_kernel<float>, dim3(grid), dim3(kFThreads), smem, stream, P);
   return hipGetLastError();
 }
 
