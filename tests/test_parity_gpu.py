@@ -165,6 +165,40 @@ def test_merge_all_empty_and_odd_width(torch):
     assert_close("lse", got_l[keep][None], rl, w32, lse=True)
 
 
+@pytest.mark.parametrize("n_q", [300, 700])
+def test_absorb_and_out_proj_many_rows(torch, n_q):
+    """Many query rows (a prefill's worth): each workgroup sweeps 10 or 22 blocks of 32 rows,
+    the last one ragged; every row against the oracle, with and without RoPE positions."""
+    n_h, d_h, d_c, d_r = 128, 128, 512, 64
+    rng = np.random.default_rng(n_q)
+    bf = lambda a: W.round_to_storage(a, W.BF16)
+    q_c, q_r = bf(rng.standard_normal((n_q, n_h, d_h))), bf(rng.standard_normal((n_q, n_h, d_r)))
+    w_uk = bf(rng.standard_normal((n_h, d_h, d_c)) / np.sqrt(d_c))
+    w_uv = bf(rng.standard_normal((n_h, d_h, d_c)) / np.sqrt(d_c))
+    o_lat = rng.standard_normal((n_q, n_h, d_c)).astype(np.float32)
+    pos = rng.integers(0, 163840, size=n_q).astype(np.int64)
+    d = B.dims(n_h, d_h, d_c, d_r, B.MLA_BF16)
+    dev = lambda a: D._tensor(a, W.BF16, "cuda")
+    say(f"[many rows] n_q={n_q}: absorb_q, absorb_q_rope, out_proj")
+    qa = B.absorb_q(d, dev(q_c), dev(q_r), dev(w_uk))
+    qa_r = B.absorb_q_rope(d, dev(q_c), dev(q_r), dev(w_uk), torch.from_numpy(pos).cuda())
+    oc = B.out_proj(d, torch.from_numpy(o_lat).cuda(), dev(w_uv))
+    torch.cuda.synchronize()
+    f = lambda a: W.to_f64(a, W.BF16)
+    for what, got, ref in [("q_abs", qa, O.absorb_q(f(q_c), f(q_r), f(w_uk))),
+                           ("q_abs with positions", qa_r, O.absorb_q_rope(f(q_c), f(q_r), f(w_uk), pos))]:
+        got = D.to_numpy_f64(got)
+        lim = 2.0 ** -8 * np.abs(ref) + 1e-4 * np.std(ref)     # one rounding of an fp32 sum
+        say(f"    {what}: worst |d|/limit {float(np.max(np.abs(got - ref) / lim)):.3f}")
+        assert np.all(np.abs(got - ref) <= lim), what
+    assert np.array_equal(D.to_numpy_f64(qa)[..., d_c:], f(q_r))
+    ref = O.out_proj(W.to_f64(bf(o_lat), W.BF16), f(w_uv))   # the kernel's operand rounding
+    got = D.to_numpy_f64(oc)
+    lim = 2.0 ** -8 * np.abs(ref) + 1e-4 * np.std(ref)
+    say(f"    o_c: worst |d|/limit {float(np.max(np.abs(got - ref) / lim)):.3f}")
+    assert np.all(np.abs(got - ref) <= lim)
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_out_proj(torch, name):
     w = workload(name)
