@@ -378,6 +378,42 @@ def main():
         torch.cuda.synchronize()
         per[name] = e0.elapsed_time(e1) / (reps * n)
 
+    # Spread of the step time: a separate pass of replays of the all-layers graph, one event
+    # between replays (the headline above is timed without them).
+    spread = None
+    if not args.no_graph:
+        n_rep = max(5, min(50, K // copies))
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
+        evs[0].record()
+        for r in range(n_rep):
+            g_all.replay()
+            evs[r + 1].record()
+        torch.cuda.synchronize()
+        st = sorted(evs[r].elapsed_time(evs[r + 1]) * 1e3 / copies for r in range(n_rep))
+        pick = lambda q: round(st[min(n_rep - 1, int(round(q * (n_rep - 1))))], 2)
+        spread = {"replays": n_rep, "steps_per_replay": copies, "p10_us": pick(0.1), "median_us": pick(0.5),
+                  "p90_us": pick(0.9)}
+
+    # The decode with its cache resident in the Infinity Cache: every launch reads the first
+    # copy (reported beside the cold figure, never as it).
+    warm_ms = None
+    if not args.no_graph and w.rows * ROW_BYTES <= MALL_BYTES * 3 // 4:
+        _, fn = calls["decode"]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(copies):
+                fn(0)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, K // copies)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        warm_ms = e0.elapsed_time(e1) / (reps * copies)
+
     dec_ms = per["decode"]
     dec_bytes = cached * ROW_BYTES + (w.rows - cached) * ROW_BYTES
     flops = float(FLOP_PER_ROW_HEAD) * w.n_h * sum(
@@ -424,6 +460,8 @@ def main():
                        else "absorb_q, decode, merge_out_proj" if fused else "absorb_q, decode, merge_splits, out_proj"),
         "mfma_frac_decode": round(flops / (dec_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
+        "step_spread": spread,
+        "decode_warm_ms": round(warm_ms, 5) if warm_ms is not None else None,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
