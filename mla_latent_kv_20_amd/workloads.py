@@ -301,7 +301,7 @@ CONFIGS: Dict[str, tuple] = {
     "dsv2_ragged_b128": (
         "DeepSeek-V2 dims, B=128, T~U{512..16384}, queries x3 (logit std ~3), bf16",
         dict(**DSV2, dtype=BF16, ragged_range=(512, 16384), ragged_batch=128, q_mult=3.0,
-             num_splits=16, split_rows=1024)),
+             num_splits=10, split_rows=1792)),
     "dsv2_mtp4_b64_t8192": (
         "DeepSeek-V2 dims, B=64, T=8192 cached + 4 new rows, 4 queries/seq, causal among new, bf16",
         dict(**DSV2, dtype=BF16, lengths=[8192] * 64, q_per_seq=4, appended_rows=True,
