@@ -271,6 +271,93 @@ out_proj_bf16_kernel(OutProjParams P) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// out_proj for many query rows (d_h = 128, d_c = 512): workgroup = (head i, run of query
+// rows), 4 waves, wave w computes output columns 32w .. 32w+31 over the whole reduction.
+// The wave's B operands (its 32 rows of W^UV_i, 128 VGPRs) are loaded once and reused by
+// every 32-row block of the run.  Each block of o_lat rows (fp32, 2 KiB per row of head i)
+// is loaded with whole contiguous rows, rounded to bf16 and staged in LDS, where all four
+// waves read their A operands.  The reduction runs as the four quarters of 8 MFMA steps of
+// out_proj_bf16_kernel, summed in the same order, so the two kernels agree bit for bit.
+// ---------------------------------------------------------------------------
+constexpr int kRowsDh = 128;
+constexpr int kRowsDc = 512;
+constexpr int kRowsPitch = kRowsDc * 2 + 16;    // bf16 o_lat row in LDS, padded against conflicts
+constexpr int kRowsBlock = 32;
+
+struct OutProjRowsParams {
+  const float* o_lat;     // [n_q, n_h, 512]
+  const bf16_bits* w_uv;  // [n_h, 128, 512]
+  bf16_bits* o_c;         // [n_q, n_h, 128]
+  int n_q, n_h, chunks, chunk_rows;
+};
+
+__global__ void __launch_bounds__(kThreads)
+out_proj_rows_kernel(OutProjRowsParams P) {
+  __shared__ __attribute__((aligned(16))) char a_lds[kRowsBlock * kRowsPitch];
+  // Workgroup L runs on XCD L % 8; all row runs of head i go to XCD i % 8, so W^UV_i is
+  // fetched into one L2.
+  const int xcd = blockIdx.x & 7;
+  const int kc = blockIdx.x >> 3;
+  const int i = (kc / P.chunks) * 8 + xcd;
+  const int r0 = (kc % P.chunks) * P.chunk_rows;
+  const int r1 = P.n_q < r0 + P.chunk_rows ? P.n_q : r0 + P.chunk_rows;
+  if (i >= P.n_h || r0 >= r1) return;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+
+  // B operands: lane l holds W^UV_i[32w + l%32][16s + 8(l/32) .. +7] for the 32 k-steps s
+  bf16x8 wb[kRowsDc / 16];
+  {
+    const bf16_bits* w = P.w_uv + ((size_t)i * kRowsDh + 32 * wave + (lane & 31)) * kRowsDc + 8 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < kRowsDc / 16; ++s) wb[s] = *(const bf16x8*)(w + 16 * s);
+  }
+
+  for (int mb = r0; mb < r1; mb += kRowsBlock) {
+    // o_lat rows mb .. mb+31 of head i -> bf16 in LDS: thread t takes 16-byte pieces
+    // t + 256u (row = piece / 128, 4 floats each); rows past r1 repeat row r1 - 1
+    if (mb > r0) __syncthreads();                 // every wave has read the previous block
+    {
+      f32x4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int c = tid + kThreads * u;
+        const int row = c >> 7;
+        const int m = mb + row < r1 ? mb + row : r1 - 1;
+        v[u] = *(const f32x4*)(P.o_lat + ((size_t)m * P.n_h + i) * kRowsDc + 4 * (c & 127));
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int c = tid + kThreads * u;
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *(u32x2*)(a_lds + (c >> 7) * kRowsPitch + 8 * (c & 127)) =
+            u32x2{pack_bf16x2(v[u][0], v[u][1]), pack_bf16x2(v[u][2], v[u][3])};
+      }
+    }
+    __syncthreads();
+    // A operands: lane l reads row l%32, k = 16s + 8(l/32) .. +7
+    const char* arow = a_lds + (lane & 31) * kRowsPitch + 16 * (lane >> 5);
+    f32x16 accq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) accq[q][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        accq[q] = mfma32x32x16(*(const bf16x8*)(arow + 32 * (8 * q + s)), wb[8 * q + s], accq[q]);
+    }
+    // D[m][n]: lane l, reg r -> row mb + 8(r/4) + 4(l/32) + r%4, column 32w + l%32
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = accq[0][r] + accq[1][r] + accq[2][r] + accq[3][r];
+      const int mm = mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (mm < r1) P.o_c[((size_t)mm * P.n_h + i) * kRowsDh + 32 * wave + (lane & 31)] = f32_to_bf16(v);
+    }
+  }
+}
+
 }  // namespace
 
 bool absorb_bf16_supported(int d_h, int d_c) {
@@ -292,6 +379,18 @@ hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, cons
 
 hipError_t launch_out_proj_bf16(const float* o_lat, const bf16_bits* w_uv, bf16_bits* o_c, int n_q,
                                 int n_h, int d_h, int d_c, hipStream_t stream) {
+  if (n_q >= 128 && d_h == kRowsDh && d_c == kRowsDc) {
+    // many rows: runs of 128 rows (whole 32-row blocks), at most 64 per head
+    OutProjRowsParams R{o_lat, w_uv, o_c, n_q, n_h, 0, 0};
+    R.chunks = (n_q + 127) / 128;
+    if (R.chunks > 64) R.chunks = 64;
+    R.chunk_rows = ((n_q + R.chunks - 1) / R.chunks + kRowsBlock - 1) / kRowsBlock * kRowsBlock;
+    R.chunks = (n_q + R.chunk_rows - 1) / R.chunk_rows;
+    const long long grid = 8LL * ((n_h + 7) / 8) * R.chunks;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(out_proj_rows_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, R);
+    return hipGetLastError();
+  }
   OutProjParams P{o_lat, w_uv, o_c, n_q, n_h, d_h, d_c};
   const int grid = 8 * ((n_h + 7) / 8) * (d_h / 32);
   hipLaunchKernelGGL(out_proj_bf16_kernel, dim3(grid), dim3(kThreads), 0, stream, P);
