@@ -80,7 +80,7 @@ typedef enum mla_status {
   MLA_ERR_SHAPE = 2,        /* a size, count or stride is out of range */
   MLA_ERR_ALIGN = 3,        /* a pointer or stride breaks the alignment rule */
   MLA_ERR_DTYPE = 4,        /* dims->dtype is not an mla_dtype_t value */
-  MLA_ERR_UNSUPPORTED = 5,  /* valid arguments this build has no kernel for */
+  MLA_ERR_UNSUPPORTED = 5,  /* valid arguments the library has no kernel for */
   MLA_ERR_LAUNCH = 6        /* a HIP launch failed (see hipGetLastError) */
 } mla_status_t;
 

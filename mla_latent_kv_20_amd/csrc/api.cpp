@@ -139,7 +139,7 @@ const char* mla_status_string(mla_status_t s) {
     case MLA_ERR_SHAPE: return "a size, count or stride is out of range";
     case MLA_ERR_ALIGN: return "a pointer or stride is not aligned as required";
     case MLA_ERR_DTYPE: return "unknown dtype";
-    case MLA_ERR_UNSUPPORTED: return "no kernel in this build for these arguments";
+    case MLA_ERR_UNSUPPORTED: return "the library has no kernel for these arguments";
     case MLA_ERR_LAUNCH: return "HIP kernel launch failed";
   }
   return "unknown status";
