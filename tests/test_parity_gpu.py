@@ -303,6 +303,31 @@ def test_single_row_gives_the_row_exactly(torch):
         assert np.array_equal(got["o_lat"][b], np.broadcast_to(c[b], (w.n_h, w.d_c)))
 
 
+def test_decode_rows_inside_wider_rows(torch):
+    """Cache rows inside 640-element rows (row stride 1280 bytes): every tile takes the
+    general-stride loads, lengths straddle tile edges and splits; against the oracle, and
+    equal bit for bit to the same call on the packed cache."""
+    w = W.make_workload("wide", **W.DSV2, dtype=W.BF16, lengths=[1, 33, 64, 95, 130], seed=21)
+    d = dims_of(w)
+    qa = W.draw_q_abs(w, seed=22)
+    t = D.to_device(w)
+    say("[edge] row stride 640 elements, splits=3 split_rows=64")
+    wide = torch.zeros((w.rows, 640), dtype=torch.bfloat16, device="cuda")
+    wide[:, :w.d_c + w.d_r] = t["cache"]
+    qa_t = D._tensor(qa, w.dtype, "cuda")
+    op, lp = B.decode(d, qa_t, wide[:, :w.d_c], wide[:, w.d_c:w.d_c + w.d_r], t["offsets"], w.batch, 1, 3, 64)
+    op2, lp2 = B.decode(d, qa_t, t["c_kv"], t["k_r"], t["offsets"], w.batch, 1, 3, 64)
+    torch.cuda.synchronize()
+    ro, rl = O.split_partials(W.to_f64(qa, w.dtype), w.f64("c_kv"), w.f64("k_r"), w.offsets, 1, 3, 64,
+                              O.default_scale(w.d_h, w.d_r))
+    live = ~np.isneginf(rl)
+    assert not live.all()
+    assert_close("o_part", D.to_numpy_f64(op)[live], ro[live], w)
+    assert_close("lse_part", D.to_numpy_f64(lp), rl, w, lse=True)
+    assert torch.equal(lp, lp2)
+    assert torch.equal(op[torch.from_numpy(live).cuda()], op2[torch.from_numpy(live).cuda()])
+
+
 def test_empty_splits_and_ragged_tails(torch):
     # lengths straddle tile edges; 6 splits of 40 rows leave trailing splits empty
     w = W.make_workload("tails", **W.DSV2, dtype=W.BF16, lengths=[1, 31, 32, 33, 95, 200], seed=6)
