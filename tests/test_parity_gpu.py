@@ -199,6 +199,31 @@ def test_absorb_and_out_proj_many_rows(torch, n_q):
     assert np.all(np.abs(got - ref) <= lim)
 
 
+@pytest.mark.parametrize("n_q", [129, 257])
+def test_out_proj_many_rows_off_the_head_group(torch, n_q):
+    """160 heads (the last XCD group half empty) and row runs of 96 rows with a ragged last
+    block: mla_out_proj against the oracle, and the fused call bitwise against the two calls."""
+    n_h, d_h, d_c = 160, 128, 512
+    rng = np.random.default_rng(40 + n_q)
+    w_uv = W.round_to_storage(rng.standard_normal((n_h, d_h, d_c)) / np.sqrt(d_c), W.BF16)
+    o, l = W.draw_partials(2, n_q, n_h, d_c, seed=41 + n_q)
+    o = o.astype(np.float16)
+    d = B.dims(n_h, d_h, d_c, 64, B.MLA_BF16)
+    say(f"[out_proj many rows] n_h=160 n_q={n_q}")
+    ot, lt, wt = torch.from_numpy(o).cuda(), torch.from_numpy(l).cuda(), D._tensor(w_uv, W.BF16, "cuda")
+    ol, _ = B.merge_splits(d, ot, lt)
+    oc = B.out_proj(d, ol, wt)
+    oc2, _, _ = B.merge_out_proj(d, ot, lt, wt)
+    torch.cuda.synchronize()
+    assert torch.equal(oc.view(torch.int16), oc2.view(torch.int16))
+    o_lat = ol.cpu().numpy().astype(np.float64)
+    ref = O.out_proj(W.to_f64(W.round_to_storage(o_lat, W.BF16), W.BF16), W.to_f64(w_uv, W.BF16))
+    got = D.to_numpy_f64(oc)
+    lim = 2.0 ** -8 * np.abs(ref) + 1e-4 * np.std(ref)
+    say(f"    o_c: worst |d|/limit {float(np.max(np.abs(got - ref) / lim)):.3f}")
+    assert np.all(np.abs(got - ref) <= lim)
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_out_proj(torch, name):
     w = workload(name)
