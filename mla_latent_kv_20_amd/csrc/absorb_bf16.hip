@@ -193,6 +193,175 @@ absorb_q_bf16_kernel(AbsorbParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// absorb_q for many query rows (d_h = 128, d_c = 512, d_r = 64): workgroup = (head i, run
+// of query rows), 4 waves, wave w computes latent columns 128w .. 128w+127.  W^UK_i is
+// staged in LDS once (as in absorb_q_bf16_kernel, one 128-column slice per wave) and read
+// with the transposing LDS read into the wave's B operands (4 column tiles x 8 k-steps,
+// 128 VGPRs), which every 32-row block of the run reuses.  Per block, the q_c rows come in
+// whole (256 bytes each) through LDS, the next block's rows are in flight during the
+// MFMAs, and the whole 1152-byte q_abs rows (latent and RoPE parts) are staged in LDS and
+// stored contiguously.  Every output element is the same MFMA chain over the same k-steps
+// as in absorb_q_bf16_kernel, with the same RoPE arithmetic, so the two agree bit for bit.
+// ---------------------------------------------------------------------------
+constexpr int kArDh = 128, kArDc = 512, kArDr = 64;
+constexpr int kArSlice = kArDh * kAbsPitch;          // one wave's staged W^UK slice (36 KiB)
+constexpr int kArQPitch = kArDh * 2 + 16;            // q_c row in LDS (272 B)
+constexpr int kArOPitch = (kArDc + kArDr) * 2 + 16;  // q_abs row in LDS (1168 B)
+constexpr int kArQOff = 0;                           // block staging, after the slices are read
+constexpr int kArOOff = 32 * kArQPitch;
+
+struct AbsorbRowsParams {
+  const bf16_bits* q_c;   // [n_q, n_h, 128]
+  const bf16_bits* q_r;   // [n_q, n_h, 64]
+  const bf16_bits* w_uk;  // [n_h, 128, 512]
+  bf16_bits* q_abs;       // [n_q, n_h, 576]
+  int n_q, n_h, chunks, chunk_rows;
+  const int64_t* pos;     // [n_q] or null
+  RopeSpec rope;
+};
+
+__global__ void __launch_bounds__(kThreads)
+absorb_q_rows_kernel(AbsorbRowsParams P) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  // Workgroup L runs on XCD L % 8; all row runs of head i go to XCD i % 8.
+  const int xcd = blockIdx.x & 7;
+  const int kc = blockIdx.x >> 3;
+  const int i = (kc / P.chunks) * 8 + xcd;
+  const int r0 = (kc % P.chunks) * P.chunk_rows;
+  const int r1 = P.n_q < r0 + P.chunk_rows ? P.n_q : r0 + P.chunk_rows;
+  if (i >= P.n_h || r0 >= r1) return;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  constexpr int kQk = kArDc + kArDr;
+
+  // the q_c block of rows mb .. mb+31 (16-byte piece t + 256u: row (t + 256u) / 16)
+  bf16x8 pf[2];
+  auto load_q = [&](int mb) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + kThreads * u;
+      const int m = mb + (e >> 4);
+      pf[u] = m < r1 ? *(const bf16x8*)(P.q_c + ((size_t)m * P.n_h + i) * kArDh + 8 * (e & 15)) : bf16x8{};
+    }
+  };
+  load_q(r0);
+
+  // W^UK_i: slice w (columns 128w .. 128w+127) at w * kArSlice, rows at kAbsPitch
+  {
+    const bf16_bits* w = P.w_uk + (size_t)i * kArDh * kArDc;
+    for (int e0 = 0; e0 < 4 * kArDh * 16; e0 += 8 * kThreads) {
+      bf16x8 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kThreads + tid;
+        const int sl = e >> 11, row = (e >> 4) & 127, c = e & 15;
+        v[u] = *(const bf16x8*)(w + (size_t)row * kArDc + 128 * sl + 8 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kThreads + tid;
+        const int sl = e >> 11, row = (e >> 4) & 127, c = e & 15;
+        *(bf16x8*)(smem + sl * kArSlice + row * kAbsPitch + c * 16) = v[u];
+      }
+    }
+  }
+  __syncthreads();
+  // B operands: column tile t of the wave's slice, k-step s: lane l gets
+  // W[16s + 8(l/32) + j][128w + 32t + l%32]
+  bf16x8 wb[4][8];
+  {
+    const int g = lane >> 4;
+    const int row = 8 * (g >> 1) + ((lane & 15) >> 2);
+    const char* slice = smem + wave * kArSlice;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const char* p = slice + (16 * s + row) * kAbsPitch + (32 * t + 16 * (g & 1) + 4 * (lane & 3)) * 2;
+        const i16x4 lo4 = lds_read_tr16(p);
+        const i16x4 hi4 = lds_read_tr16(p + 4 * kAbsPitch);
+        const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        wb[t][s] = __builtin_bit_cast(bf16x8, v8);
+      }
+  }
+  // RoPE pair indices of this thread: row t / 8 of a block, pairs k = 4 (t % 8) + j
+  const int rrow = tid >> 3;
+  double inv[4];
+  if (P.pos) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) inv[j] = rope_inv_freq(4 * (tid & 7) + j, kArDr, P.rope);
+  }
+  char* qst = smem + kArQOff;
+  char* ost = smem + kArOOff;
+  __syncthreads();                                 // every wave has read its slice: LDS is free
+
+  for (int mb = r0; mb < r1; mb += 32) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + kThreads * u;
+      *(bf16x8*)(qst + (e >> 4) * kArQPitch + 16 * (e & 15)) = pf[u];
+    }
+    __syncthreads();
+    bf16x8 qa[8];
+    {
+      const char* qr = qst + (lane & 31) * kArQPitch + 16 * (lane >> 5);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qa[s] = *(const bf16x8*)(qr + 32 * s);
+    }
+    if (mb + 32 < r1) load_q(mb + 32);
+    // RoPE part of the block's rows: thread t, row t / 8, pairs (k, k + 32), k = 4 (t % 8) + j
+    {
+      const int m = mb + rrow;
+      if (m < r1) {
+        const bf16_bits* src = P.q_r + ((size_t)m * P.n_h + i) * kArDr;
+        bf16_bits* dst = (bf16_bits*)(ost + rrow * kArOPitch) + kArDc;
+        if (P.pos == nullptr) {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          *(u32x2*)(dst + 8 * (tid & 7)) = *(const u32x2*)(src + 8 * (tid & 7));
+          *(u32x2*)(dst + 8 * (tid & 7) + 4) = *(const u32x2*)(src + 8 * (tid & 7) + 4);
+        } else {
+          const int64_t ps = P.pos[m];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int k = 4 * (tid & 7) + j;
+            double x = bf16_to_f32(src[k]);
+            double y = bf16_to_f32(src[k + kArDr / 2]);
+            rope_rotate(x, y, ps, inv[j]);
+            dst[k] = f32_to_bf16((float)x);
+            dst[k + kArDr / 2] = f32_to_bf16((float)y);
+          }
+        }
+      }
+    }
+    // the latent part: four 32 x 32 column tiles
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) acc = mfma32x32x16(qa[s], wb[t][s], acc);
+      const int col = 128 * wave + 32 * t + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        *(bf16_bits*)(ost + row * kArOPitch + col * 2) = f32_to_bf16(acc[r]);
+      }
+    }
+    __syncthreads();
+    // whole q_abs rows: 72 pieces of 16 bytes per row
+    for (int e = tid; e < 32 * 72; e += kThreads) {
+      const int row = e / 72, c = e - row * 72;
+      if (mb + row < r1)
+        *(bf16x8*)(P.q_abs + ((size_t)(mb + row) * P.n_h + i) * kQk + 8 * c) =
+            *(const bf16x8*)(ost + row * kArOPitch + 16 * c);
+    }
+    __syncthreads();                               // qst and ost are free for the next block
+  }
+}
+
+// ---------------------------------------------------------------------------
 // out_proj: workgroup = (head i, block of 32 output columns of d_h); wave w runs a quarter
 // of the d_c reduction and the four partial 32 x 32 products are summed through LDS.
 // W^UV_i rows are [d_h][d_c] with d_c (the reduction index) contiguous, so B operands load
@@ -370,6 +539,22 @@ bool out_proj_bf16_supported(int d_h, int d_c) {
 hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, const bf16_bits* w_uk,
                                 bf16_bits* q_abs, int n_q, int n_h, int d_h, int d_c, int d_r,
                                 const int64_t* positions, const RopeSpec& rope, hipStream_t stream) {
+  if (n_q >= 128 && d_h == kArDh && d_c == kArDc && d_r == kArDr) {
+    // many rows: runs of up to 512 rows (whole 32-row blocks), at least 2 per head
+    AbsorbRowsParams R{q_c, q_r, w_uk, q_abs, n_q, n_h, 0, 0, positions, rope};
+    R.chunks = (n_q + 511) / 512;
+    if (R.chunks < 2) R.chunks = 2;
+    R.chunk_rows = ((n_q + R.chunks - 1) / R.chunks + 31) / 32 * 32;
+    R.chunks = (n_q + R.chunk_rows - 1) / R.chunk_rows;
+    const size_t smem_rows = (size_t)4 * kArSlice;
+    static const hipError_t attr = hipFuncSetAttribute((const void*)absorb_q_rows_kernel,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_rows);
+    if (attr != hipSuccess) return attr;
+    const long long grid = 8LL * ((n_h + 7) / 8) * R.chunks;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(absorb_q_rows_kernel, dim3((unsigned)grid), dim3(kThreads), smem_rows, stream, R);
+    return hipGetLastError();
+  }
   AbsorbParams P{q_c, q_r, w_uk, q_abs, n_q, n_h, d_h, d_c, d_r, positions, rope};
   const size_t smem = (size_t)d_h * kAbsPitch + 32 * kAbsOutPitch;
   const int grid = 8 * ((n_h + 7) / 8) * (d_c / kAbsCols);

@@ -167,8 +167,9 @@ def test_merge_all_empty_and_odd_width(torch):
 
 @pytest.mark.parametrize("n_q", [300, 700])
 def test_absorb_and_out_proj_many_rows(torch, n_q):
-    """Many query rows (a prefill's worth): each workgroup sweeps 10 or 22 blocks of 32 rows,
-    the last one ragged; every row against the oracle, with and without RoPE positions."""
+    """Many query rows (a prefill's worth, the many-row kernels): runs of whole 32-row blocks,
+    the last one ragged; every row against the oracle, with and without RoPE positions, and
+    absorb_q bitwise against the decode-size kernel called on 60 rows at a time."""
     n_h, d_h, d_c, d_r = 128, 128, 512, 64
     rng = np.random.default_rng(n_q)
     bf = lambda a: W.round_to_storage(a, W.BF16)
@@ -183,7 +184,13 @@ def test_absorb_and_out_proj_many_rows(torch, n_q):
     qa = B.absorb_q(d, dev(q_c), dev(q_r), dev(w_uk))
     qa_r = B.absorb_q_rope(d, dev(q_c), dev(q_r), dev(w_uk), torch.from_numpy(pos).cuda())
     oc = B.out_proj(d, torch.from_numpy(o_lat).cuda(), dev(w_uv))
+    # the same rows in calls of 60 (the decode-size kernels): bitwise equal
+    qc_t, qr_t, wk_t, pos_t = dev(q_c), dev(q_r), dev(w_uk), torch.from_numpy(pos).cuda()
+    parts = [(B.absorb_q(d, qc_t[a:a + 60], qr_t[a:a + 60], wk_t),
+              B.absorb_q_rope(d, qc_t[a:a + 60], qr_t[a:a + 60], wk_t, pos_t[a:a + 60])) for a in range(0, n_q, 60)]
     torch.cuda.synchronize()
+    assert torch.equal(qa.view(torch.int16), torch.cat([p[0] for p in parts]).view(torch.int16))
+    assert torch.equal(qa_r.view(torch.int16), torch.cat([p[1] for p in parts]).view(torch.int16))
     f = lambda a: W.to_f64(a, W.BF16)
     for what, got, ref in [("q_abs", qa, O.absorb_q(f(q_c), f(q_r), f(w_uk))),
                            ("q_abs with positions", qa_r, O.absorb_q_rope(f(q_c), f(q_r), f(w_uk), pos))]:
