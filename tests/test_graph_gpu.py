@@ -144,3 +144,43 @@ def test_prologue_and_projections_graph_replays_equal_eager(torch):
             step()
         torch.cuda.synchronize()
         assert torch.equal(u.view(torch.int16), ref[3].view(torch.int16)), rep
+
+
+def test_many_row_kernels_graph_replays_equal_eager(torch):
+    """The many-row forms of mla_absorb_q, mla_absorb_q_rope and mla_out_proj (300 query
+    rows) captured once: every replay equals the eager run bit for bit."""
+    n_h, d_h, d_c, d_r, n = 128, 128, 512, 64, 300
+    d = B.dims(n_h, d_h, d_c, d_r, B.MLA_BF16)
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    rnd = lambda *shape, scale=1.0: (torch.randn(shape, generator=gen, device="cuda") * scale).to(torch.bfloat16)
+    q_c, q_r = rnd(n, n_h, d_h), rnd(n, n_h, d_r)
+    w_uk, w_uv = rnd(n_h, d_h, d_c, scale=d_c ** -0.5), rnd(n_h, d_h, d_c, scale=d_c ** -0.5)
+    o_lat = torch.randn((n, n_h, d_c), generator=gen, device="cuda")
+    pos = torch.randint(0, 163840, (n,), generator=gen, device="cuda", dtype=torch.int64)
+    qa = torch.empty((n, n_h, d_c + d_r), dtype=torch.bfloat16, device="cuda")
+    qa_r, oc = torch.empty_like(qa), torch.empty((n, n_h, d_h), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def step():
+        B.absorb_q(d, q_c, q_r, w_uk, qa)
+        B.absorb_q_rope(d, q_c, q_r, w_uk, pos, qa_r, rope=B.rope(yarn_factor=40.0))
+        B.out_proj(d, o_lat, w_uv, oc)
+
+    say(f"[graph] many-row kernels n_q={n}: eager")
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (qa, qa_r, oc)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in (qa, qa_r, oc):
+            x.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say(f"[graph] many-row kernels replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for x, r in zip((qa, qa_r, oc), ref):
+            assert torch.equal(x.view(torch.int16), r.view(torch.int16)), rep
