@@ -243,7 +243,8 @@ def test_out_proj(torch, name):
 
 
 @pytest.mark.parametrize("S,f16,n_q", [(1, True, 1), (3, True, 33), (8, True, 32), (8, False, 64),
-                                        (13, False, 40), (64, True, 7), (70, True, 3), (3, True, 160),
+                                        (13, False, 40), (12, True, 48), (16, True, 17), (17, True, 9),
+                                        (64, True, 7), (70, True, 3), (3, True, 160),
                                         (1, False, 300)])
 def test_merge_out_proj_equals_the_two_calls(torch, S, f16, n_q):
     """The fused call writes exactly what mla_merge_splits + mla_out_proj write."""
