@@ -267,7 +267,6 @@ mla_decode_bf16_kernel(DecodeParams P) {
   // Waves past the last head (n_h not a multiple of 128) still load tiles and meet the
   // barriers; they read the last head's query and store nothing.
   const bool active = hg * kHeadsPerWg + wave * 32 < P.n_h;   // wave-uniform
-  const int head_ld = active ? head : P.n_h - 1;
 
   const int64_t row0 = P.offsets[b];
   const int64_t len = P.offsets[b + 1] - row0;
