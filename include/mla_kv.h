@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 7
+#define MLA_ABI_VERSION 8
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -140,6 +140,9 @@ const char* mla_status_string(mla_status_t status);
  *   q_r   [n_q, n_h, d_r]        dtype      per-head RoPE query, already rotated
  *   w_uk  [n_h, d_h, d_c]        dtype      W^UK_i as [d_h, d_c] per head
  *   q_abs [n_q, n_h, d_c + d_r]  dtype      out; bf16 is rounded once from fp32
+ *
+ * bf16 needs 16-byte aligned q_c, q_r, w_uk and q_abs (MLA_ERR_ALIGN otherwise): the
+ * kernels move every operand in 16-byte pieces.
  */
 mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t n_q,
                           const void* q_c, const void* q_r, const void* w_uk,
@@ -295,6 +298,13 @@ mla_status_t mla_out_folded(const mla_dims_t* dims, int32_t n_q, int32_t d_model
  * num_splits * n_q * n_h floats.  Returns 0 on bad arguments. */
 size_t mla_partial_bytes(const mla_dims_t* dims, int32_t n_q, int32_t num_splits,
                          int32_t partial_dtype);
+
+/* Bytes of the split buffers of a decode plan with fp32 split results, the larger form:
+ * mla_partial_bytes(dims, n_q, num_splits, MLA_F32) for o_part plus
+ * num_splits * n_q * n_h * 4 for lse_part.  The caller owns both buffers (the library
+ * allocates nothing); fp16 split results need mla_partial_bytes(..., MLA_F16) for o_part.
+ * Returns 0 on bad arguments. */
+size_t mla_decode_workspace_bytes(const mla_dims_t* dims, int32_t n_q, int32_t num_splits);
 
 /*
  * mla_decode - attention of every query head over the latent rows, one result

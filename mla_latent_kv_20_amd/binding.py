@@ -9,7 +9,6 @@ Nothing here computes a result: a missing library raises instead of falling back
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional
 
@@ -53,6 +52,7 @@ SIGNATURES = {
     "mla_abi_version": (_I32, []),
     "mla_status_string": (ctypes.c_char_p, [_I32]),
     "mla_partial_bytes": (_SZ, [_DIMS_P, _I32, _I32, _I32]),
+    "mla_decode_workspace_bytes": (_SZ, [_DIMS_P, _I32, _I32]),
     "mla_check_offsets": (_I32, [_P, _I32, _I32, _I64]),
     "mla_absorb_q": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P, _P]),
     "mla_decode": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _I64, _P, _I64, _P, _I32, _I32, _I32, _P, _P, _P]),
@@ -72,6 +72,12 @@ SIGNATURES = {
     "mla_kv_append_workspace_bytes": (_SZ, [_DIMS_P, _I32]),
     "mla_quantize_rows_fp8": (_I32, [_DIMS_P, _I64, _P, _I64, _P, _P, _I64, _P, _P]),
     "mla_decode_fp8": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _P, _P, _P]),
+    # device calibration (include/mla_calib.h)
+    "mla_calib_mfma_grid": (_I32, []),
+    "mla_calib_mfma": (_I32, [_I32, _P, _P]),
+    "mla_calib_mfma_flop": (ctypes.c_double, [_I32]),
+    "mla_calib_read": (_I32, [_P, _I64, _I32, _P, _P]),
+    "mla_calib_read_bytes": (_I64, [_I64, _I32]),
 }
 
 _lib = None
@@ -433,5 +439,28 @@ def rope_softmax_scale(d: MlaDims, rope: Optional[MlaRope] = None) -> float:
     return float(load().mla_rope_softmax_scale(ctypes.byref(d), ctypes.byref(rope) if rope is not None else None))
 
 
-def default_scale(d_h: int, d_r: int) -> float:
-    return 1.0 / math.sqrt(d_h + d_r)
+
+# ---------------------------------------------------------------------------
+# Device calibration (include/mla_calib.h): the benchmark brackets these with events.
+# ---------------------------------------------------------------------------
+
+def calib_mfma(iters: int, out=None):
+    """Back-to-back bf16 MFMAs on every SIMD; returns (out buffer, FLOPs of the launch)."""
+    import torch
+    lib = load()
+    n = int(lib.mla_calib_mfma_grid()) * 256
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device="cuda")
+    _check("mla_calib_mfma", lib.mla_calib_mfma(int(iters), _ptr(out), _stream(None)))
+    return out, float(lib.mla_calib_mfma_flop(int(iters)))
+
+
+def calib_read(src, workgroups: int = 256, out=None):
+    """Streaming read of (most of) the device tensor src; returns (out buffer, bytes read)."""
+    import torch
+    lib = load()
+    if out is None:
+        out = torch.empty(int(workgroups), dtype=torch.float32, device=src.device)
+    nbytes = src.numel() * src.element_size()
+    _check("mla_calib_read", lib.mla_calib_read(_ptr(src), int(nbytes), int(workgroups), _ptr(out), _stream(None)))
+    return out, int(lib.mla_calib_read_bytes(int(nbytes), int(workgroups)))

@@ -152,6 +152,12 @@ size_t mla_partial_bytes(const mla_dims_t* dims, int32_t n_q, int32_t num_splits
          (partial_dtype == MLA_F16 ? 2 : 4);
 }
 
+size_t mla_decode_workspace_bytes(const mla_dims_t* dims, int32_t n_q, int32_t num_splits) {
+  const size_t o = mla_partial_bytes(dims, n_q, num_splits, MLA_F32);
+  if (o == 0 && !(n_q == 0 && check_dims(dims) == MLA_OK && num_splits >= 1)) return 0;
+  return o + (size_t)num_splits * (size_t)n_q * (size_t)dims->n_h * sizeof(float);
+}
+
 mla_status_t mla_check_offsets(const int64_t* host_offsets, int32_t batch, int32_t q_per_seq,
                                int64_t total_rows) {
   if (batch < 0 || q_per_seq < 1 || total_rows < 0) return MLA_ERR_SHAPE;
@@ -190,7 +196,7 @@ mla_status_t absorb_common(const mla_dims_t* dims, int32_t n_q, const void* q_c,
                                              dims->d_r, positions, spec, stream));
   if (!mla::absorb_bf16_supported(dims->d_h, dims->d_c) || dims->d_r % 8) return MLA_ERR_UNSUPPORTED;
   if (positions && dims->d_r > 512) return MLA_ERR_UNSUPPORTED;  // a pair index per thread of 256
-  if (!aligned(q_c, 16) || !aligned(w_uk, 16)) return MLA_ERR_ALIGN;
+  if (!aligned(q_c, 16) || !aligned(q_r, 16) || !aligned(w_uk, 16) || !aligned(q_abs, 16)) return MLA_ERR_ALIGN;
   return launched(mla::launch_absorb_q_bf16((const uint16_t*)q_c, (const uint16_t*)q_r,
                                             (const uint16_t*)w_uk, (uint16_t*)q_abs, n_q, dims->n_h,
                                             dims->d_h, dims->d_c, dims->d_r, positions, spec, stream));

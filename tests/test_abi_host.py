@@ -14,7 +14,7 @@ import pytest
 from mla_latent_kv_20_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mla_kv.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("mla_kv.h", "mla_calib.h")]
 
 FAKE = 0x100000          # 1 MiB-aligned fake device address: never dereferenced in these tests
 
@@ -28,7 +28,7 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(mla_[a-z_0-9]+)\s*\(", text, re.M)))
 
 
@@ -37,7 +37,20 @@ def test_every_declared_entry_point_is_exported(lib):
     assert set(names) == set(B.SIGNATURES), names
     for n in names:
         assert hasattr(lib, n)
-    assert lib.mla_abi_version() == 7
+    assert lib.mla_abi_version() == 8
+
+
+def test_calibration_argument_checks(lib):
+    assert lib.mla_calib_mfma_grid() == 1024
+    assert lib.mla_calib_mfma(0, FAKE, None) == B.MLA_ERR_SHAPE
+    assert lib.mla_calib_mfma(10, None, None) == B.MLA_ERR_NULL
+    assert lib.mla_calib_mfma_flop(10) == 1024 * 4 * 10 * 4 * 32768.0
+    assert lib.mla_calib_mfma_flop(0) == 0.0
+    assert lib.mla_calib_read(None, 1 << 30, 256, FAKE, None) == B.MLA_ERR_NULL
+    assert lib.mla_calib_read(FAKE, 1 << 30, 0, FAKE, None) == B.MLA_ERR_SHAPE
+    assert lib.mla_calib_read(FAKE, 1000, 256, FAKE, None) == B.MLA_ERR_SHAPE      # under one tile each
+    assert lib.mla_calib_read(FAKE + 8, 1 << 30, 256, FAKE, None) == B.MLA_ERR_ALIGN
+    assert lib.mla_calib_read_bytes(1 << 30, 256) == (1 << 30) // (256 * 36864) * 256 * 36864
 
 
 def test_status_strings(lib):
@@ -96,6 +109,12 @@ def test_absorb_merge_out_proj_argument_checks(lib):
     assert lib.mla_absorb_q(byref(d), -3, FAKE, FAKE, FAKE, FAKE, None) == B.MLA_ERR_SHAPE
     assert lib.mla_absorb_q(byref(d), 4, FAKE, None, FAKE, FAKE, None) == B.MLA_ERR_NULL
     assert lib.mla_absorb_q(byref(d), 4, FAKE + 1, FAKE, FAKE, FAKE, None) == B.MLA_ERR_ALIGN
+    # bf16: every operand moves in 16-byte pieces, q_r and q_abs included
+    assert lib.mla_absorb_q(byref(d), 4, FAKE, FAKE + 8, FAKE, FAKE, None) == B.MLA_ERR_ALIGN
+    assert lib.mla_absorb_q(byref(d), 4, FAKE, FAKE, FAKE, FAKE + 8, None) == B.MLA_ERR_ALIGN
+    assert lib.mla_absorb_q_rope(byref(d), 4, FAKE, FAKE + 2, FAKE, FAKE, None, FAKE + 8, None) == B.MLA_ERR_ALIGN
+    # fp32 keeps element alignment
+    assert lib.mla_absorb_q(byref(dims(dtype=B.MLA_F32)), 4, FAKE, FAKE + 2, FAKE, FAKE, None) == B.MLA_ERR_ALIGN
     assert lib.mla_absorb_q(byref(dims(d_c=200)), 4, FAKE, FAKE, FAKE, FAKE, None) == B.MLA_ERR_UNSUPPORTED
     assert lib.mla_merge_splits(byref(d), 4, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == B.MLA_ERR_SHAPE
     assert lib.mla_merge_splits(byref(d), 4, 2, 0, FAKE, FAKE, None, FAKE, None) == B.MLA_ERR_NULL
@@ -266,6 +285,12 @@ def test_partial_bytes(lib):
     assert lib.mla_partial_bytes(ctypes.byref(d), 32, 8, B.MLA_BF16) == 0
     assert lib.mla_partial_bytes(ctypes.byref(d), 32, 0, B.MLA_F32) == 0
     assert lib.mla_partial_bytes(None, 32, 1, B.MLA_F32) == 0
+    # decode workspace: fp32 split results plus the split lse values
+    assert lib.mla_decode_workspace_bytes(ctypes.byref(d), 32, 8) == 8 * 32 * 128 * (512 * 4 + 4)
+    assert lib.mla_decode_workspace_bytes(ctypes.byref(d), 0, 8) == 0
+    assert lib.mla_decode_workspace_bytes(ctypes.byref(d), 32, 0) == 0
+    assert lib.mla_decode_workspace_bytes(ctypes.byref(d), -1, 8) == 0
+    assert lib.mla_decode_workspace_bytes(None, 32, 8) == 0
 
 
 def test_check_offsets(lib):

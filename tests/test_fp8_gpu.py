@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 
 import oracle as O
+from bounds import check_lse, lse_bound
 from mla_latent_kv_20_amd import binding as B
 from mla_latent_kv_20_amd import device as D
 from mla_latent_kv_20_amd import workloads as W
@@ -212,21 +213,38 @@ def test_fp8_step_end_to_end(torch, name):
                                 w.f64("w_uk"), w.f64("w_uv"), w.q_per_seq, num_splits=S, split_rows=R)
         check("o_c", oc, ref["o_c"])
         check("o_lat", ol, ref["o_lat"])
-        m = 1e-2 * float(np.max(np.abs(ref["lse"]))) + 1e-3
-        assert float(np.max(np.abs(lse - ref["lse"]))) <= m
+        q_abs = O.absorb_q(w.f64("q_c"), w.f64("q_r"), w.f64("w_uk"))
+        check_lse("lse", lse, ref["lse"], lse_bound(q_abs, deq[:, :512], w.offsets, w.q_per_seq,
+                                                    O.default_scale(w.d_h, w.d_r)), say)
 
 
-def test_fp8_full_size_sampled(torch):
+def test_fp8_full_size(torch):
     """The benchmark's workload (32 x 4096 rows, 8 splits of 512): every code row against the
-    oracle's quantizer, the step's output on 8 sequences against the oracle's decode."""
+    oracle's quantizer, and the step's outputs on every sequence against the oracle's decode
+    over the dequantized rows, one sequence at a time."""
     w = workload("dsv2_b32_t4096")
     say(f"[fp8 full] {w.name} rows={w.rows} splits={w.num_splits} split_rows={w.split_rows}")
     codes, scales, deq = quantize_on_gpu(torch, w, D.packed_rows(w))
     oc, lse, ol = fp8_step(torch, w, codes, scales, w.num_splits, w.split_rows)
-    seqs = [0, 5, 9, 14, 18, 23, 27, 31]
-    rows = np.concatenate([np.arange(w.offsets[b], w.offsets[b + 1]) for b in seqs])
-    offs = np.concatenate([[0], np.cumsum(w.lengths[seqs])]).astype(np.int64)
-    ref = O.absorbed_decode(deq[rows, :512], deq[rows, 512:], offs, w.f64("q_c")[seqs], w.f64("q_r")[seqs],
-                            w.f64("w_uk"), w.f64("w_uv"), 1, num_splits=w.num_splits, split_rows=w.split_rows)
-    check("o_c", oc[seqs], ref["o_c"])
-    check("o_lat", ol[seqs], ref["o_lat"])
+    q_abs = O.absorb_q(w.f64("q_c"), w.f64("q_r"), w.f64("w_uk"))
+    scale = O.default_scale(w.d_h, w.d_r)
+    worst = {"o_c": 0.0, "o_lat": 0.0}
+    peak = {"o_c": 0.0, "o_lat": 0.0}
+    lse_ratio = 0.0
+    for b in range(w.batch):
+        rows = np.arange(w.offsets[b], w.offsets[b + 1])
+        offs = np.array([0, len(rows)], np.int64)
+        ref = O.absorbed_decode(deq[rows, :512], deq[rows, 512:], offs, w.f64("q_c")[b:b + 1],
+                                w.f64("q_r")[b:b + 1], w.f64("w_uk"), w.f64("w_uv"), 1,
+                                num_splits=w.num_splits, split_rows=w.split_rows)
+        for k, g in (("o_c", oc[b:b + 1]), ("o_lat", ol[b:b + 1])):
+            worst[k] = max(worst[k], float(np.max(np.abs(g - ref[k]))))
+            peak[k] = max(peak[k], float(np.max(np.abs(ref[k]))))
+        lb = lse_bound(q_abs[b:b + 1], deq[rows, :512], offs, 1, scale)
+        lse_ratio = max(lse_ratio, float(np.max(np.abs(lse[b:b + 1] - ref["lse"]) / lb)))
+    for k in worst:
+        tol = 1e-2 * peak[k] + 1e-3
+        say(f"    {k}: max|d| = {worst[k]:.3e} over all {w.batch} sequences (bound {tol:.3e})")
+        assert worst[k] <= tol
+    say(f"    lse: max |d|/bound = {lse_ratio:.3f}")
+    assert lse_ratio <= 1.0
