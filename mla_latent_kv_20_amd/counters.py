@@ -2,6 +2,7 @@
 `rocprofv3 --pmc ... --output-format csv` writes.
 
     python -m mla_latent_kv_20_amd.counters DIR [DIR ...] [--kernels REGEX]
+    python -m mla_latent_kv_20_amd.counters --stats KERNEL_STATS_CSV [--kernels REGEX]
 
 Each DIR holds one pass (*_counter_collection.csv and *_agent_info.csv).  Counters of the same
 kernel are averaged over its dispatches (the first dispatch of each kernel is dropped as a
@@ -116,12 +117,28 @@ def markdown(rows):
     return "\n".join(out)
 
 
+def stats_table(path: str, kernels: str = ".*") -> str:
+    """The kernel-trace statistics (`rocprofv3 --kernel-trace --stats`) as a markdown table."""
+    pat = re.compile(kernels)
+    out = ["| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for row in csv.DictReader(open(path)):
+        if not pat.search(row["Name"]):
+            continue
+        out.append(f"| {short_name(row['Name'])} | {row['Calls']} | {float(row['AverageNs']) / 1e3:.2f} | "
+                   f"{float(row['MinNs']) / 1e3:.2f} | {float(row['MaxNs']) / 1e3:.2f} | {float(row['Percentage']):.1f}% |")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("dirs", nargs="+")
+    ap.add_argument("dirs", nargs="*")
+    ap.add_argument("--stats", help="a *_kernel_stats.csv of a kernel-trace run")
     ap.add_argument("--kernels", default=".*")
     ap.add_argument("--raw", action="store_true", help="also print every averaged counter")
     a = ap.parse_args()
+    if a.stats:
+        print(stats_table(a.stats, a.kernels))
+        return
     rows = summarize(a.dirs, a.kernels)
     print(markdown(rows))
     if a.raw:
