@@ -42,7 +42,8 @@
  * Conventions shared by every call
  *  - All tensor arguments are device pointers, row-major, densely packed unless
  *    a stride is given.  The caller owns every buffer; the library allocates
- *    nothing and keeps no state.  Outputs must not overlap inputs.
+ *    nothing and keeps no state (mla_kv_append_noalloc's fixed device array, one
+ *    per GPU, aside).  Outputs must not overlap inputs.
  *  - Every call only enqueues work on `stream` (0 = the null stream) and
  *    returns; it never synchronizes.  Calls on one stream run in order.
  *  - Arguments are checked on the host before anything is launched; a failed
@@ -72,7 +73,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 8
+#define MLA_ABI_VERSION 9
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -81,7 +82,9 @@ typedef enum mla_status {
   MLA_ERR_ALIGN = 3,        /* a pointer or stride breaks the alignment rule */
   MLA_ERR_DTYPE = 4,        /* dims->dtype is not an mla_dtype_t value */
   MLA_ERR_UNSUPPORTED = 5,  /* valid arguments the library has no kernel for */
-  MLA_ERR_LAUNCH = 6        /* a HIP launch failed (see hipGetLastError) */
+  MLA_ERR_LAUNCH = 6,       /* a HIP launch failed (see hipGetLastError) */
+  MLA_ERR_SCRATCH = 7,      /* more than a fixed device array holds (mla_kv_append_noalloc) */
+  MLA_ERR_DEVICE = 8        /* the stream is not on the current device (mla_kv_append_noalloc) */
 } mla_status_t;
 
 typedef enum mla_dtype {
@@ -205,6 +208,30 @@ mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t n_new, int32_t d_mode
                            const void* w_dkv, const void* w_kr, const int64_t* positions,
                            const int64_t* dst_rows, void* rows, int64_t stride, const mla_rope_t* rope,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the fixed device array behind mla_kv_append_noalloc: 8 MiB per GPU. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/*
+ * mla_kv_append_noalloc - mla_kv_append for callers that cannot allocate device memory:
+ * code under HIP graph capture, serving loops and harnesses that forbid hipMalloc.  The
+ * same arguments and the same checks as mla_kv_append without the workspace; its fp32
+ * partial sums go to a fixed array of MLA_NOALLOC_SCRATCH_BYTES inside this library, one
+ * per GPU, held from the first call on that GPU until the process ends.  The call itself
+ * allocates nothing: no hipMalloc, no hipFree, no allocating library routine.
+ *  - needs mla_kv_append_workspace_bytes(dims, n_new) <= MLA_NOALLOC_SCRATCH_BYTES
+ *    (at d_c + d_r = 576: n_new <= 455), else MLA_ERR_SCRATCH; fp32 uses no scratch;
+ *  - `stream` must belong to the current device, else MLA_ERR_DEVICE;
+ *  - the array keeps the last call's partial sums; every call writes each entry before
+ *    reading it, so nothing needs clearing;
+ *  - every call on one GPU shares that GPU's array: calls that overlap in time (two
+ *    streams, two host threads) race, and the caller must order them.
+ * Outputs equal mla_kv_append's bit for bit (the same kernels).
+ */
+mla_status_t mla_kv_append_noalloc(const mla_dims_t* dims, int32_t n_new, int32_t d_model, const void* h,
+                                   const void* w_dkv, const void* w_kr, const int64_t* positions,
+                                   const int64_t* dst_rows, void* rows, int64_t stride,
+                                   const mla_rope_t* rope, hipStream_t stream);
 
 /*
  * mla_quantize_rows_fp8 - quantize cache rows to FP8 E4M3 codes with one scale per row.

@@ -22,6 +22,9 @@ MLA_ERR_ALIGN = 3
 MLA_ERR_DTYPE = 4
 MLA_ERR_UNSUPPORTED = 5
 MLA_ERR_LAUNCH = 6
+MLA_ERR_SCRATCH = 7
+MLA_ERR_DEVICE = 8
+NOALLOC_SCRATCH_BYTES = 8 << 20
 MLA_F32 = 0
 MLA_BF16 = 1
 MLA_F16 = 2
@@ -70,6 +73,7 @@ SIGNATURES = {
     "mla_fold_o": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P]),
     "mla_out_folded": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
     "mla_kv_append_workspace_bytes": (_SZ, [_DIMS_P, _I32]),
+    "mla_kv_append_noalloc": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _I64, _ROPE_P, _P]),
     "mla_quantize_rows_fp8": (_I32, [_DIMS_P, _I64, _P, _I64, _P, _P, _I64, _P, _P]),
     "mla_decode_fp8": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _P, _P, _P]),
     # device calibration (include/mla_calib.h)
@@ -202,6 +206,18 @@ def kv_append(d: MlaDims, h, w_dkv, w_kr, positions, dst_rows, rows, rope: Optio
                                                   rows.stride(0), ctypes.byref(rope) if rope is not None else None,
                                                   _ptr(workspace) if workspace is not None else None,
                                                   ws_bytes, _stream(stream)))
+    return rows
+
+
+def kv_append_noalloc(d: MlaDims, h, w_dkv, w_kr, positions, dst_rows, rows, rope: Optional[MlaRope] = None,
+                      stream=None):
+    """kv_append with the partial sums in the library's fixed device array: no workspace,
+    nothing allocated here or in the call; returns rows."""
+    n_new, d_model = h.shape
+    _check("mla_kv_append_noalloc",
+           load().mla_kv_append_noalloc(ctypes.byref(d), n_new, d_model, _ptr(h), _ptr(w_dkv), _ptr(w_kr),
+                                        _ptr(positions), _ptr(dst_rows), _ptr(rows), rows.stride(0),
+                                        ctypes.byref(rope) if rope is not None else None, _stream(stream)))
     return rows
 
 

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_kv.so")
 SOURCES = ["api.cpp", "decode_bf16.hip", "absorb_bf16.hip", "merge_f32.hip", "fused_bf16.hip", "prologue.hip",
-           "quant_fp8.hip", "decode_fp8.hip", "fold.hip", "calib.hip"]
+           "quant_fp8.hip", "decode_fp8.hip", "fold.hip", "calib.hip", "noalloc.hip"]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 

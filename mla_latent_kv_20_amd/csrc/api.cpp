@@ -39,6 +39,8 @@ hipError_t launch_kv_append(bool bf16, const void* h, const void* w_dkv, const v
                             const int64_t* positions, const int64_t* dst_rows, void* rows, int64_t stride,
                             float* workspace, int n_new, int d_model, int d_c, int d_r, const RopeSpec& rope,
                             hipStream_t stream);
+// noalloc.hip: the fixed device array's address on the current device (checked against stream's)
+mla_status_t noalloc_scratch(hipStream_t stream, void** addr);
 // quant_fp8.hip, decode_fp8.hip
 bool quantize_rows_supported(int width);
 hipError_t launch_quantize_rows(bool bf16, const void* src, int64_t src_stride, int64_t n,
@@ -117,6 +119,31 @@ mla_status_t rope_spec(const mla_rope_t* r, mla::RopeSpec* out) {
   return MLA_OK;
 }
 
+// Every check of mla_kv_append but its workspace's; fills the RoPE spec.  n_new == 0 passes
+// after the shape checks (a no-op call).
+mla_status_t kv_append_check(const mla_dims_t* dims, int32_t n_new, int32_t d_model, const void* h,
+                             const void* w_dkv, const void* w_kr, const int64_t* positions,
+                             const int64_t* dst_rows, void* rows, int64_t stride, const mla_rope_t* rope,
+                             mla::RopeSpec* spec) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  st = rope_spec(rope, spec);
+  if (st != MLA_OK) return st;
+  if (n_new < 0 || d_model < 1) return MLA_ERR_SHAPE;
+  if (n_new == 0) return MLA_OK;
+  if (!h || !w_dkv || !w_kr || !positions || !dst_rows || !rows) return MLA_ERR_NULL;
+  if (stride < (int64_t)dims->d_c + dims->d_r) return MLA_ERR_SHAPE;
+  if ((int64_t)n_new * d_model >= kMaxElems || (int64_t)dims->d_c * d_model >= kMaxElems) return MLA_ERR_SHAPE;
+  if (!aligned(positions, 8) || !aligned(dst_rows, 8)) return MLA_ERR_ALIGN;
+  const uintptr_t a = esize(dims);
+  if (!aligned(h, a) || !aligned(w_dkv, a) || !aligned(w_kr, a) || !aligned(rows, a)) return MLA_ERR_ALIGN;
+  if (dims->dtype == MLA_BF16) {
+    if (!mla::kv_append_bf16_supported(d_model, dims->d_c, dims->d_r)) return MLA_ERR_UNSUPPORTED;
+    if (!aligned(h, 16) || !aligned(w_dkv, 16) || !aligned(w_kr, 16)) return MLA_ERR_ALIGN;
+  }
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -141,6 +168,8 @@ const char* mla_status_string(mla_status_t s) {
     case MLA_ERR_DTYPE: return "unknown dtype";
     case MLA_ERR_UNSUPPORTED: return "the library has no kernel for these arguments";
     case MLA_ERR_LAUNCH: return "HIP kernel launch failed";
+    case MLA_ERR_SCRATCH: return "the call needs more than the library's fixed scratch array holds";
+    case MLA_ERR_DEVICE: return "the stream does not belong to the current device";
   }
   return "unknown status";
 }
@@ -224,29 +253,38 @@ mla_status_t mla_kv_append(const mla_dims_t* dims, int32_t n_new, int32_t d_mode
                            const void* w_dkv, const void* w_kr, const int64_t* positions,
                            const int64_t* dst_rows, void* rows, int64_t stride, const mla_rope_t* rope,
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  mla_status_t st = check_dims(dims);
-  if (st != MLA_OK) return st;
   mla::RopeSpec spec;
-  st = rope_spec(rope, &spec);
-  if (st != MLA_OK) return st;
-  if (n_new < 0 || d_model < 1) return MLA_ERR_SHAPE;
-  if (n_new == 0) return MLA_OK;
-  if (!h || !w_dkv || !w_kr || !positions || !dst_rows || !rows) return MLA_ERR_NULL;
-  if (stride < (int64_t)dims->d_c + dims->d_r) return MLA_ERR_SHAPE;
-  if ((int64_t)n_new * d_model >= kMaxElems || (int64_t)dims->d_c * d_model >= kMaxElems) return MLA_ERR_SHAPE;
-  if (!aligned(positions, 8) || !aligned(dst_rows, 8)) return MLA_ERR_ALIGN;
-  const uintptr_t a = esize(dims);
-  if (!aligned(h, a) || !aligned(w_dkv, a) || !aligned(w_kr, a) || !aligned(rows, a)) return MLA_ERR_ALIGN;
+  const mla_status_t st = kv_append_check(dims, n_new, d_model, h, w_dkv, w_kr, positions, dst_rows, rows, stride,
+                                          rope, &spec);
+  if (st != MLA_OK || n_new == 0) return st;
   const bool bf16 = dims->dtype == MLA_BF16;
   if (bf16) {
-    if (!mla::kv_append_bf16_supported(d_model, dims->d_c, dims->d_r)) return MLA_ERR_UNSUPPORTED;
-    if (!aligned(h, 16) || !aligned(w_dkv, 16) || !aligned(w_kr, 16)) return MLA_ERR_ALIGN;
     if (!workspace) return MLA_ERR_NULL;
     if (workspace_bytes < mla::kv_append_workspace_bytes(true, n_new, dims->d_c, dims->d_r)) return MLA_ERR_SHAPE;
     if (!aligned(workspace, 4)) return MLA_ERR_ALIGN;
   }
   return launched(mla::launch_kv_append(bf16, h, w_dkv, w_kr, positions, dst_rows, rows, stride,
                                         (float*)workspace, n_new, d_model, dims->d_c, dims->d_r, spec, stream));
+}
+
+mla_status_t mla_kv_append_noalloc(const mla_dims_t* dims, int32_t n_new, int32_t d_model, const void* h,
+                                   const void* w_dkv, const void* w_kr, const int64_t* positions,
+                                   const int64_t* dst_rows, void* rows, int64_t stride, const mla_rope_t* rope,
+                                   hipStream_t stream) {
+  mla::RopeSpec spec;
+  mla_status_t st = kv_append_check(dims, n_new, d_model, h, w_dkv, w_kr, positions, dst_rows, rows, stride, rope,
+                                    &spec);
+  if (st != MLA_OK || n_new == 0) return st;
+  const bool bf16 = dims->dtype == MLA_BF16;
+  const size_t need = mla::kv_append_workspace_bytes(bf16, n_new, dims->d_c, dims->d_r);
+  if (need > MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need) {
+    st = mla::noalloc_scratch(stream, &ws);
+    if (st != MLA_OK) return st;
+  }
+  return launched(mla::launch_kv_append(bf16, h, w_dkv, w_kr, positions, dst_rows, rows, stride, (float*)ws,
+                                        n_new, d_model, dims->d_c, dims->d_r, spec, stream));
 }
 
 mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, int32_t q_per_seq, const void* q_abs,

@@ -37,7 +37,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert set(names) == set(B.SIGNATURES), names
     for n in names:
         assert hasattr(lib, n)
-    assert lib.mla_abi_version() == 8
+    assert lib.mla_abi_version() == 9
 
 
 def test_calibration_argument_checks(lib):
@@ -54,7 +54,7 @@ def test_calibration_argument_checks(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(9):
         assert lib.mla_status_string(code)
     assert lib.mla_status_string(99) == b"unknown status"
 
@@ -174,6 +174,23 @@ def test_prologue_argument_checks(lib):
     assert app(dims(d_r=63)) == B.MLA_ERR_SHAPE                    # RoPE pairs need an even d_r
     f32 = dims(dtype=B.MLA_F32)
     assert lib.mla_kv_append_workspace_bytes(ctypes.byref(f32), 4) == 0
+    # the no-allocation form: the same checks, then the fixed array's limit, all before any
+    # HIP call (so they run here, with no GPU)
+    nal = lambda d, n=4, dm=5120, h=FAKE, wd=FAKE, wr=FAKE, pos=FAKE, dst=FAKE, rows=FAKE, stride=576: \
+        lib.mla_kv_append_noalloc(ctypes.byref(d), n, dm, h, wd, wr, pos, dst, rows, stride, None, None)
+    assert nal(d, n=0, h=None, wd=None, wr=None, pos=None, dst=None, rows=None) == B.MLA_OK
+    assert nal(d, n=-1) == B.MLA_ERR_SHAPE
+    for k in ("h", "wd", "wr", "pos", "dst", "rows"):
+        assert nal(d, **{k: None}) == B.MLA_ERR_NULL
+    assert nal(d, h=FAKE + 8) == B.MLA_ERR_ALIGN
+    assert nal(d, dm=5000) == B.MLA_ERR_UNSUPPORTED
+    most = B.NOALLOC_SCRATCH_BYTES // (8 * 576 * 4)
+    assert most == 455
+    assert lib.mla_kv_append_workspace_bytes(ctypes.byref(d), most) <= B.NOALLOC_SCRATCH_BYTES
+    assert lib.mla_kv_append_workspace_bytes(ctypes.byref(d), most + 1) > B.NOALLOC_SCRATCH_BYTES
+    assert nal(d, n=most + 1) == B.MLA_ERR_SCRATCH
+    assert nal(d, n=4096) == B.MLA_ERR_SCRATCH
+    assert b"scratch" in lib.mla_status_string(B.MLA_ERR_SCRATCH)
     rope = lambda d, n=4, qc=FAKE, qr=FAKE, w=FAKE, pos=FAKE, out=FAKE, rp=None: \
         lib.mla_absorb_q_rope(ctypes.byref(d), n, qc, qr, w, pos, ctypes.byref(rp) if rp is not None else None,
                               out, None)
