@@ -59,23 +59,18 @@ absorb_q_bf16_kernel(AbsorbParams P) {
   const int d_qk = P.d_c + P.d_r;
 
   char* ostage = smem + P.d_h * kAbsPitch;      // [32][kAbsOutPitch] output staging
+  const int qpitch = P.d_h * 2 + 16;              // q_c staging row: 16 rows of a 16-byte read on distinct banks
+  char* qstage = ostage + 32 * kAbsOutPitch;      // [32][qpitch] the first query block's q_c rows
 
-  // A operands of the first query block, loaded before the weight slice so that the two
-  // memory latencies overlap.
-  const int ksteps = P.d_h / 16;                  // <= 16 (d_h <= 256)
-  bf16x8 qa[16];
-  {
-    const int m = lane & 31;
-    const bf16_bits* q = P.q_c + ((size_t)(m < P.n_q ? m : 0) * P.n_h + i) * P.d_h + 8 * (lane >> 5);
-#pragma unroll
-    for (int s = 0; s < 16; ++s)
-      if (s < ksteps) qa[s] = *(const bf16x8*)(q + 16 * s);
-  }
-
-  // Stage W^UK_i[:, cb:cb+128] in LDS (16-byte chunks, 16 per row): all loads of a
-  // thread are issued before its LDS writes, so their latencies overlap.
+  // The weight slice W^UK_i[:, cb:cb+128] goes out first (16-byte chunks, 16 per row), then
+  // the first block's q_c rows (16-byte chunks, whole rows): the queries are shared by the
+  // four waves, so one copy of them goes through LDS rather than each wave loading its A
+  // operands itself (32 rows per instruction).
   const bf16_bits* w = P.w_uk + (size_t)i * P.d_h * P.d_c + cb;
   const int chunks = P.d_h * (kAbsCols / 8);     // <= 4096 (d_h <= 256)
+  const int ksteps = P.d_h / 16;                  // <= 16 (d_h <= 256)
+  const int qcpr = P.d_h / 8;                     // 16-byte chunks per q_c row
+  const int qchunks = 32 * qcpr;                  // <= 1024
   for (int e0 = 0; e0 < chunks; e0 += 8 * kThreads) {
     bf16x8 v[8];
 #pragma unroll
@@ -83,13 +78,39 @@ absorb_q_bf16_kernel(AbsorbParams P) {
       const int e = e0 + u * kThreads + tid;
       if (e < chunks) v[u] = *(const bf16x8*)(w + (size_t)(e >> 4) * P.d_c + (e & 15) * 8);
     }
+    bf16x8 qv[4];
+    if (e0 == 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = u * kThreads + tid;
+        const int m = e / qcpr;
+        if (e < qchunks && m < P.n_q) qv[u] = *(const bf16x8*)(P.q_c + ((size_t)m * P.n_h + i) * P.d_h + (e % qcpr) * 8);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int e = e0 + u * kThreads + tid;
       if (e < chunks) *(bf16x8*)(smem + (e >> 4) * kAbsPitch + (e & 15) * 16) = v[u];
     }
+    if (e0 == 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = u * kThreads + tid;
+        const int m = e / qcpr;
+        if (e < qchunks) *(bf16x8*)(qstage + m * qpitch + (e % qcpr) * 16) = m < P.n_q ? qv[u] : bf16x8{};
+      }
+    }
   }
   __syncthreads();
+
+  // A operands of the first query block from the staged rows
+  bf16x8 qa[16];
+  {
+    const char* qrow = qstage + (lane & 31) * qpitch + 16 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s < ksteps) qa[s] = *(const bf16x8*)(qrow + 32 * s);
+  }
 
   // B operands for every k-step: lane l gets W[16s + 8(l/32) + j][32w + l%32], j = 0..7.
   bf16x8 wb[16];
@@ -556,7 +577,11 @@ hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, cons
     return hipGetLastError();
   }
   AbsorbParams P{q_c, q_r, w_uk, q_abs, n_q, n_h, d_h, d_c, d_r, positions, rope};
-  const size_t smem = (size_t)d_h * kAbsPitch + 32 * kAbsOutPitch;
+  const size_t smem = (size_t)d_h * kAbsPitch + 32 * kAbsOutPitch + (size_t)32 * (d_h * 2 + 16);
+  static const hipError_t attr = hipFuncSetAttribute((const void*)absorb_q_bf16_kernel,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)(256 * kAbsPitch + 32 * kAbsOutPitch + 32 * (256 * 2 + 16)));
+  if (attr != hipSuccess) return attr;
   const int grid = 8 * ((n_h + 7) / 8) * (d_c / kAbsCols);
   hipLaunchKernelGGL(absorb_q_bf16_kernel, dim3(grid), dim3(kThreads), smem, stream, P);
   return hipGetLastError();

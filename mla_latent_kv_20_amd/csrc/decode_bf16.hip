@@ -187,7 +187,8 @@ mla_decode_bf16_kernel(DecodeParams P) {
   //  - seqs_per_xcd > 0 (16 or more sequences): every workgroup ranks the sequences by
   //    length (longest first, ties by index) and XCD x takes ranks x, 15-x, 16+x, 31-x, ...
   //    (snake order), longest first.  Every XCD then gets the same number of sequences
-  //    and nearly the same number of tiles, however ragged the lengths.  Only non-empty
+  //    and nearly the same number of tiles, however ragged the lengths.  When every length
+  //    is equal the ranks are the indices and the ranking is skipped.  Only non-empty
   //    splits are enumerated (the split-0 workgroup marks the empty ones): the dispatcher
   //    deals an XCD's workgroups to its shader engines in a fixed rotation, so empty
   //    workgroups interleaved with real ones would load the engines unevenly.
@@ -199,6 +200,7 @@ mla_decode_bf16_kernel(DecodeParams P) {
   if (P.streams >= 8 && j >= P.streams_per_xcd) return;
   int b, s;
   int used_splits = P.num_splits;                  // splits of sequence b that hold rows
+  int64_t row0_l = -1, len_l = 0;                  // from LDS when the ranked mapping read them
   if (P.streams < 8) {
     // fewer streams than XCDs (one long prefill, a few sequences): (stream, member) items
     // dealt round-robin over the XCDs, so that every XCD works
@@ -208,44 +210,78 @@ mla_decode_bf16_kernel(DecodeParams P) {
     b = stream / P.num_splits;
     s = stream - b * P.num_splits;
   } else if (P.seqs_per_xcd > 0) {
-    // lengths in LDS (free until the first loads), padded to a multiple of 4 with -1,
-    // which ranks below every length
-    const int bpad = (P.batch + 3) & ~3;
-    int* lens = (int*)smem;                        // [bpad]
+    // offsets and lengths in LDS (free until the first loads), the lengths padded to a
+    // multiple of 16 with -1, which ranks below every length
+    const int bpad = (P.batch + 15) & ~15;
+    int64_t* offs = (int64_t*)smem;                // [batch]: each sequence's first row, read once
+    int* lens = (int*)(offs + bpad);               // [bpad]
     int* by_rank = lens + bpad;                    // [batch]: sequence of each rank
-    for (int i = threadIdx.x; i < bpad; i += kThreads)
-      lens[i] = i < P.batch ? (int)(P.offsets[i + 1] - P.offsets[i]) : -1;
-    __syncthreads();
-    for (int c = threadIdx.x; c < P.batch; c += kThreads) {
-      const int lc = lens[c];
-      int rank = 0;
-      for (int i = 0; i < bpad; i += 4) {
-        typedef int i32x4 __attribute__((ext_vector_type(4)));
-        const i32x4 v = *(const i32x4*)(lens + i);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rank += (v[e] > lc || (v[e] == lc && i + e < c)) ? 1 : 0;
-      }
-      by_rank[rank] = c;                           // the ranks are a permutation of 0..batch-1
+    for (int i = threadIdx.x; i < bpad; i += kThreads) {
+      const int64_t o0 = i < P.batch ? P.offsets[i] : 0;
+      const int64_t o1 = i < P.batch ? P.offsets[i + 1] : 0;
+      lens[i] = i < P.batch ? (int)(o1 - o0) : -1;
+      if (i < P.batch) offs[i] = o0;
     }
     __syncthreads();
+    // Equal lengths (every wave finds the same): the ranks are the sequence indices.
+    const int len0 = lens[0];
+    bool uniform = true;
+    for (int i0 = 0; i0 < P.batch; i0 += 64) {
+      const int i = i0 + (int)(threadIdx.x & 63);
+      uniform = uniform && __all(i >= P.batch || lens[i] == len0);
+    }
+    if (!uniform) {
+      for (int c = threadIdx.x; c < P.batch; c += kThreads) {
+        const int lc = lens[c];
+        int rank = 0;
+        typedef int i32x4 __attribute__((ext_vector_type(4)));
+        for (int i = 0; i < bpad; i += 16) {       // four reads in flight
+          i32x4 v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = *(const i32x4*)(lens + i + 4 * q);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rank += (v[q][e] > lc || (v[q][e] == lc && i + 4 * q + e < c)) ? 1 : 0;
+        }
+        by_rank[rank] = c;                         // the ranks are a permutation of 0..batch-1
+      }
+      __syncthreads();
+    }
     // this XCD's sequences in rank order, each with its non-empty splits: item j
-    int base = 0;
     b = -1;
     s = 0;
-    for (int m = 0; m < P.seqs_per_xcd; ++m) {
-      const int p = 8 * m + ((m & 1) ? 7 - xcd : xcd);
-      if (p >= P.batch) break;                     // p grows with m
-      const int bm = by_rank[p];
-      const int len = lens[bm];
-      int ns = P.split_rows > 0 ? (len + P.split_rows - 1) / P.split_rows : P.num_splits;
+    if (uniform) {
+      int ns = P.split_rows > 0 ? (len0 + P.split_rows - 1) / P.split_rows : P.num_splits;
       ns = ns < 1 ? 1 : (ns > P.num_splits ? P.num_splits : ns);
-      if (j < base + ns) {
-        b = bm;
-        s = j - base;
+      const int m = j / ns;
+      const int p = 8 * m + ((m & 1) ? 7 - xcd : xcd);
+      if (m < P.seqs_per_xcd && p < P.batch) {
+        b = p;
+        s = j - m * ns;
         used_splits = ns;
-        break;
+        row0_l = offs[p];
+        len_l = len0;
       }
-      base += ns;
+    } else {
+      int base = 0;
+      for (int m = 0; m < P.seqs_per_xcd; ++m) {
+        const int p = 8 * m + ((m & 1) ? 7 - xcd : xcd);
+        if (p >= P.batch) break;                   // p grows with m
+        const int bm = by_rank[p];
+        const int len = lens[bm];
+        int ns = P.split_rows > 0 ? (len + P.split_rows - 1) / P.split_rows : P.num_splits;
+        ns = ns < 1 ? 1 : (ns > P.num_splits ? P.num_splits : ns);
+        if (j < base + ns) {
+          b = bm;
+          s = j - base;
+          used_splits = ns;
+          row0_l = offs[bm];
+          len_l = len;
+          break;
+        }
+        base += ns;
+      }
     }
     __syncthreads();                               // every wave has read LDS before it is reused
     if (b < 0) return;                             // past this XCD's items (workgroup-uniform)
@@ -268,8 +304,8 @@ mla_decode_bf16_kernel(DecodeParams P) {
   // barriers; they read the last head's query and store nothing.
   const bool active = hg * kHeadsPerWg + wave * 32 < P.n_h;   // wave-uniform
 
-  const int64_t row0 = P.offsets[b];
-  const int64_t len = P.offsets[b + 1] - row0;
+  const int64_t row0 = row0_l >= 0 ? row0_l : P.offsets[b];
+  const int64_t len = row0_l >= 0 ? len_l : P.offsets[b + 1] - row0;
   const int64_t vis = len - P.q_per_seq + r + 1;
   int64_t lo, hi;
   if (P.num_splits == 1) {
@@ -628,7 +664,7 @@ hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* rows, int
   size_t smem = (size_t)kStages * kTileBytes;   // the query staging area lies inside the ring
   const size_t out_stage = (size_t)kWaves * 32 * (f16_partials ? out_row_bytes<_Float16>() : out_row_bytes<float>());
   smem = smem > out_stage ? smem : out_stage;
-  if (P.seqs_per_xcd > 0 && (size_t)(2 * (batch + 3)) * sizeof(int) > smem) {   // lengths and ranks do not fit in LDS
+  if (P.seqs_per_xcd > 0 && (size_t)((batch + 15) & ~15) * (sizeof(int64_t) + 2 * sizeof(int)) > smem) {
     P.seqs_per_xcd = 0;
     P.streams_per_xcd = (P.streams + 7) / 8;
   }

@@ -319,3 +319,21 @@ def test_check_offsets(lib):
     assert B.check_offsets(np.array([0, 4, 9], np.int64), 2, 4, 9) == B.MLA_OK
     assert B.check_offsets(np.array([-1, 4], np.int64), 1, 1, 9) == B.MLA_ERR_SHAPE
     assert B.check_offsets(np.zeros(1, np.int64), 0, 1, 0) == B.MLA_OK
+
+
+def test_no_kernel_spills_to_scratch():
+    """The build records the compiler's per-kernel resource figures; no kernel may spill (a
+    spill in the decode's tile loop would cost a memory round trip per tile)."""
+    import csv
+    import os
+    path = os.path.join(os.path.dirname(B.LIB_PATH), "kernel_resources.txt")
+    if not os.path.exists(path):
+        pytest.skip("library not built")
+    rows = list(csv.DictReader(open(path), delimiter="\t"))
+    assert any("mla_decode_bf16_kernel" in r["kernel"] for r in rows)
+    for r in rows:
+        assert r["ScratchSize [bytes/lane]"] == "0", r["kernel"]
+        assert r["VGPRs Spill"] == "0", r["kernel"]
+    # the bf16 decode holds a 128-head group per workgroup: one wave per SIMD, every register
+    dec = [r for r in rows if "mla_decode_bf16_kernel" in r["kernel"]]
+    assert all(int(r["VGPRs"]) + int(r["AGPRs"]) <= 512 for r in dec)
