@@ -46,8 +46,10 @@ constexpr int kLoads = kTile * kChunks / kThreads;            // 9 loads of 1 Ki
 constexpr int kStages = 3;              // tile ring: scores of t, weighted sum of t-1, loads of t+1
 constexpr int kKSteps = kDqk / 16;       // 36 MFMA k-steps for the scores
 constexpr int kKReg = kDc / 16;          // 32 k-steps of the latent part (then 4 of the RoPE part)
-constexpr int kQStageWave = 32 * 512;    // query staging per wave: 32 heads x 256 columns bf16
-constexpr int kQStageLoads = 2 * kQStageWave / 1024;          // 1 KiB loads per wave, both halves' worth
+constexpr int kQStaged = 30;             // latent k-steps of the queries staged through LDS
+constexpr int kQChunks = 2 * kQStaged;   // 16-byte chunks per head in the staging area (60)
+constexpr int kQStageWave = 32 * kQChunks * 16;               // 30 KiB per wave: 32 heads
+constexpr int kQStageLoads = kQStageWave / 1024;              // 30 loads of 1 KiB per wave
 constexpr int kDvTiles = kDc / 32;       // 16 output tiles of 32 dv
 constexpr float kRescaleSlack = 8.0f;    // log2 units
 constexpr int kKAhead = 6;               // K operand reads in flight
@@ -58,7 +60,7 @@ constexpr int kWaitVmcnt0 = 0x0F70;      // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt
 static_assert(kTile * kChunks == kLoads * kThreads, "tile must split evenly into 1 KiB loads");
 static_assert(kKSteps == 4 * kLoads, "one tile load per 4 score steps");
 static_assert(kKSteps - kKReg == 4, "RoPE part: 4 k-steps of 16");
-static_assert(kTileBytes + kWaves * kQStageWave <= kStages * kTileBytes, "query staging fits in stages 1-2");
+static_assert(kTileBytes + kWaves * kQStageWave <= 160 * 1024, "tile 0 and the query staging fit in LDS");
 
 // Issue order of the score k-steps when they are interleaved with the weighted sum: the
 // latent steps 0..31 in order (one accumulator chain), the 4 RoPE steps (a second chain)
@@ -340,30 +342,19 @@ mla_decode_bf16_kernel(DecodeParams P) {
   const uint32_t lane16 = (uint32_t)lane * 16;
 
   // ---- prologue.  Queries: all 36 k-steps (latent and RoPE parts) live in VGPRs as MFMA
-  // B operands for the whole split.  The latent part comes in two halves of 256 columns,
-  // issued together: half 0 through an LDS staging area with direct-to-LDS loads, each
-  // instruction reading two contiguous 512-byte half-rows, and half 1 with the 64 RoPE
-  // columns straight into registers in the MFMA layout (32 rows per instruction; the
-  // staging area has room for one half only).  The staging area lies in tile stages 1-2,
-  // which take no loads before the barrier that opens tile 0.  In it, wave w owns heads
-  // 32w .. 32w+31 at 512 bytes each, chunk c of head h stored at chunk c ^ (h & 15).
+  // B operands for the whole split.  Latent k-steps 0..29 come through an LDS staging area
+  // by direct-to-LDS loads of contiguous 16-byte chunks (8 cache lines per instruction);
+  // k-steps 30-31 and the 4 RoPE steps load straight into their registers in the MFMA
+  // layout (32 rows per instruction).  The staging area follows tile stage 0 and takes
+  // tile stages 1-2 (no loads before the barrier that opens tile 0) and the LDS beyond the
+  // ring.  In it, wave w owns heads 32w .. 32w+31 at kQChunks chunks each, logical chunk c
+  // of head h stored at c ^ ((h >> 2) & 3): the 16 heads of a 16-lane read then fall on
+  // 16 distinct bank groups.
   bf16x8 qb[kKSteps];
   char* qstage = smem + kTileBytes + wave * kQStageWave;
   const char* qbase = (const char*)(P.q_abs + ((size_t)n * P.n_h + hg * kHeadsPerWg) * kDqk);
-  uint32_t qoff[kQStageLoads / 2];               // per-lane source offsets of half 0
-#pragma unroll
-  for (int j = 0; j < kQStageLoads / 2; ++j) {
-    const int hl = 2 * j + (lane >> 5);          // head of the wave filled by this lane
-    int hq = wave * 32 + hl;
-    hq = hg * kHeadsPerWg + hq < P.n_h ? hq : P.n_h - 1 - hg * kHeadsPerWg;
-    const int c = (lane & 31) ^ (hl & 15);
-    qoff[j] = (uint32_t)(hq * kRowBytes + c * 16);
-  }
-  const uint32_t qstage_lds = __builtin_amdgcn_readfirstlane(lds_addr(qstage));
-#pragma unroll
-  for (int j = 0; j < kQStageLoads / 2; ++j) global_to_lds16_sv(qbase, qoff[j], qstage_lds + j * 1024);
 
-  // first tile
+  // first tile: its loads go out first (they come from HBM, the queries mostly from L2)
   {
     const char* src = first_row;
     char* stage = smem;
@@ -376,23 +367,35 @@ mla_decode_bf16_kernel(DecodeParams P) {
       for (int i = 0; i < kLoads; ++i) load_clamped(src, stride_bytes, rmax, stage, wave, i, lane);
     }
   }
-  // Half 1 and the RoPE part go straight into their B-operand registers (lane l: head
-  // l%32, 16 bytes per k-step), so that their memory latency overlaps that of half 0.
+  {
+    const uint32_t qstage_lds = __builtin_amdgcn_readfirstlane(lds_addr(qstage));
+    const int hmax = P.n_h - 1 - hg * kHeadsPerWg;   // last head of the group that exists
+#pragma unroll
+    for (int j = 0; j < kQStageLoads; ++j) {
+      const int g = 64 * j + lane;                 // slot of this lane's chunk
+      const int h = g / kQChunks;                  // head of the wave
+      const int c = (g - h * kQChunks) ^ ((h >> 2) & 3);
+      int hq = wave * 32 + h;
+      hq = hq < hmax ? hq : hmax;
+      global_to_lds16_sv(qbase, (uint32_t)(hq * kRowBytes + c * 16), qstage_lds + j * 1024);
+    }
+  }
+  // k-steps 30-31 and the RoPE part straight into their B-operand registers (lane l: head
+  // l%32, 16 bytes per k-step)
   {
     int hq = wave * 32 + (lane & 31);
     hq = hg * kHeadsPerWg + hq < P.n_h ? hq : P.n_h - 1 - hg * kHeadsPerWg;
-    const bf16_bits* qh = (const bf16_bits*)qbase + (size_t)hq * kDqk + kDc / 2 + 8 * (lane >> 5);
+    const bf16_bits* qh = (const bf16_bits*)qbase + (size_t)hq * kDqk + 8 * (lane >> 5);
 #pragma unroll
-    for (int ks = 0; ks < kKReg / 2; ++ks) qb[kKReg / 2 + ks] = *(const bf16x8*)(qh + 16 * ks);
-#pragma unroll
-    for (int ks = 0; ks < kKSteps - kKReg; ++ks) qb[kKReg + ks] = *(const bf16x8*)(qh + kDc / 2 + 16 * ks);
+    for (int ks = kQStaged; ks < kKSteps; ++ks) qb[ks] = *(const bf16x8*)(qh + 16 * ks);
   }
-  const char* qrd = qstage + (lane & 31) * 512;  // this lane's head row in the staging area
-  const int qx = lane & 15;                      // its chunk swap (head & 15)
-  wait_vmcnt<kLoads + kKReg / 2 + (kKSteps - kKReg)>();   // half 0 landed
+  const int qh_l = lane & 31;                    // this lane's head in the staging area
+  const char* qrd = qstage + qh_l * (kQChunks * 16);
+  const int qx = (qh_l >> 2) & 3;                // its chunk swap
+  wait_vmcnt<kKSteps - kQStaged>();              // tile 0 and the staged queries landed
 #pragma unroll
-  for (int ks = 0; ks < kKReg / 2; ++ks) qb[ks] = *(const bf16x8*)(qrd + 16 * ((2 * ks + (lane >> 5)) ^ qx));
-  wait_vmcnt<0>();                               // half 1 and the first tile landed
+  for (int ks = 0; ks < kQStaged; ++ks) qb[ks] = *(const bf16x8*)(qrd + 16 * ((2 * ks + (lane >> 5)) ^ qx));
+  wait_vmcnt<0>();                               // the directly loaded steps landed
   // All queries (and the first tile) resident.  A builtin wait, so the compiler knows
   // the query loads have landed and places no vmcnt waits for them inside the tile loop,
   // where they would also stall on in-flight tile prefetches.
@@ -661,7 +664,8 @@ hipError_t launch_decode_bf16(const bf16_bits* q_abs, const bf16_bits* rows, int
   P.seqs_per_xcd = batch >= 16 ? (batch + 7) / 8 : 0;
   P.streams_per_xcd = P.seqs_per_xcd > 0 ? P.seqs_per_xcd * num_splits : (P.streams + 7) / 8;
   P.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  size_t smem = (size_t)kStages * kTileBytes;   // the query staging area lies inside the ring
+  size_t smem = (size_t)kTileBytes + (size_t)kWaves * kQStageWave;   // tile 0 and the query staging
+  smem = smem > (size_t)kStages * kTileBytes ? smem : (size_t)kStages * kTileBytes;
   const size_t out_stage = (size_t)kWaves * 32 * (f16_partials ? out_row_bytes<_Float16>() : out_row_bytes<float>());
   smem = smem > out_stage ? smem : out_stage;
   if (P.seqs_per_xcd > 0 && (size_t)((batch + 15) & ~15) * (sizeof(int64_t) + 2 * sizeof(int)) > smem) {

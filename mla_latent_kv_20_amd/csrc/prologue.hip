@@ -13,7 +13,8 @@
 // bf16, two kernels.  At decode batch sizes the call is bound by the down-projection
 // weights ((d_c + d_r) x d_model), so they are spread over many workgroups: workgroup =
 // (32 output columns, 32 tokens, one of kSplitK slices of d_model), four waves splitting
-// the slice, every load of a wave in flight at once.  Each workgroup writes its fp32 32x32
+// the slice, every load of a wave in flight at once.  Slice ks runs on XCD ks, so each
+// XCD's L2 fetches only its eighth of the hidden states.  Each workgroup writes its fp32 32x32
 // product to the caller's workspace; the finishing kernel sums the slices in order,
 // rotates the k^R pairs (columns k and k + d_r/2 of one token) and stores bf16 rows.
 #include "mla_common.h"
@@ -22,6 +23,7 @@ namespace mla {
 namespace {
 
 constexpr int kSplitK = 8;                    // slices of d_model over workgroups
+static_assert(kSplitK == 8, "one slice of d_model per XCD");
 constexpr int kAppWaves = 4;
 constexpr int kAppThreads = kAppWaves * 64;
 constexpr int kMaxSteps = 16;                 // k-steps of 16 per wave: d_model <= 8*4*16*16
@@ -44,9 +46,13 @@ __global__ void __launch_bounds__(kAppThreads)
 kv_append_partial_kernel(AppendParams P) {
   __shared__ f32x16 red[kAppWaves][64];
   const int width = P.d_c + P.d_r;
-  const int cb = blockIdx.x;                      // 32-column block of [c^KV | k^R]
-  const int tok0 = blockIdx.y * 32;
-  const int ks = blockIdx.z;                      // K slice
+  // Workgroups are dealt round-robin over the 8 XCDs (workgroup L on XCD L % 8): slice ks
+  // of d_model runs on XCD ks, so each XCD's L2 fetches only its slice of the hidden states.
+  const int L = blockIdx.x;
+  const int ks = L % kSplitK;                     // K slice
+  const int cbs = (P.d_c + P.d_r) / 32;
+  const int cb = (L / kSplitK) % cbs;             // 32-column block of [c^KV | k^R]
+  const int tok0 = (L / kSplitK / cbs) * 32;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int tok = tok0 + (lane & 31);
@@ -173,7 +179,7 @@ hipError_t launch_kv_append(bool bf16, const void* h, const void* w_dkv, const v
                             hipStream_t stream) {
   AppendParams P{h, w_dkv, w_kr, positions, dst_rows, rows, workspace, stride, n_new, d_model, d_c, d_r, rope};
   if (bf16) {
-    hipLaunchKernelGGL(kv_append_partial_kernel, dim3((d_c + d_r) / 32, (n_new + 31) / 32, kSplitK),
+    hipLaunchKernelGGL(kv_append_partial_kernel, dim3((d_c + d_r) / 32 * ((n_new + 31) / 32) * kSplitK),
                        dim3(kAppThreads), 0, stream, P);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
