@@ -46,6 +46,7 @@ constexpr int kTileBytes = kTile * kRowBytes;                 // 18432
 constexpr int kTileBlocks = kTileBytes / 1024;                // 18 loads of 1 KiB
 constexpr int kScaleArea = 256;          // a 4-byte direct-to-LDS load fills 64 x 4 bytes
 constexpr int kStageBytes = kTileBytes + 1024;                // tile, two scale areas, padding
+constexpr int kQStageWave = 32 * 1024;   // query staging per wave: 32 heads x 512 latent bf16
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kHeadsPerWg = kWaves * 32;
@@ -61,6 +62,7 @@ constexpr int kWaitVmcnt0 = 0x0F70;      // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt
 
 static_assert(kTileBlocks == 4 * kLoads - 2, "waves 0-1 load five blocks, waves 2-3 four and the scales");
 static_assert(kStageBytes % 1024 == 0 && kTileBytes + 2 * kScaleArea <= kStageBytes, "stage layout");
+static_assert(kStageBytes + kWaves * kQStageWave <= 160 * 1024, "tile 0 and the query staging fit in LDS");
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -384,13 +386,36 @@ mla_decode_fp8_kernel(DecodeParams P) {
   i32x8 qhi[kKSteps], qlo[kKSteps];
   float q_log2_scale;                          // scale_log2 * 2^-e_h: MFMA sums to log2 units
   {
-    const bf16_bits* qh = P.q_abs + ((size_t)n * P.n_h + head_ld) * kDqk + 32 * (lane >> 5);
+    // The latent part (k-steps 0..7) comes through an LDS staging area after tile stage 0,
+    // by direct-to-LDS loads of one head's contiguous 1 KiB per instruction (wave w: heads
+    // 32w .. 32w+31 of the group, chunk c of head h stored at c ^ (h & 15), so the 16 heads
+    // of a 16-lane read fall on distinct bank groups); the RoPE k-step loads straight into
+    // registers.  Loaded per lane in the operand layout, every instruction touched 32 rows.
     i32x4 raw[kKSteps][4];
+    {
+      const char* qbase = (const char*)(P.q_abs + ((size_t)n * P.n_h + hg * kHeadsPerWg) * kDqk);
+      const int hmax = P.n_h - 1 - hg * kHeadsPerWg;   // last head of the group that exists
+      const uint32_t qlds = __builtin_amdgcn_readfirstlane(lds_addr(smem + kStageBytes + wave * kQStageWave));
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
+      for (int j = 0; j < 32; ++j) {
+        const int hq = wave * 32 + j < hmax ? wave * 32 + j : hmax;
+        global_to_lds16_sv(qbase, (uint32_t)(hq * (kDqk * 2) + ((lane ^ (j & 15)) * 16)), qlds + j * 1024);
+      }
+    }
+    const bf16_bits* qh = P.q_abs + ((size_t)n * P.n_h + head_ld) * kDqk + 32 * (lane >> 5);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) raw[ks][u] = *(const i32x4*)(qh + 64 * ks + 8 * u);
-    wait_vmcnt<0>();                           // the queries and tile 0
+    for (int u = 0; u < 4; ++u) raw[kKSteps - 1][u] = *(const i32x4*)(qh + 64 * (kKSteps - 1) + 8 * u);
+    wait_vmcnt<4>();                           // tile 0 and the staged queries
+    {
+      const int hl = lane & 31;
+      const char* qrd = smem + kStageBytes + wave * kQStageWave + hl * 1024;
+#pragma unroll
+      for (int ks = 0; ks < kKSteps - 1; ++ks)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          raw[ks][u] = *(const i32x4*)(qrd + 16 * ((8 * ks + 4 * (lane >> 5) + u) ^ (hl & 15)));
+    }
+    wait_vmcnt<0>();                           // the RoPE k-step
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     uint32_t amax = 0;                         // largest |q| (bf16 magnitudes order as integers)
 #pragma unroll
@@ -628,7 +653,8 @@ hipError_t launch_decode_fp8(const bf16_bits* q_abs, const uint8_t* codes, int64
   P.seqs_per_xcd = batch >= 16 ? (batch + 7) / 8 : 0;
   P.streams_per_xcd = P.seqs_per_xcd > 0 ? P.seqs_per_xcd * num_splits : (P.streams + 7) / 8;
   P.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  size_t smem = (size_t)kStages * kStageBytes;
+  size_t smem = (size_t)kStageBytes + (size_t)kWaves * kQStageWave;   // tile 0 and the query staging
+  smem = smem > (size_t)kStages * kStageBytes ? smem : (size_t)kStages * kStageBytes;
   const size_t out_stage = (size_t)kWaves * 32 * (f16_partials ? out_row_bytes<_Float16>() : out_row_bytes<float>());
   smem = smem > out_stage ? smem : out_stage;
   if (P.seqs_per_xcd > 0 && (size_t)((batch + 15) & ~15) * (sizeof(int64_t) + 2 * sizeof(int)) > smem) {
