@@ -190,6 +190,26 @@ def test_decode_fp8_head_counts_off_the_group_size(torch, n_h):
     check("lse_part", D.to_numpy_f64(lp), rl, lse=True)
 
 
+@pytest.mark.parametrize("lengths", [[70] * 24, [70] * 11 + [71] + [70] * 12])
+def test_decode_fp8_sixteen_or_more_sequences(torch, lengths):
+    """The length-dealt mapping at 24 sequences, equal lengths (ranks read off) and one
+    longer sequence (ranked), with an empty last split."""
+    w = W.make_workload("uni8", **W.DSV2, dtype=W.BF16, lengths=lengths, seed=11)
+    say(f"[decode_fp8] {len(lengths)} sequences, {'equal' if len(set(lengths)) == 1 else 'unequal'} lengths")
+    codes, scales, deq = quantize_on_gpu(torch, w, D.packed_rows(w))
+    qa = W.draw_q_abs(w)
+    op, lp = B.decode_fp8(dims_of(w), D._tensor(qa, W.BF16, "cuda"), codes, scales,
+                          torch.from_numpy(w.offsets.astype(np.int64)).cuda(), w.batch, 1, 4, 32,
+                          partial_dtype=B.MLA_F16)
+    torch.cuda.synchronize()
+    ro, rl = O.split_partials(W.to_f64(qa, W.BF16), deq[:, :512], deq[:, 512:], w.offsets, 1, 4, 32,
+                              O.default_scale(w.d_h, w.d_r))
+    live = ~np.isneginf(rl)
+    assert not live.all()
+    check("o_part", D.to_numpy_f64(op)[live], ro[live])
+    check("lse_part", D.to_numpy_f64(lp), rl, lse=True)
+
+
 def fp8_step(torch, w, codes, scales, S, R):
     """absorb_q, decode_fp8, merge_out_proj through the ABI; returns o_c, lse, o_lat."""
     d = dims_of(w)

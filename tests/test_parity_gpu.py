@@ -411,6 +411,21 @@ def test_head_counts_off_the_group_size(torch, n_h):
     check_lse("lse", got["lse"], ref["lse"], step_lse_bound(oracle_args(w), w), say)
 
 
+@pytest.mark.parametrize("lengths", [[70] * 24, [70] * 11 + [71] + [70] * 12])
+def test_sixteen_or_more_sequences_equal_and_unequal(torch, lengths):
+    """At 16 or more sequences the decode deals them to XCDs by length; with every length
+    equal it takes the ranks as the indices without ranking.  Both, with the last of 4 splits
+    of 32 rows left empty (70 rows need 3), so the split-0 workgroup marks it."""
+    w = W.make_workload("uni", **W.DSV2, dtype=W.BF16, lengths=lengths, seed=11)
+    a = oracle_args(w)
+    say(f"[edge] {len(lengths)} sequences, {'equal' if len(set(lengths)) == 1 else 'unequal'} lengths, 4 x 32")
+    got = run_step(w, 4, 32)
+    ref = O.absorbed_decode(**a, num_splits=4, split_rows=32)
+    assert_close("o_c", got["o_c"], ref["o_c"], w)
+    assert_close("o_lat", got["o_lat"], ref["o_lat"], w)
+    check_lse("lse", got["lse"], ref["lse"], step_lse_bound(a, w), say)
+
+
 def test_split_plans_agree_and_runs_repeat_bitwise(torch):
     w = workload("dsv2_small")
     say("[edge] split plans 1/7/64 and repeatability")
