@@ -23,6 +23,7 @@ constexpr int kFDc = 512;                    // latent width handled (one 512-wi
 constexpr int kFPitch = kFDc * 2 + 16;       // bf16 o_lat row in LDS, padded against conflicts
 constexpr int kFSteps = kFDc / 64;           // k-steps of 16 per wave: a quarter of d_c
 constexpr int kFFast = 8;                    // splits whose loads all go out at once
+static_assert(kFFast == 8, "the split-weight sum below is written out for 8 splits");
 constexpr int kFWRowBytes = kFDc * 2;        // one W^UV row (bf16)
 
 struct FusedParams {
@@ -176,12 +177,18 @@ __device__ __forceinline__ void merge_rows_fast(const PartT* o_part, const float
                                                 float* z) {
   constexpr int kVec = 16 / (int)sizeof(PartT);       // elements per 16-byte load
   typedef PartT pvec __attribute__((ext_vector_type(kVec)));
-  float lse_l[kRows];
+  // Every lane holds all of a row's split lse values (wave-uniform loads), so the maximum,
+  // the weights and their sum need no cross-lane exchange.  The sum runs in the tree a
+  // butterfly over lanes 0..7 would form, ((w0 + w4) + (w2 + w6)) + ((w1 + w5) + (w3 + w7)),
+  // with zero weights for absent splits.
+  float lse[kRows][kFFast];
   pvec raw[kRows][kFFast][8 / kVec];
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
     const bool live = r < nrows;
-    lse_l[r] = live && lane < num_splits ? lse_part[(size_t)lane * qh_count + qh[r]] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kFFast; ++k)
+      lse[r][k] = live && k < num_splits ? lse_part[(size_t)k * qh_count + qh[r]] : -INFINITY;
 #pragma unroll
     for (int k = 0; k < kFFast; ++k)
       if (live && k < num_splits)
@@ -192,20 +199,25 @@ __device__ __forceinline__ void merge_rows_fast(const PartT* o_part, const float
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
     if (r >= nrows) break;
-    M[r] = fwave_max(lse_l[r]);
-    if (M[r] == -INFINITY) {
+    float m = lse[r][0];
+#pragma unroll
+    for (int k = 1; k < kFFast; ++k) m = fmaxf(m, lse[r][k]);
+    M[r] = m;
+    if (m == -INFINITY) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
       z[r] = 0.f;
       continue;
     }
-    const float w_l = expf(lse_l[r] - M[r]);
-    z[r] = fwave_sum(w_l);
+    float w[kFFast];
+#pragma unroll
+    for (int k = 0; k < kFFast; ++k) w[k] = k < num_splits ? expf(lse[r][k] - m) : 0.f;
+    z[r] = ((w[0] + w[4]) + (w[2] + w[6])) + ((w[1] + w[5]) + (w[3] + w[7]));
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kFFast; ++k) {
       if (k < num_splits) {
-        const float ws = __shfl(w_l, k);
+        const float ws = w[k];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, (float)raw[r][k][e / kVec][e % kVec], acc[e]) : acc[e];
       }
@@ -221,22 +233,22 @@ __device__ __forceinline__ void merge_rows_fast(const PartT* o_part, const float
 // W^UV_i (128 KiB) first streams into LDS with direct-to-LDS loads of one whole 1 KiB row
 // each; read straight into the MFMA operand layout, every load instruction would touch 32
 // rows at 32 bytes each (16.5 against 15.3 us at 32 queries).  Each of the 8 waves then
-// merges 2 of the block's rows (every load in flight at once) into LDS as bf16.  The projection then runs as in mla_out_proj: for each 32-column block of
-// d_h, four k quarters of 8 MFMA steps summed in quarter order; wave w computes column
-// block (w & 3) for quarters (w >> 2) and (w >> 2) + 2.  The MFMA M dimension is 32, so
-// rows 16-31 of each product repeat rows 0-15 and are not stored.
+// merges 2 of the block's rows (every load in flight at once) into LDS as bf16.  The
+// projection then runs as in mla_out_proj: for each 32-column block of d_h, four k quarters
+// of 8 MFMA steps summed in quarter order.  Waves 0-3 take column block w with all four
+// quarters as independent chains in registers, so no partial product goes through LDS and
+// the other four waves are done after the merge.  The MFMA M dimension is 32, so rows 16-31
+// of each product repeat rows 0-15 and are not stored.
 constexpr int kFRows = 16;                   // query rows per workgroup
 constexpr int kFColBlocks = 4;               // 32-column blocks of d_h = 128
 
 template <typename PartT>
 __global__ void __launch_bounds__(kFThreads)
 merge_out_proj_kernel(FusedParams P) {
-  // LDS: W^UV_i (d_h rows of 1 KiB, chunk c of row r at c ^ (r & 15)), reused for the
-  // k-quarter partial products once the MFMAs have read it; then o_lat rows (bf16)
+  // LDS: W^UV_i (d_h rows of 1 KiB, chunk c of row r at c ^ (r & 15)), then o_lat rows (bf16)
   extern __shared__ __attribute__((aligned(1024))) char smem_f[];
   char* w_lds = smem_f;
   char* o_lds = smem_f + 32 * kFColBlocks * kFWRowBytes;
-  f32x16 (*red)[kFColBlocks][64] = (f32x16 (*)[kFColBlocks][64])smem_f;   // [k quarter][column block][lane]
   const int qblocks = (P.n_q + kFRows - 1) / kFRows;
   const int xcd = blockIdx.x & 7;
   const int kq = blockIdx.x >> 3;
@@ -250,10 +262,8 @@ merge_out_proj_kernel(FusedParams P) {
   const PartT* o_part = (const PartT*)P.o_part;
   const int rows = P.n_q - mb < kFRows ? P.n_q - mb : kFRows;
 
-  // B operands: lane l holds W^UV_i[32 cbk + l%32][16 (8 q + s) + 8 (l/32) .. +7] for the
-  // wave's two quarters q
+  // B operands (waves 0-3): lane l holds W^UV_i[32 cbk + l%32][16 (8 q + s) + 8 (l/32) .. +7]
   const int cbk = wave & 3;
-  const int q0 = wave >> 2;
   // W^UV_i streams into LDS first: each instruction one whole 1 KiB row (wave w: rows
   // 16w .. 16w+15), lane L filling physical chunk L with logical chunk L ^ (r & 15)
   {
@@ -305,37 +315,30 @@ merge_out_proj_kernel(FusedParams P) {
   wait_vmcnt<0>();                                // this wave's W^UV rows have landed
   lds_barrier();
 
-  // ---- o_c block = o_lat block (bf16) . W^UV_i^T
-  {
+  // ---- o_c block = o_lat block (bf16) . W^UV_i^T: waves 0-3, column block w, all four
+  // k quarters as independent chains, summed in quarter order as out_proj does
+  if (wave < kFColBlocks) {
     const char* a = o_lds + (lane & 15) * kFPitch + 16 * (lane >> 5);
     const int wr = 32 * cbk + (lane & 31);       // W^UV row of this lane's B operands
     const char* wrow = w_lds + wr * kFWRowBytes;
-    f32x16 accq[2];
+    f32x16 accq[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q = q0 + 2 * h;
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) accq[h][r] = 0.f;
+      for (int r = 0; r < 16; ++r) accq[q][r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < kFSteps; ++s) {
+    for (int s = 0; s < kFSteps; ++s)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
         const int c = 2 * (kFSteps * q + s) + (lane >> 5);
         const bf16x8 wb = *(const bf16x8*)(wrow + ((c ^ (wr & 15)) * 16));
-        accq[h] = mfma32x32x16(*(const bf16x8*)(a + 32 * (kFSteps * q + s)), wb, accq[h]);
+        accq[q] = mfma32x32x16(*(const bf16x8*)(a + 32 * (kFSteps * q + s)), wb, accq[q]);
       }
-    }
-    __syncthreads();                               // every wave has read W^UV: red reuses it
-#pragma unroll
-    for (int h = 0; h < 2; ++h) red[q0 + 2 * h][cbk][lane] = accq[h];
-  }
-  __syncthreads();
-  // wave w finishes column block (w & 3), registers 8 (w >> 2) .. +7: rows 16 (w >> 2)
-  // .. +15 of the D layout (lane l, reg r -> row 8 (r/4) + 4 (l/32) + r%4); only rows < 16
-  // are real, so waves 4-7 have nothing to store.
-  if (q0 == 0) {
+    // registers 0..7 hold rows 0..15 of the D layout (lane l, reg r -> row 8 (r/4) +
+    // 4 (l/32) + r%4); rows 16-31 repeat them
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
-      const float v = red[0][cbk][lane][rr] + red[1][cbk][lane][rr] + red[2][cbk][lane][rr] +
-                      red[3][cbk][lane][rr];
+      const float v = ((accq[0][rr] + accq[1][rr]) + accq[2][rr]) + accq[3][rr];
       const int mm = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
       if (mm < rows)
         P.o_c[((size_t)(mb + mm) * P.n_h + i) * P.d_h + 32 * cbk + (lane & 31)] = f32_to_bf16(v);

@@ -25,6 +25,7 @@ namespace {
 constexpr int kMergeThreads = 256;
 constexpr int kMergeWaves = kMergeThreads / 64;
 constexpr int kFastSplits = 8;
+static_assert(kFastSplits == 8, "the split-weight sum of the fast path is written out for 8 splits");
 
 template <typename PartT>
 __device__ __forceinline__ void load8(const PartT* p, float* v);
@@ -66,12 +67,20 @@ merge_splits_kernel(const PartT* __restrict__ o_part, const float* __restrict__ 
   if (num_splits <= kFastSplits && d_c == 8 * 64) {
     // One 512-wide stripe and at most 8 splits: every load (the lse values and all partial
     // rows) is issued before the first reduction, so the wave waits on one memory latency.
-    const float lse_l = lane < num_splits ? lse_part[(size_t)lane * qh_count + qh] : -INFINITY;
+    // Every lane holds all the split lse values (wave-uniform loads), so the maximum, the
+    // weights and their sum need no cross-lane exchange; the sum runs in the tree a
+    // butterfly over lanes 0..7 forms, ((w0 + w4) + (w2 + w6)) + ((w1 + w5) + (w3 + w7)),
+    // with zero weights for absent splits.
+    float lse_s[kFastSplits];
+#pragma unroll
+    for (int k = 0; k < kFastSplits; ++k) lse_s[k] = k < num_splits ? lse_part[(size_t)k * qh_count + qh] : -INFINITY;
     float v[kFastSplits][8];
 #pragma unroll
     for (int k = 0; k < kFastSplits; ++k)
       if (k < num_splits) load8(o_part + ((size_t)k * qh_count + qh) * d_c + 8 * lane, v[k]);
-    const float M = wave_max(lse_l);
+    float M = lse_s[0];
+#pragma unroll
+    for (int k = 1; k < kFastSplits; ++k) M = fmaxf(M, lse_s[k]);
     float* out = o_lat + (size_t)qh * d_c + 8 * lane;
     if (M == -INFINITY) {                         // no split saw a row
       *(f32x4*)out = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -79,13 +88,15 @@ merge_splits_kernel(const PartT* __restrict__ o_part, const float* __restrict__ 
       if (lane == 0) lse[qh] = -INFINITY;
       return;
     }
-    const float w_l = expf(lse_l - M);            // 0 for lanes past the last split
-    const float z = wave_sum(w_l);
+    float w[kFastSplits];
+#pragma unroll
+    for (int k = 0; k < kFastSplits; ++k) w[k] = k < num_splits ? expf(lse_s[k] - M) : 0.f;
+    const float z = ((w[0] + w[4]) + (w[2] + w[6])) + ((w[1] + w[5]) + (w[3] + w[7]));
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kFastSplits; ++k) {
       if (k < num_splits) {
-        const float ws = __shfl(w_l, k);
+        const float ws = w[k];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, v[k][e], acc[e]) : acc[e];
       }
