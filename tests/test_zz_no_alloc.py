@@ -78,6 +78,25 @@ def test_noalloc_matches_workspace_entry_point(torch):
                                _bits(base[torch.from_numpy(untouched).cuda()]))
 
 
+def test_noalloc_fp32_needs_no_array(torch):
+    """fp32 rows use no partial sums: the call takes no scratch and still equals mla_kv_append."""
+    w = W.make_config("tiny_f32")
+    d = B.dims(w.n_h, w.d_h, w.d_c, w.d_r, B.MLA_F32)
+    n, d_model = 6, 24
+    pos = np.arange(n, dtype=np.int64) * 5 + 3
+    dst = np.array([4, 0, 9, 2, 7, 5], dtype=np.int64)
+    p = W.draw_prologue(w, d_model, pos, dst, seed=5)
+    say(f"[kv_append_noalloc] fp32: n_new={n} d_model={d_model}")
+    args = [D._tensor(p.h, W.F32, "cuda"), D._tensor(p.w_dkv, W.F32, "cuda"), D._tensor(p.w_kr, W.F32, "cuda"),
+            torch.from_numpy(p.positions).cuda(), torch.from_numpy(p.dst_rows).cuda()]
+    base = torch.full((10, w.d_c + w.d_r), 2.0, dtype=torch.float32, device="cuda")
+    ref, got = base.clone(), base.clone()
+    B.kv_append(d, *args, ref)
+    B.kv_append_noalloc(d, *args, got)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+
+
 def test_noalloc_rejects_more_than_the_array_holds(torch):
     w = W.make_config("dsv2_small")
     d = B.dims(w.n_h, w.d_h, w.d_c, w.d_r, B.MLA_BF16)
