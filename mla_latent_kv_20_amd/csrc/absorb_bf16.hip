@@ -40,9 +40,12 @@ struct AbsorbParams {
   RopeSpec rope;
 };
 
+// kDhT: d_h fixed at compile time (the loops then have no runtime bounds), or 0 for any d_h.
+template <int kDhT>
 __global__ void __launch_bounds__(kThreads)
 absorb_q_bf16_kernel(AbsorbParams P) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int d_h = kDhT > 0 ? kDhT : P.d_h;
   // Workgroups are dealt round-robin over the 8 XCDs: workgroup L runs on XCD L % 8.  All
   // column blocks of head i go to XCD i % 8, so the head's queries are fetched into one
   // L2 once and shared by its blocks.
@@ -58,33 +61,39 @@ absorb_q_bf16_kernel(AbsorbParams P) {
   const int lane = tid & 63;
   const int d_qk = P.d_c + P.d_r;
 
-  char* ostage = smem + P.d_h * kAbsPitch;      // [32][kAbsOutPitch] output staging
-  const int qpitch = P.d_h * 2 + 16;              // q_c staging row: 16 rows of a 16-byte read on distinct banks
+  char* ostage = smem + d_h * kAbsPitch;          // [32][kAbsOutPitch] output staging
+  const int qpitch = d_h * 2 + 16;                // q_c staging row: 16 rows of a 16-byte read on distinct banks
   char* qstage = ostage + 32 * kAbsOutPitch;      // [32][qpitch] the first query block's q_c rows
 
   // The weight slice W^UK_i[:, cb:cb+128] goes out first (16-byte chunks, 16 per row), then
   // the first block's q_c rows (16-byte chunks, whole rows): the queries are shared by the
   // four waves, so one copy of them goes through LDS rather than each wave loading its A
   // operands itself (32 rows per instruction).
-  const bf16_bits* w = P.w_uk + (size_t)i * P.d_h * P.d_c + cb;
-  const int chunks = P.d_h * (kAbsCols / 8);     // <= 4096 (d_h <= 256)
-  const int ksteps = P.d_h / 16;                  // <= 16 (d_h <= 256)
-  const int qcpr = P.d_h / 8;                     // 16-byte chunks per q_c row
+  const bf16_bits* w = P.w_uk + (size_t)i * d_h * P.d_c + cb;
+  const int chunks = d_h * (kAbsCols / 8);        // <= 4096 (d_h <= 256)
+  const int ksteps = d_h / 16;                    // <= 16 (d_h <= 256)
+  const int qcpr = d_h / 8;                       // 16-byte chunks per q_c row
   const int qchunks = 32 * qcpr;                  // <= 1024
   for (int e0 = 0; e0 < chunks; e0 += 8 * kThreads) {
     bf16x8 v[8];
+    // Every load is unconditional (an index past the end re-reads the last chunk, which is
+    // not stored): a load under a branch leaves its register undefined on the other path,
+    // and the compiler then waits for it in the middle of issuing the rest.
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int e = e0 + u * kThreads + tid;
-      if (e < chunks) v[u] = *(const bf16x8*)(w + (size_t)(e >> 4) * P.d_c + (e & 15) * 8);
+      int e = e0 + u * kThreads + tid;
+      e = e < chunks ? e : chunks - 1;
+      v[u] = *(const bf16x8*)(w + (size_t)(e >> 4) * P.d_c + (e & 15) * 8);
     }
     bf16x8 qv[4];
     if (e0 == 0) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int e = u * kThreads + tid;
-        const int m = e / qcpr;
-        if (e < qchunks && m < P.n_q) qv[u] = *(const bf16x8*)(P.q_c + ((size_t)m * P.n_h + i) * P.d_h + (e % qcpr) * 8);
+        int e = u * kThreads + tid;
+        e = e < qchunks ? e : qchunks - 1;
+        int m = e / qcpr;
+        m = m < P.n_q ? m : P.n_q - 1;
+        qv[u] = *(const bf16x8*)(P.q_c + ((size_t)m * P.n_h + i) * d_h + (e % qcpr) * 8);
       }
     }
 #pragma unroll
@@ -134,7 +143,7 @@ absorb_q_bf16_kernel(AbsorbParams P) {
   for (int mb = 0; mb < P.n_q; mb += 32) {
     const int m = mb + (lane & 31);
     const bool mrow = m < P.n_q;
-    const bf16_bits* q = P.q_c + ((size_t)(mrow ? m : 0) * P.n_h + i) * P.d_h + 8 * (lane >> 5);
+    const bf16_bits* q = P.q_c + ((size_t)(mrow ? m : 0) * P.n_h + i) * d_h + 8 * (lane >> 5);
     if (mb > 0) {
 #pragma unroll
       for (int s = 0; s < 16; ++s)
@@ -580,12 +589,19 @@ hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, cons
   }
   AbsorbParams P{q_c, q_r, w_uk, q_abs, n_q, n_h, d_h, d_c, d_r, positions, rope};
   const size_t smem = (size_t)d_h * kAbsPitch + 32 * kAbsOutPitch + (size_t)32 * (d_h * 2 + 16);
-  static const hipError_t attr = hipFuncSetAttribute((const void*)absorb_q_bf16_kernel,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)absorb_q_bf16_kernel<0>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      (int)(256 * kAbsPitch + 32 * kAbsOutPitch + 32 * (256 * 2 + 16)));
   if (attr != hipSuccess) return attr;
+  static const hipError_t attr128 = hipFuncSetAttribute((const void*)absorb_q_bf16_kernel<128>,
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                        (int)(128 * kAbsPitch + 32 * kAbsOutPitch + 32 * (128 * 2 + 16)));
+  if (attr128 != hipSuccess) return attr128;
   const int grid = 8 * ((n_h + 7) / 8) * (d_c / kAbsCols);
-  hipLaunchKernelGGL(absorb_q_bf16_kernel, dim3(grid), dim3(kThreads), smem, stream, P);
+  if (d_h == 128)
+    hipLaunchKernelGGL(absorb_q_bf16_kernel<128>, dim3(grid), dim3(kThreads), smem, stream, P);
+  else
+    hipLaunchKernelGGL(absorb_q_bf16_kernel<0>, dim3(grid), dim3(kThreads), smem, stream, P);
   return hipGetLastError();
 }
 

@@ -113,6 +113,35 @@ def test_absorb_q(torch, name):
         assert np.array_equal(got[..., w.d_c:], ref[..., w.d_c:])
 
 
+@pytest.mark.parametrize("d_h,d_c,n_q", [(48, 128, 5), (64, 256, 40), (256, 128, 33)])
+def test_absorb_q_other_head_dims(torch, d_h, d_c, n_q):
+    """bf16 absorb_q at head dimensions other than 128 (the kernel's general form): a weight
+    slice that does not fill the last load round (d_h = 48), two 32-row query blocks, a
+    head count that is not a multiple of 8; with and without RoPE positions."""
+    n_h, d_r = 12, 16
+    rng = np.random.default_rng(d_h + n_q)
+    bf = lambda a: W.round_to_storage(a, W.BF16)
+    q_c, q_r = bf(rng.standard_normal((n_q, n_h, d_h))), bf(rng.standard_normal((n_q, n_h, d_r)))
+    w_uk = bf(rng.standard_normal((n_h, d_h, d_c)) / np.sqrt(d_h))
+    pos = rng.integers(0, 163840, size=n_q).astype(np.int64)
+    d = B.dims(n_h, d_h, d_c, d_r, B.MLA_BF16)
+    dev = lambda a: D._tensor(a, W.BF16, "cuda")
+    say(f"[absorb_q] d_h={d_h} d_c={d_c} n_q={n_q} n_h={n_h}")
+    qa = B.absorb_q(d, dev(q_c), dev(q_r), dev(w_uk))
+    qa_r = B.absorb_q_rope(d, dev(q_c), dev(q_r), dev(w_uk), torch.from_numpy(pos).cuda())
+    torch.cuda.synchronize()
+    f = lambda a: W.to_f64(a, W.BF16)
+    for what, got, ref in [("q_abs", qa, O.absorb_q(f(q_c), f(q_r), f(w_uk))),
+                           ("q_abs with positions", qa_r, O.absorb_q_rope(f(q_c), f(q_r), f(w_uk), pos))]:
+        got = D.to_numpy_f64(got)
+        lim = 2.0 ** -8 * np.abs(ref[..., :d_c]) + 1e-4 * np.std(ref[..., :d_c])   # one rounding of an fp32 sum
+        assert np.all(np.abs(got[..., :d_c] - ref[..., :d_c]) <= lim), what
+        if what == "q_abs":
+            assert np.array_equal(got[..., d_c:], ref[..., d_c:])
+        else:                              # the rotation's one bf16 rounding
+            assert np.all(np.abs(got[..., d_c:] - ref[..., d_c:]) <= 2.0 ** -8 * np.abs(ref[..., d_c:]) + 1e-6), what
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_decode(torch, name):
     w = workload(name)
