@@ -569,10 +569,13 @@ bool out_proj_bf16_supported(int d_h, int d_c) {
 hipError_t launch_absorb_q_bf16(const bf16_bits* q_c, const bf16_bits* q_r, const bf16_bits* w_uk,
                                 bf16_bits* q_abs, int n_q, int n_h, int d_h, int d_c, int d_r,
                                 const int64_t* positions, const RopeSpec& rope, hipStream_t stream) {
-  if (n_q >= 64 && d_h == kArDh && d_c == kArDc && d_r == kArDr) {
-    // many rows: runs of up to 512 rows (whole 32-row blocks), at least 2 per head.  From 64
-    // rows this form is the faster one (11.3 against 11.8 us at 64 rows, 12.3 against 14.7
-    // with positions); at 32 rows the (head, 128 columns) workgroups are (8.2 against 10.6).
+  // Many rows: runs of up to 512 rows (whole 32-row blocks), at least 2 per head.  Measured
+  // against the (head, 128 columns) workgroups with 128 heads: without positions from 128
+  // rows (15.2 against 15.4 us; 11.4 against 9.9 at 64, 14.6 against 12.8 at 96), with
+  // positions from 64 (12.3 against 13.1 us), where the column form's per-head RoPE loop is
+  // the slower part.
+  const int rows_from = positions ? 64 : 128;
+  if (n_q >= rows_from && d_h == kArDh && d_c == kArDc && d_r == kArDr) {
     AbsorbRowsParams R{q_c, q_r, w_uk, q_abs, n_q, n_h, 0, 0, positions, rope};
     R.chunks = (n_q + 511) / 512;
     if (R.chunks < 2) R.chunks = 2;

@@ -200,7 +200,7 @@ def test_merge_all_empty_and_odd_width(torch):
     assert_close("lse", got_l[keep][None], rl, w32, lse=True)
 
 
-@pytest.mark.parametrize("n_q", [64, 100, 300, 700])
+@pytest.mark.parametrize("n_q", [64, 100, 128, 300, 700])
 def test_absorb_and_out_proj_many_rows(torch, n_q):
     """Many query rows (a prefill's worth, the many-row kernels): runs of whole 32-row blocks,
     the last one ragged; every row against the oracle, with and without RoPE positions, and
