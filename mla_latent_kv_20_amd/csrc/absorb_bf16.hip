@@ -407,6 +407,9 @@ struct OutProjParams {
 
 constexpr int kOutMaxSteps = 8;    // k-steps of 16 per wave: d_c <= 4 * 8 * 16 = 512
 
+// kStepsT: the k-steps per wave (d_c / 64) fixed at compile time, so that every load is
+// unconditional and all of them issue before the first wait, or 0 for any d_c.
+template <int kStepsT>
 __global__ void __launch_bounds__(kThreads)
 out_proj_bf16_kernel(OutProjParams P) {
   __shared__ f32x16 red[kWaves][64];
@@ -422,7 +425,7 @@ out_proj_bf16_kernel(OutProjParams P) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int steps = P.d_c / 64;                   // k-steps of this wave
+  const int steps = kStepsT > 0 ? kStepsT : P.d_c / 64;   // k-steps of this wave
   const int k0 = wave * steps * 16 + 8 * (lane >> 5);
 
   // B operands: lane l holds W^UV_i[nb + l%32][k0 + 16s .. +7]
@@ -624,7 +627,10 @@ hipError_t launch_out_proj_bf16(const float* o_lat, const bf16_bits* w_uv, bf16_
   }
   OutProjParams P{o_lat, w_uv, o_c, n_q, n_h, d_h, d_c};
   const int grid = 8 * ((n_h + 7) / 8) * (d_h / 32);
-  hipLaunchKernelGGL(out_proj_bf16_kernel, dim3(grid), dim3(kThreads), 0, stream, P);
+  if (d_c == 64 * kOutMaxSteps)
+    hipLaunchKernelGGL(out_proj_bf16_kernel<kOutMaxSteps>, dim3(grid), dim3(kThreads), 0, stream, P);
+  else
+    hipLaunchKernelGGL(out_proj_bf16_kernel<0>, dim3(grid), dim3(kThreads), 0, stream, P);
   return hipGetLastError();
 }
 

@@ -71,40 +71,52 @@ merge_splits_kernel(const PartT* __restrict__ o_part, const float* __restrict__ 
     // weights and their sum need no cross-lane exchange; the sum runs in the tree a
     // butterfly over lanes 0..7 forms, ((w0 + w4) + (w2 + w6)) + ((w1 + w5) + (w3 + w7)),
     // with zero weights for absent splits.
+    // The loads are unconditional (a split past the last re-reads the last one; its weight
+    // is zero) and the rows stay raw 16-byte vectors until they are used: a load under a
+    // branch, or converted where it is issued, would make the wave wait for it before
+    // issuing the next.
+    constexpr int kVec = 16 / (int)sizeof(PartT);        // elements per 16-byte load
+    typedef PartT pvec __attribute__((ext_vector_type(kVec)));
     float lse_s[kFastSplits];
+    pvec raw[kFastSplits][8 / kVec];
 #pragma unroll
-    for (int k = 0; k < kFastSplits; ++k) lse_s[k] = k < num_splits ? lse_part[(size_t)k * qh_count + qh] : -INFINITY;
-    float v[kFastSplits][8];
+    for (int k = 0; k < kFastSplits; ++k) {
+      const int kk = k < num_splits ? k : num_splits - 1;
+      lse_s[k] = lse_part[(size_t)kk * qh_count + qh];
+#pragma unroll
+      for (int h = 0; h < 8 / kVec; ++h)
+        raw[k][h] = *(const pvec*)(o_part + ((size_t)kk * qh_count + qh) * d_c + 8 * lane + kVec * h);
+    }
 #pragma unroll
     for (int k = 0; k < kFastSplits; ++k)
-      if (k < num_splits) load8(o_part + ((size_t)k * qh_count + qh) * d_c + 8 * lane, v[k]);
+      if (k >= num_splits) lse_s[k] = -INFINITY;
     float M = lse_s[0];
 #pragma unroll
     for (int k = 1; k < kFastSplits; ++k) M = fmaxf(M, lse_s[k]);
-    float* out = o_lat + (size_t)qh * d_c + 8 * lane;
-    if (M == -INFINITY) {                         // no split saw a row
-      *(f32x4*)out = f32x4{0.f, 0.f, 0.f, 0.f};
-      *(f32x4*)(out + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (lane == 0) lse[qh] = -INFINITY;
-      return;
-    }
+    // No branch between the loads and their use (the compiler would otherwise sink the
+    // loads below it): a row that no split saw (M = -inf) gets zero weights and, at the end,
+    // zero outputs and lse = -inf.
+    const bool none = M == -INFINITY;
+    const float m_ref = none ? 0.f : M;
     float w[kFastSplits];
 #pragma unroll
-    for (int k = 0; k < kFastSplits; ++k) w[k] = k < num_splits ? expf(lse_s[k] - M) : 0.f;
+    for (int k = 0; k < kFastSplits; ++k) w[k] = k < num_splits ? expf(lse_s[k] - m_ref) : 0.f;
     const float z = ((w[0] + w[4]) + (w[2] + w[6])) + ((w[1] + w[5]) + (w[3] + w[7]));
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kFastSplits; ++k) {
-      if (k < num_splits) {
-        const float ws = w[k];
+      const float ws = w[k];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, v[k][e], acc[e]) : acc[e];
-      }
+      for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, (float)raw[k][e / kVec][e % kVec], acc[e]) : acc[e];
     }
     const float inv_z = 1.0f / z;
-    *(f32x4*)out = f32x4{acc[0] * inv_z, acc[1] * inv_z, acc[2] * inv_z, acc[3] * inv_z};
-    *(f32x4*)(out + 4) = f32x4{acc[4] * inv_z, acc[5] * inv_z, acc[6] * inv_z, acc[7] * inv_z};
-    if (lane == 0) lse[qh] = M + logf(z);
+    float* out = o_lat + (size_t)qh * d_c + 8 * lane;
+    float r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = none ? 0.f : acc[e] * inv_z;
+    *(f32x4*)out = f32x4{r[0], r[1], r[2], r[3]};
+    *(f32x4*)(out + 4) = f32x4{r[4], r[5], r[6], r[7]};
+    if (lane == 0) lse[qh] = none ? -INFINITY : M + logf(z);
     return;
   }
   // Up to 64 splits: lane s holds split s's lse (one load).  Splits of weight zero (empty
