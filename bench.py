@@ -39,6 +39,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 ROW_BYTES = 1152               # one cached latent row [c_KV 512 ; k_R 64] in bf16
 FLOP_PER_ROW_HEAD = 2 * 576 + 2 * 512   # score + weighted sum, per (row, query head)
 MALL_BYTES = 256 << 20
+LAUNCHES_PER_GRAPH = 8          # per-kernel timing: launches captured per replayed graph
 D_MODEL = 5120                 # DeepSeek-V2 hidden width: input of the decode prologue
 D_CQ = 1536                    # DeepSeek-V2 compressed query width (W^UQ's input)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
@@ -427,19 +428,22 @@ def main():
         for j in range(n):
             fn(j)
         torch.cuda.synchronize()
-        reps = max(1, K // n)
+        # At least LAUNCHES_PER_GRAPH launches per replay (each copy equally often): the gap
+        # between two replays is then shared by that many launches.
+        m = n * max(1, math.ceil(LAUNCHES_PER_GRAPH / n))
+        reps = max(1, K // m)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         if args.no_graph:                  # eager launches (counter runs): host cost may show
             e0.record()
             for _ in range(reps):
-                for j in range(n):
-                    fn(j)
+                for j in range(m):
+                    fn(j % n)
             e1.record()
         else:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for j in range(n):
-                    fn(j)
+                for j in range(m):
+                    fn(j % n)
             g.replay()
             torch.cuda.synchronize()
             e0.record()
@@ -447,7 +451,7 @@ def main():
                 g.replay()
             e1.record()
         torch.cuda.synchronize()
-        per[name] = e0.elapsed_time(e1) / (reps * n)
+        per[name] = e0.elapsed_time(e1) / (reps * m)
 
     # Spread of the step time: a separate pass of replays of the all-layers graph, one event
     # between replays (the headline above is timed without them).

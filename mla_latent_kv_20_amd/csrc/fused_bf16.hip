@@ -181,50 +181,58 @@ __device__ __forceinline__ void merge_rows_fast(const PartT* o_part, const float
   // the weights and their sum need no cross-lane exchange.  The sum runs in the tree a
   // butterfly over lanes 0..7 would form, ((w0 + w4) + (w2 + w6)) + ((w1 + w5) + (w3 + w7)),
   // with zero weights for absent splits.
+  // Every load is unconditional: a split past the last re-reads the last one (its weight is
+  // zero), a row past the block's end reads a valid row (qh) and is not used.  A load under
+  // a branch would leave its register undefined on the other path, and the compiler would
+  // wait for it in the middle of issuing the rest.
   float lse[kRows][kFFast];
   pvec raw[kRows][kFFast][8 / kVec];
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
-    const bool live = r < nrows;
 #pragma unroll
-    for (int k = 0; k < kFFast; ++k)
-      lse[r][k] = live && k < num_splits ? lse_part[(size_t)k * qh_count + qh[r]] : -INFINITY;
+    for (int k = 0; k < kFFast; ++k) {
+      const int kk = k < num_splits ? k : num_splits - 1;
+      lse[r][k] = lse_part[(size_t)kk * qh_count + qh[r]];
+    }
 #pragma unroll
-    for (int k = 0; k < kFFast; ++k)
-      if (live && k < num_splits)
+    for (int k = 0; k < kFFast; ++k) {
+      const int kk = k < num_splits ? k : num_splits - 1;
 #pragma unroll
-        for (int h = 0; h < 8 / kVec; ++h)
-          raw[r][k][h] = *(const pvec*)(o_part + ((size_t)k * qh_count + qh[r]) * kFDc + 8 * lane + kVec * h);
+      for (int h = 0; h < 8 / kVec; ++h)
+        raw[r][k][h] = *(const pvec*)(o_part + ((size_t)kk * qh_count + qh[r]) * kFDc + 8 * lane + kVec * h);
+    }
   }
 #pragma unroll
+  for (int r = 0; r < kRows; ++r)
+#pragma unroll
+    for (int k = 0; k < kFFast; ++k)
+      if (!(r < nrows && k < num_splits)) lse[r][k] = -INFINITY;
+#pragma unroll
   for (int r = 0; r < kRows; ++r) {
-    if (r >= nrows) break;
     float m = lse[r][0];
 #pragma unroll
     for (int k = 1; k < kFFast; ++k) m = fmaxf(m, lse[r][k]);
     M[r] = m;
-    if (m == -INFINITY) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
-      z[r] = 0.f;
-      continue;
-    }
+    // No branch between the loads and their use (the compiler would sink the loads below
+    // it): a row that no split saw, or one past the block's end, gets zero weights and zero
+    // outputs.
+    const bool none = m == -INFINITY;
+    const float m_ref = none ? 0.f : m;
     float w[kFFast];
 #pragma unroll
-    for (int k = 0; k < kFFast; ++k) w[k] = k < num_splits ? expf(lse[r][k] - m) : 0.f;
-    z[r] = ((w[0] + w[4]) + (w[2] + w[6])) + ((w[1] + w[5]) + (w[3] + w[7]));
+    for (int k = 0; k < kFFast; ++k) w[k] = k < num_splits ? expf(lse[r][k] - m_ref) : 0.f;
+    const float zz = ((w[0] + w[4]) + (w[2] + w[6])) + ((w[1] + w[5]) + (w[3] + w[7]));
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kFFast; ++k) {
-      if (k < num_splits) {
-        const float ws = w[k];
+      const float ws = w[k];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, (float)raw[r][k][e / kVec][e % kVec], acc[e]) : acc[e];
-      }
+      for (int e = 0; e < 8; ++e) acc[e] = ws != 0.f ? fmaf(ws, (float)raw[r][k][e / kVec][e % kVec], acc[e]) : acc[e];
     }
-    const float inv_z = 1.0f / z[r];
+    const float inv_z = 1.0f / zz;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[r][e] = acc[e] * inv_z;
+    for (int e = 0; e < 8; ++e) o[r][e] = none ? 0.f : acc[e] * inv_z;
+    z[r] = none ? 0.f : zz;
   }
 }
 
