@@ -41,7 +41,9 @@ struct AppendParams {
   RopeSpec rope;
 };
 
-// Kernel 1: partial products of one (column block, token block, K slice).
+// Kernel 1: partial products of one (column block, token block, K slice).  kStepsT: the
+// k-steps per wave fixed at compile time (every load unconditional), or 0 for any d_model.
+template <int kStepsT>
 __global__ void __launch_bounds__(kAppThreads)
 kv_append_partial_kernel(AppendParams P) {
   __shared__ f32x16 red[kAppWaves][64];
@@ -60,7 +62,7 @@ kv_append_partial_kernel(AppendParams P) {
   const int col = 32 * cb + (lane & 31);          // output column of this lane's W row
   const bf16_bits* wrow = col < P.d_c ? (const bf16_bits*)P.w_dkv + (size_t)col * P.d_model
                                       : (const bf16_bits*)P.w_kr + (size_t)(col - P.d_c) * P.d_model;
-  const int steps = P.d_model / (16 * kSplitK * kAppWaves);   // k-steps per wave
+  const int steps = kStepsT > 0 ? kStepsT : P.d_model / (16 * kSplitK * kAppWaves);   // k-steps per wave
   const int k0 = (ks * kAppWaves + wave) * steps * 16 + 8 * (lane >> 5);
   const bf16_bits* hp = (const bf16_bits*)P.h + (size_t)tok_ld * P.d_model + k0;
   const bf16_bits* wp = wrow + k0;
@@ -107,20 +109,31 @@ __global__ void kv_append_finish_kernel(AppendParams P) {
     const int c = (int)(e % per_tok);
     const float* src = P.ws + (size_t)t * width;
     const size_t slice = (size_t)P.n_new * width;
-    bf16_bits* dst = (bf16_bits*)P.rows + P.dst[t] * P.stride;
-    if (c < P.d_c) {
-      float v = 0.f;
-      for (int s = 0; s < kSplitK; ++s) v += src[s * slice + c];
-      dst[c] = f32_to_bf16(v);
+    // Every load of the element (its slices' partial sums, the row index, the position) is
+    // issued before the first is used, and the slices are added in slice order.
+    const bool lat = c < P.d_c;
+    const int k = lat ? 0 : c - P.d_c;
+    const int cx = lat ? c : P.d_c + k;
+    float vx[kSplitK], vy[kSplitK];
+#pragma unroll
+    for (int s = 0; s < kSplitK; ++s) {
+      vx[s] = src[s * slice + cx];
+      vy[s] = src[s * slice + (lat ? cx : cx + half)];
+    }
+    const int64_t row = P.dst[t];
+    const int64_t pos = P.pos[t];
+    bf16_bits* dst = (bf16_bits*)P.rows + row * P.stride;
+    float x = 0.f, y = 0.f;
+#pragma unroll
+    for (int s = 0; s < kSplitK; ++s) {
+      x += vx[s];
+      y += vy[s];
+    }
+    if (lat) {
+      dst[c] = f32_to_bf16(x);
     } else {
-      const int k = c - P.d_c;
-      float x = 0.f, y = 0.f;
-      for (int s = 0; s < kSplitK; ++s) {
-        x += src[s * slice + P.d_c + k];
-        y += src[s * slice + P.d_c + k + half];
-      }
       double dx = x, dy = y;
-      rope_pair(dx, dy, P.pos[t], k, P.d_r, P.rope);
+      rope_pair(dx, dy, pos, k, P.d_r, P.rope);
       dst[P.d_c + k] = f32_to_bf16((float)dx);
       dst[P.d_c + k + half] = f32_to_bf16((float)dy);
     }
@@ -179,7 +192,11 @@ hipError_t launch_kv_append(bool bf16, const void* h, const void* w_dkv, const v
                             hipStream_t stream) {
   AppendParams P{h, w_dkv, w_kr, positions, dst_rows, rows, workspace, stride, n_new, d_model, d_c, d_r, rope};
   if (bf16) {
-    hipLaunchKernelGGL(kv_append_partial_kernel, dim3((d_c + d_r) / 32 * ((n_new + 31) / 32) * kSplitK),
+    if (d_model == 16 * kSplitK * kAppWaves * 10)
+      hipLaunchKernelGGL(kv_append_partial_kernel<10>, dim3((d_c + d_r) / 32 * ((n_new + 31) / 32) * kSplitK),
+                       dim3(kAppThreads), 0, stream, P);
+    else
+      hipLaunchKernelGGL(kv_append_partial_kernel<0>, dim3((d_c + d_r) / 32 * ((n_new + 31) / 32) * kSplitK),
                        dim3(kAppThreads), 0, stream, P);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
