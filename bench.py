@@ -6,7 +6,9 @@ A step is one pass of the whole path -- absorb_q, decode, then the split merge a
 projection (one fused call by default; --unfused runs merge_splits and out_proj) -- over one batch of a seeded synthetic DeepSeek-V2-shaped latent cache.  The cache and the
 two weight matrices are held in several device copies ("layers") used round-robin, so a
 step's inputs come from HBM rather than from the 256 MB on-chip Infinity Cache, as when
-consecutive layers of a model run.  Inputs are resident on the device before timing.
+consecutive layers of a model run.  One replayed HIP graph holds 60 steps, one per layer of
+the 60-layer model, as a serving loop captures a whole decode step.  Inputs are resident on
+the device before timing.
 
 Prints one JSON line: throughput in cached latent tokens per second over the whole step,
 the decode kernel's roofline fraction (HIP-event timing inside the timed region), and the
@@ -39,7 +41,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 ROW_BYTES = 1152               # one cached latent row [c_KV 512 ; k_R 64] in bf16
 FLOP_PER_ROW_HEAD = 2 * 576 + 2 * 512   # score + weighted sum, per (row, query head)
 MALL_BYTES = 256 << 20
-LAUNCHES_PER_GRAPH = 8          # per-kernel timing: launches captured per replayed graph
+MODEL_LAYERS = 60              # DeepSeek-V2's layers: the steps (or launches) one replayed graph holds
 D_MODEL = 5120                 # DeepSeek-V2 hidden width: input of the decode prologue
 D_CQ = 1536                    # DeepSeek-V2 compressed query width (W^UQ's input)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
@@ -280,9 +282,11 @@ def main():
     torch.cuda.synchronize()
     K = args.steps
 
-    # Whole-step throughput: the steps of all layer copies are captured once as one HIP
-    # graph (one step per layer, as a serving loop captures a model's layers) and replayed;
-    # a second graph holds the K % copies remaining steps, so exactly K steps are timed.
+    # Whole-step throughput: one HIP graph holds MODEL_LAYERS steps, one per layer of the
+    # model (a serving loop captures a model's layers), cycling over the layer copies, and is
+    # replayed; a second graph holds the K % n_graph remaining steps, so exactly K steps are
+    # timed.
+    n_graph = copies * max(1, math.ceil(MODEL_LAYERS / copies))
     if not args.no_graph:
         def capture(n):
             g = torch.cuda.CUDAGraph()
@@ -290,15 +294,15 @@ def main():
                 for c in range(n):
                     step(c)
             return g
-        g_all = capture(copies)
-        g_rest = capture(K % copies) if K % copies else None
-        for i in range(max(1, args.warmup // copies)):
+        g_all = capture(n_graph)
+        g_rest = capture(K % n_graph) if K % n_graph else None
+        for i in range(max(1, args.warmup // n_graph)):
             g_all.replay()
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         g0.record()
-        for i in range(K // copies):
+        for i in range(K // n_graph):
             g_all.replay()
         if g_rest is not None:
             g_rest.replay()
@@ -428,9 +432,9 @@ def main():
         for j in range(n):
             fn(j)
         torch.cuda.synchronize()
-        # At least LAUNCHES_PER_GRAPH launches per replay (each copy equally often): the gap
-        # between two replays is then shared by that many launches.
-        m = n * max(1, math.ceil(LAUNCHES_PER_GRAPH / n))
+        # At least MODEL_LAYERS launches per replay (each copy equally often): the gap between
+        # two replays is then shared by that many launches, as in the whole-step graph.
+        m = n * max(1, math.ceil(MODEL_LAYERS / n))
         reps = max(1, K // m)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         if args.no_graph:                  # eager launches (counter runs): host cost may show
@@ -457,16 +461,16 @@ def main():
     # between replays (the headline above is timed without them).
     spread = None
     if not args.no_graph:
-        n_rep = max(5, min(50, K // copies))
+        n_rep = max(5, min(50, K // n_graph))
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
         evs[0].record()
         for r in range(n_rep):
             g_all.replay()
             evs[r + 1].record()
         torch.cuda.synchronize()
-        st = sorted(evs[r].elapsed_time(evs[r + 1]) * 1e3 / copies for r in range(n_rep))
+        st = sorted(evs[r].elapsed_time(evs[r + 1]) * 1e3 / n_graph for r in range(n_rep))
         pick = lambda q: round(st[min(n_rep - 1, int(round(q * (n_rep - 1))))], 2)
-        spread = {"replays": n_rep, "steps_per_replay": copies, "p10_us": pick(0.1), "median_us": pick(0.5),
+        spread = {"replays": n_rep, "steps_per_replay": n_graph, "p10_us": pick(0.1), "median_us": pick(0.5),
                   "p90_us": pick(0.9)}
 
     # The decode with its cache resident in the Infinity Cache: every launch reads the first
@@ -534,7 +538,8 @@ def main():
         "fp8_cache": (fp8_summary(w, per, flops, tokens, fcopies) if fp8 else None),
         "folding": (fold_summary(w, per, esz) if fold else None),
         "decode_merge_tokens_per_s": round(tokens / ((dec_ms + per.get("merge", 0.0)) * 1e-3), 1),
-        "timing": "hip graph replay (one graph per pass over the layer copies)" if not args.no_graph else "eager launches",
+        "timing": (f"hip graph replay ({n_graph} steps per graph, one per model layer, cycling over {copies} layer copies)"
+                   if not args.no_graph else "eager launches"),
         "step_calls": ("absorb_q, decode, out_proj (one fp32 split: no merge)" if S == 1 and part == B.MLA_F32
                        else "absorb_q, decode, merge_out_proj" if fused else "absorb_q, decode, merge_splits, out_proj"),
         "mfma_frac_decode": round(flops / (dec_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
