@@ -72,9 +72,9 @@ merge_splits_kernel(const PartT* __restrict__ o_part, const float* __restrict__ 
     // butterfly over lanes 0..7 forms, ((w0 + w4) + (w2 + w6)) + ((w1 + w5) + (w3 + w7)),
     // with zero weights for absent splits.
     // The loads are unconditional (a split past the last re-reads the last one; its weight
-    // is zero) and the rows stay raw 16-byte vectors until they are used: a load under a
-    // branch, or converted where it is issued, would make the wave wait for it before
-    // issuing the next.
+    // is zero): a load under a branch leaves its register undefined on the other path, and
+    // the compiler then waits for it before issuing the next.  The rows stay raw 16-byte
+    // vectors until they are used (measured faster here than converting each on arrival).
     constexpr int kVec = 16 / (int)sizeof(PartT);        // elements per 16-byte load
     typedef PartT pvec __attribute__((ext_vector_type(kVec)));
     float lse_s[kFastSplits];
