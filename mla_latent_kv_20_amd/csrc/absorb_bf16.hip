@@ -179,37 +179,44 @@ absorb_q_bf16_kernel(AbsorbParams P) {
     }
   }
 
-  // RoPE part: copied once per head, by the first column block, 16 bytes per thread with
-  // every load of a thread in flight before its stores.  It comes last, so that its
-  // memory latency does not delay the weight loads above.  With token positions the pairs
-  // (k, k + d_r/2) are rotated on the way ([notes] "MLA 코드 구현": q^R is rotated head by
-  // head at the new tokens' positions).
-  if (cbi == 0 && P.pos == nullptr) {
+  // RoPE part, 16 bytes per thread with every load of a thread in flight before its stores.
+  // It comes last, so that its memory latency does not delay the weight loads above.  With
+  // token positions the pairs (k, k + d_r/2) are rotated on the way ([notes] "MLA 코드 구현":
+  // q^R is rotated head by head at the new tokens' positions), and the head's query rows are
+  // shared out over its nblk column blocks (block cbi takes rows cbi, cbi + nblk, ...); so
+  // they are for a copy of more than one 16-byte chunk per thread.  A shorter copy is the
+  // first block's alone.
+  const bool spread = P.pos != nullptr || P.n_q * (P.d_r / 8) > kThreads;
+  const int rfirst = spread ? cbi : 0;            // this block's rows: rfirst + rstep * r
+  const int rstep = spread ? nblk : 1;
+  const int rrows = spread ? (P.n_q > cbi ? (P.n_q - cbi + nblk - 1) / nblk : 0) : (cbi == 0 ? P.n_q : 0);
+  if (P.pos == nullptr) {
     const int cpr = P.d_r / 8;                    // 16-byte chunks per query row (d_r % 8 == 0)
-    const int total = P.n_q * cpr;
+    const int total = rrows * cpr;
     for (int e0 = 0; e0 < total; e0 += 4 * kThreads) {
       bf16x8 v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int e = e0 + u * kThreads + tid;
         if (e < total)
-          v[u] = *(const bf16x8*)(P.q_r + ((size_t)(e / cpr) * P.n_h + i) * P.d_r + (e % cpr) * 8);
+          v[u] = *(const bf16x8*)(P.q_r + ((size_t)(rfirst + rstep * (e / cpr)) * P.n_h + i) * P.d_r + (e % cpr) * 8);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int e = e0 + u * kThreads + tid;
         if (e < total)
-          *(bf16x8*)(P.q_abs + ((size_t)(e / cpr) * P.n_h + i) * d_qk + P.d_c + (e % cpr) * 8) = v[u];
+          *(bf16x8*)(P.q_abs + ((size_t)(rfirst + rstep * (e / cpr)) * P.n_h + i) * d_qk + P.d_c + (e % cpr) * 8) = v[u];
       }
     }
-  } else if (cbi == 0) {
-    // thread (k, query slot): one inverse frequency per thread, the queries strided
+  } else {
+    // thread (k, query slot): one inverse frequency per thread, the block's rows strided
     const int half = P.d_r / 2;
     const int slots = kThreads / half;            // query slots per pair index (d_r <= 512)
     if (tid < half * slots) {
       const int k = tid % half;
       const double inv = rope_inv_freq(k, P.d_r, P.rope);
-      for (int n = tid / half; n < P.n_q; n += slots) {
+      for (int rr = tid / half; rr < rrows; rr += slots) {
+        const int n = rfirst + rstep * rr;
         const bf16_bits* src = P.q_r + ((size_t)n * P.n_h + i) * P.d_r;
         double x = bf16_to_f32(src[k]);
         double y = bf16_to_f32(src[k + half]);
