@@ -210,6 +210,28 @@ def test_decode_fp8_sixteen_or_more_sequences(torch, lengths):
     check("lse_part", D.to_numpy_f64(lp), rl, lse=True)
 
 
+@pytest.mark.parametrize("equal", [False, True])
+def test_decode_fp8_more_sequences_than_threads(torch, equal):
+    """300 sequences, more than the workgroup's 256 threads: every loop of the length ranking
+    takes several passes; ragged lengths of 1..40 rows (several splits empty) or all equal."""
+    rng = np.random.default_rng(23)
+    lengths = [17] * 300 if equal else [int(x) for x in rng.integers(1, 41, size=300)]
+    w = W.make_workload("many8", **W.DSV2, dtype=W.BF16, lengths=lengths, seed=12)
+    say(f"[decode_fp8] 300 sequences, {'equal' if equal else 'ragged'} lengths, 3 x 16")
+    codes, scales, deq = quantize_on_gpu(torch, w, D.packed_rows(w))
+    qa = W.draw_q_abs(w)
+    op, lp = B.decode_fp8(dims_of(w), D._tensor(qa, W.BF16, "cuda"), codes, scales,
+                          torch.from_numpy(w.offsets.astype(np.int64)).cuda(), w.batch, 1, 3, 16,
+                          partial_dtype=B.MLA_F16)
+    torch.cuda.synchronize()
+    ro, rl = O.split_partials(W.to_f64(qa, W.BF16), deq[:, :512], deq[:, 512:], w.offsets, 1, 3, 16,
+                              O.default_scale(w.d_h, w.d_r))
+    live = ~np.isneginf(rl)
+    assert not live.all()
+    check("o_part", D.to_numpy_f64(op)[live], ro[live])
+    check("lse_part", D.to_numpy_f64(lp), rl, lse=True)
+
+
 def fp8_step(torch, w, codes, scales, S, R):
     """absorb_q, decode_fp8, merge_out_proj through the ABI; returns o_c, lse, o_lat."""
     d = dims_of(w)
