@@ -24,8 +24,9 @@
 // without rounding (v_cvt_scalef32_pk_bf16_fp8, scale 1); s_r is folded into p before p's
 // one rounding to bf16.
 //
-// Work item, waves, two-stage direct-to-LDS tile ring, softmax and epilogue are those of
-// the bf16 decode.  What differs:
+// Work item, waves, softmax and epilogue are those of the bf16 decode.  What differs:
+//  * the direct-to-LDS tile ring has two stages and the scores and weighted sum of a tile
+//    run in sequence (the bf16 decode interleaves them over a third stage);
 //  * a 32-row tile is 18 KiB: 18 loads of 1 KiB, five per wave (waves 2 and 3 load four
 //    and the tile's 32 row scales, with a 4-byte direct-to-LDS load);
 //  * K operands: two 16-byte LDS reads per lane give one 64-code k-step;
