@@ -190,10 +190,11 @@ mla_decode_bf16_kernel(DecodeParams P) {
   //    length (longest first, ties by index) and XCD x takes ranks x, 15-x, 16+x, 31-x, ...
   //    (snake order), longest first.  Every XCD then gets the same number of sequences
   //    and nearly the same number of tiles, however ragged the lengths.  When every length
-  //    is equal the ranks are the indices and the ranking is skipped.  Only non-empty
-  //    splits are enumerated (the split-0 workgroup marks the empty ones): the dispatcher
-  //    deals an XCD's workgroups to its shader engines in a fixed rotation, so empty
-  //    workgroups interleaved with real ones would load the engines unevenly.
+  //    is equal the ranks are the indices and the ranking is skipped; otherwise an XCD's
+  //    items go longest first.  Only non-empty splits are enumerated (the split-0
+  //    workgroup marks the empty ones): the dispatcher deals an XCD's workgroups to its
+  //    shader engines in a fixed rotation, so empty workgroups interleaved with real ones
+  //    would load the engines unevenly.
   const int L = blockIdx.x;
   const int xcd = L & 7;
   const int k = L >> 3;
@@ -265,7 +266,40 @@ mla_decode_bf16_kernel(DecodeParams P) {
         row0_l = offs[p];
         len_l = len0;
       }
+    } else if (P.seqs_per_xcd <= 64) {
+      // Longest first: every split of split_rows rows (all but each sequence's last) in
+      // rank order, then the last splits, longest first (ties in rank order).  A CU that
+      // frees up late then takes a short item.  Lane m of every wave holds this XCD's
+      // sequence m; the chosen item's values are read from its lane.
+      const int m = (int)(threadIdx.x & 63);
+      const int pm = 8 * m + ((m & 1) ? 7 - xcd : xcd);
+      const bool valid = m < P.seqs_per_xcd && pm < P.batch;
+      const int bm = valid ? by_rank[pm] : 0;
+      const int len = valid ? lens[bm] : 0;
+      int ns = P.split_rows > 0 ? (len + P.split_rows - 1) / P.split_rows : P.num_splits;
+      ns = ns < 1 ? 1 : (ns > P.num_splits ? P.num_splits : ns);
+      const int nfull = valid ? ns - 1 : 0;
+      const int tail = valid ? len - (ns - 1) * P.split_rows : -1;
+      int before = 0, total = 0, rank = 0;      // full splits before sequence m, all of them; rank of m's last
+      for (int mm = 0; mm < P.seqs_per_xcd; ++mm) {
+        const int f = __builtin_amdgcn_readlane(nfull, mm);
+        const int tm = __builtin_amdgcn_readlane(tail, mm);
+        before += mm < m ? f : 0;
+        total += f;
+        rank += (tm > tail || (tm == tail && mm < m)) ? 1 : 0;
+      }
+      const bool hit = valid && (j < total ? (j >= before && j < before + nfull) : rank == j - total);
+      const unsigned long long hits = __ballot(hit);
+      if (hits) {                                  // else past this XCD's items
+        const int src = __ffsll((long long)hits) - 1;
+        b = __builtin_amdgcn_readlane(bm, src);
+        used_splits = __builtin_amdgcn_readlane(ns, src);
+        s = j < total ? j - __builtin_amdgcn_readlane(before, src) : used_splits - 1;
+        row0_l = offs[b];
+        len_l = __builtin_amdgcn_readlane(len, src);
+      }
     } else {
+      // more than 64 sequences per XCD: sequence by sequence in rank order
       int base = 0;
       for (int m = 0; m < P.seqs_per_xcd; ++m) {
         const int p = 8 * m + ((m & 1) ? 7 - xcd : xcd);

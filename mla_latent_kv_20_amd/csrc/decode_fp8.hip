@@ -228,7 +228,7 @@ mla_decode_fp8_kernel(DecodeParams P) {
   // ---- work item: as the bf16 decode (round-robin XCDs; fewer than 8 streams: items dealt
   // round-robin; else streams of one sequence on one XCD; with 16 or more sequences,
   // length-ranked snake order and only non-empty splits, the ranks read off at once when
-  // every length is equal).
+  // every length is equal, an XCD's items longest first when they are not).
   const int L = blockIdx.x;
   const int xcd = L & 7;
   const int k = L >> 3;
@@ -299,6 +299,36 @@ mla_decode_fp8_kernel(DecodeParams P) {
         used_splits = ns;
         row0_l = offs[p];
         len_l = len0;
+      }
+    } else if (P.seqs_per_xcd <= 64) {
+      // longest first, as the bf16 decode: the full splits in rank order, then the last
+      // splits, longest first; lane m holds this XCD's sequence m
+      const int m = (int)(threadIdx.x & 63);
+      const int pm = 8 * m + ((m & 1) ? 7 - xcd : xcd);
+      const bool valid = m < P.seqs_per_xcd && pm < P.batch;
+      const int bm = valid ? by_rank[pm] : 0;
+      const int len = valid ? lens[bm] : 0;
+      int ns = P.split_rows > 0 ? (len + P.split_rows - 1) / P.split_rows : P.num_splits;
+      ns = ns < 1 ? 1 : (ns > P.num_splits ? P.num_splits : ns);
+      const int nfull = valid ? ns - 1 : 0;
+      const int tail = valid ? len - (ns - 1) * P.split_rows : -1;
+      int before = 0, total = 0, rank = 0;
+      for (int mm = 0; mm < P.seqs_per_xcd; ++mm) {
+        const int f = __builtin_amdgcn_readlane(nfull, mm);
+        const int tm = __builtin_amdgcn_readlane(tail, mm);
+        before += mm < m ? f : 0;
+        total += f;
+        rank += (tm > tail || (tm == tail && mm < m)) ? 1 : 0;
+      }
+      const bool hit = valid && (j < total ? (j >= before && j < before + nfull) : rank == j - total);
+      const unsigned long long hits = __ballot(hit);
+      if (hits) {
+        const int src = __ffsll((long long)hits) - 1;
+        b = __builtin_amdgcn_readlane(bm, src);
+        used_splits = __builtin_amdgcn_readlane(ns, src);
+        s = j < total ? j - __builtin_amdgcn_readlane(before, src) : used_splits - 1;
+        row0_l = offs[b];
+        len_l = __builtin_amdgcn_readlane(len, src);
       }
     } else {
       int base = 0;
