@@ -472,6 +472,22 @@ def test_more_sequences_than_threads(torch, equal):
     check_lse("lse", got["lse"], ref["lse"], step_lse_bound(a, w), say)
 
 
+def test_ragged_sequences_with_several_queries(torch):
+    """20 sequences of unequal lengths (the longest-first dealing of an XCD's items), each
+    with 3 new tokens that attend causally among themselves."""
+    rng = np.random.default_rng(31)
+    lengths = [int(x) for x in rng.integers(0, 200, size=20)]
+    w = W.make_workload("rq", **W.DSV2, dtype=W.BF16, lengths=lengths, q_per_seq=3, appended_rows=True,
+                        seed=13)
+    a = oracle_args(w)
+    say("[edge] 20 ragged sequences, 3 queries each, 4 x 48")
+    got = run_step(w, 4, 48)
+    ref = O.absorbed_decode(**a, num_splits=4, split_rows=48)
+    assert_close("o_c", got["o_c"], ref["o_c"], w)
+    assert_close("o_lat", got["o_lat"], ref["o_lat"], w)
+    check_lse("lse", got["lse"], ref["lse"], step_lse_bound(a, w), say)
+
+
 def test_split_plans_agree_and_runs_repeat_bitwise(torch):
     w = workload("dsv2_small")
     say("[edge] split plans 1/7/64 and repeatability")
