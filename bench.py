@@ -203,6 +203,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="layer copies (0: enough to exceed 2x MALL)")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--split-rows", type=int, default=0)
+    ap.add_argument("--plan", choices=["config", "auto"], default="config",
+                    help="split plan: the workload's own, or mla_plan_splits on its lengths (auto)")
     ap.add_argument("--partials", choices=["auto", "f32", "f16"], default="auto",
                     help="storage of split results (auto: fp16 when there is a merge)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -236,9 +238,11 @@ def main():
     dev = torch.device("cuda:0")
 
     w = W.make_config(args.config)
-    S = args.num_splits or w.num_splits
-    R = args.split_rows or w.split_rows
     d = B.dims(w.n_h, w.d_h, w.d_c, w.d_r, B.MLA_BF16 if w.dtype == W.BF16 else B.MLA_F32)
+    S, R = (B.plan_splits(d, w.offsets, w.batch, w.q_per_seq) if args.plan == "auto"
+            else (w.num_splits, w.split_rows))
+    S = args.num_splits or S
+    R = args.split_rows or R
     esz = 2 if w.dtype == W.BF16 else 4
     layer_bytes = w.rows * (w.d_c + w.d_r) * esz + 2 * w.n_h * w.d_h * w.d_c * esz
     copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / layer_bytes))
@@ -524,7 +528,7 @@ def main():
         "data": "synthetic (seeded Gaussian latent cache, DeepSeek-V2 attention dims, random weights)",
         "config": {"workload": args.config, "batch": w.batch, "seq_len": int(w.lengths.max()),
                    "cached_rows": cached, "q_per_seq": w.q_per_seq, "n_h": w.n_h, "d_h": w.d_h,
-                   "d_c": w.d_c, "d_r": w.d_r, "num_splits": S, "split_rows": R, "layer_copies": copies,
+                   "d_c": w.d_c, "d_r": w.d_r, "num_splits": S, "split_rows": R, "plan": args.plan, "layer_copies": copies,
                    "partials": {B.MLA_F32: "f32", B.MLA_F16: "f16"}[part]},
         "roofline": roof,
         "kernels_ms_mean": {n: round(v, 5) for n, v in per.items()},

@@ -20,6 +20,7 @@
  *   mla_out_proj      o^C_i = W^UV_i o_lat_i                     (value absorption)
  *
  * mla_merge_out_proj does the last two in one call, with the same results.
+ * mla_plan_splits picks mla_decode's split plan from the sequence lengths (host code).
  *
  * The decode prologue builds this step's inputs from the hidden states:
  *   mla_kv_append     new cache rows [W^DKV h ; RoPE(W^KR h)] at given rows
@@ -73,7 +74,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 9
+#define MLA_ABI_VERSION 10
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -392,6 +393,32 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, int32_t q_per_seq
  */
 mla_status_t mla_check_offsets(const int64_t* host_offsets, int32_t batch,
                                int32_t q_per_seq, int64_t total_rows);
+
+/*
+ * mla_plan_splits - choose num_splits and split_rows for mla_decode (and mla_decode_fp8) from
+ * the sequences' lengths.  Any partition of a query's visible rows into splits merges to the
+ * same attention ([notes] "Key에 대한 수식 전개": one softmax over all visible rows; the
+ * merge is exact by log-sum-exp), so the plan only decides speed.  The choice comes from a
+ * model of the decode on MI355X: the kernel's own dealing of workgroups to the 8 XCDs and
+ * their order within an XCD, every CU taking the next workgroup when it frees up, a fixed
+ * start plus a time per 32-row tile for each workgroup, and the split results' bytes for
+ * the merge.  Host code only; nothing runs on the GPU.
+ *
+ *   dims         n_h, d_h and d_c are used (the heads per workgroup, the split results' size
+ *                and the weights the merge reads)
+ *   host_offsets [batch+1] int64 in host memory: the seq_offsets mla_decode will take
+ *   q_per_seq    as mla_decode
+ *   max_splits   the largest num_splits the caller's split buffers allow (>= 1)
+ *   num_splits, split_rows  out: the plan; split_rows is a multiple of 32, and 0 with
+ *                num_splits == 1
+ * Returns MLA_OK; MLA_ERR_NULL for a NULL pointer (host_offsets may be NULL when batch is
+ * 0: then the plan is one split); MLA_ERR_SHAPE for batch < 0, q_per_seq < 1,
+ * max_splits < 1, a negative offset or a sequence shorter than q_per_seq, or a batch too
+ * large to model (over 2^20 workgroups even with one split).
+ */
+mla_status_t mla_plan_splits(const mla_dims_t* dims, const int64_t* host_offsets, int32_t batch,
+                             int32_t q_per_seq, int32_t max_splits, int32_t* num_splits,
+                             int32_t* split_rows);
 
 /*
  * mla_merge_splits - combine split results.  Softmax over a disjoint union of

@@ -57,6 +57,7 @@ SIGNATURES = {
     "mla_partial_bytes": (_SZ, [_DIMS_P, _I32, _I32, _I32]),
     "mla_decode_workspace_bytes": (_SZ, [_DIMS_P, _I32, _I32]),
     "mla_check_offsets": (_I32, [_P, _I32, _I32, _I64]),
+    "mla_plan_splits": (_I32, [_DIMS_P, _P, _I32, _I32, _I32, _P, _P]),
     "mla_absorb_q": (_I32, [_DIMS_P, _I32, _P, _P, _P, _P, _P]),
     "mla_decode": (_I32, [_DIMS_P, _I32, _I32, _P, _P, _I64, _P, _I64, _P, _I32, _I32, _I32, _P, _P, _P]),
     "mla_merge_splits": (_I32, [_DIMS_P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
@@ -331,6 +332,16 @@ def check_offsets(host_offsets, batch: int, q_per_seq: int, total_rows: int) -> 
     import numpy as np
     a = np.ascontiguousarray(host_offsets, dtype=np.int64)
     return int(load().mla_check_offsets(a.ctypes.data if a.size else None, batch, q_per_seq, total_rows))
+
+
+def plan_splits(d: MlaDims, host_offsets, batch: int, q_per_seq: int, max_splits: int = 64):
+    """mla_plan_splits on a host int64 numpy array: (num_splits, split_rows)."""
+    import numpy as np
+    a = np.ascontiguousarray(host_offsets, dtype=np.int64)
+    ns, sr = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("mla_plan_splits", load().mla_plan_splits(ctypes.byref(d), a.ctypes.data if a.size else None, batch,
+                                                     q_per_seq, max_splits, ctypes.byref(ns), ctypes.byref(sr)))
+    return ns.value, sr.value
 
 
 def default_partial_dtype(d: MlaDims, num_splits: int) -> int:

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_kv.so")
 RESOURCES = os.path.join(HERE, "kernel_resources.txt")
 SOURCES = ["api.cpp", "decode_bf16.hip", "absorb_bf16.hip", "merge_f32.hip", "fused_bf16.hip", "prologue.hip",
-           "quant_fp8.hip", "decode_fp8.hip", "fold.hip", "calib.hip", "noalloc.hip"]
+           "quant_fp8.hip", "decode_fp8.hip", "fold.hip", "calib.hip", "noalloc.hip", "plan.cpp"]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 

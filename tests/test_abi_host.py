@@ -37,7 +37,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert set(names) == set(B.SIGNATURES), names
     for n in names:
         assert hasattr(lib, n)
-    assert lib.mla_abi_version() == 9
+    assert lib.mla_abi_version() == 10
 
 
 def test_calibration_argument_checks(lib):
