@@ -210,14 +210,15 @@ def test_decode_fp8_sixteen_or_more_sequences(torch, lengths):
     check("lse_part", D.to_numpy_f64(lp), rl, lse=True)
 
 
-@pytest.mark.parametrize("equal", [False, True])
-def test_decode_fp8_more_sequences_than_threads(torch, equal):
+@pytest.mark.parametrize("count,equal", [(300, False), (300, True), (600, False)])
+def test_decode_fp8_more_sequences_than_threads(torch, count, equal):
     """300 sequences, more than the workgroup's 256 threads: every loop of the length ranking
-    takes several passes; ragged lengths of 1..40 rows (several splits empty) or all equal."""
+    takes several passes; ragged lengths of 1..40 rows (several splits empty) or all equal.
+    600 ragged sequences put more than 64 on an XCD (items sequence by sequence)."""
     rng = np.random.default_rng(23)
-    lengths = [17] * 300 if equal else [int(x) for x in rng.integers(1, 41, size=300)]
+    lengths = [17] * count if equal else [int(x) for x in rng.integers(1, 41, size=count)]
     w = W.make_workload("many8", **W.DSV2, dtype=W.BF16, lengths=lengths, seed=12)
-    say(f"[decode_fp8] 300 sequences, {'equal' if equal else 'ragged'} lengths, 3 x 16")
+    say(f"[decode_fp8] {count} sequences, {'equal' if equal else 'ragged'} lengths, 3 x 16")
     codes, scales, deq = quantize_on_gpu(torch, w, D.packed_rows(w))
     qa = W.draw_q_abs(w)
     op, lp = B.decode_fp8(dims_of(w), D._tensor(qa, W.BF16, "cuda"), codes, scales,

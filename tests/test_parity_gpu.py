@@ -455,16 +455,17 @@ def test_sixteen_or_more_sequences_equal_and_unequal(torch, lengths):
     check_lse("lse", got["lse"], ref["lse"], step_lse_bound(a, w), say)
 
 
-@pytest.mark.parametrize("equal", [False, True])
-def test_more_sequences_than_threads(torch, equal):
+@pytest.mark.parametrize("count,equal", [(300, False), (300, True), (600, False)])
+def test_more_sequences_than_threads(torch, count, equal):
     """300 sequences: more than the workgroup's 256 threads, so each loop of the length
     ranking (offsets read, equal-length vote, ranks) takes several passes; ragged lengths of
-    1..40 rows (several splits empty) or all equal."""
+    1..40 rows (several splits empty) or all equal.  600 ragged sequences put more than 64
+    on an XCD, where its items go sequence by sequence instead of longest first."""
     rng = np.random.default_rng(23)
-    lengths = [17] * 300 if equal else [int(x) for x in rng.integers(1, 41, size=300)]
+    lengths = [17] * count if equal else [int(x) for x in rng.integers(1, 41, size=count)]
     w = W.make_workload("many", **W.DSV2, dtype=W.BF16, lengths=lengths, seed=12)
     a = oracle_args(w)
-    say(f"[edge] 300 sequences, {'equal' if equal else 'ragged'} lengths, 3 x 16")
+    say(f"[edge] {count} sequences, {'equal' if equal else 'ragged'} lengths, 3 x 16")
     got = run_step(w, 3, 16)
     ref = O.absorbed_decode(**a, num_splits=3, split_rows=16)
     assert_close("o_c", got["o_c"], ref["o_c"], w)
